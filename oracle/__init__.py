@@ -1,0 +1,173 @@
+"""fp64 CPU oracle of the learned-relative GQA attention forward (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package.  The product path (the HIP library and its Python
+binding) never does, and this package imports nothing from the product path.
+
+The arithmetic lives in ``attn_oracle.c`` (plain sequential fp64 loops, OpenMP
+over query rows only).  This wrapper applies the defaults of the forward's
+optional arguments, as the page "nemo_automodel.components.models.inkling2.
+flex_attention" (Inkling2FlexAttention.forward, parameters key_valid,
+positions, key_positions) describes them, read as follows:
+
+* ``key_valid`` defaults to ``valid`` (single context-parallel rank);
+* ``positions`` defaults to the global column ``query_offset + i`` (one
+  document);
+* ``key_positions`` defaults to ``positions`` when keys and queries are the same
+  tokens (``Sk == Sq`` and ``query_offset == 0``), otherwise to the key column.
+
+Parity is pinned by the tests in ``tests/test_oracle_pins.py`` (brute force,
+textbook causal attention, closed forms, invariants); see that file's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+import time
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O3, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O3", "-march=x86-64-v2", "-fopenmp", "-fPIC", "-shared",
+               "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            lib.attn_oracle_fwd.restype = ctypes.c_int
+            lib.attn_oracle_fwd.argtypes = [
+                P, P, P, P, ctypes.c_int, P, P, P, P, P,
+                ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int,
+                P, ctypes.c_int64, P, P, P, ctypes.c_int]
+            lib.attn_oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _as_np(t, dtype):
+    """Host numpy view/copy of a tensor or array in the exact storage dtype."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            t = t.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16)
+            if t.dtype == torch.bool:
+                return t.numpy().astype(np.uint8)
+            t = t.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(t), dtype=dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().attn_oracle_max_threads())
+
+
+def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
+             key_positions=None, window: Optional[int] = None, query_offset: int = 0,
+             rows=None, n_threads: int = 0, profiles_bf16: Optional[bool] = None):
+    """fp64 forward.  Returns ``(out, lse, n_allowed)`` as numpy arrays.
+
+    ``q``/``k``/``v`` are bf16 (torch tensors, or uint16 bit arrays); ``profiles``
+    fp32 or bf16.  With ``rows`` (flattened ``b*Sq + i``) only those rows are
+    computed and the outputs are compact: ``out [n, Hq, D]``, ``lse [n, Hq]``,
+    ``n_allowed [n]``; otherwise ``out [B, Sq, Hq, D]``, ``lse [B, Sq, Hq]``,
+    ``n_allowed [B, Sq]``.
+    """
+    import torch
+
+    B, Sq, Hq, D = (int(x) for x in q.shape)
+    Sk, Hkv = int(k.shape[1]), int(k.shape[2])
+    E = int(profiles.shape[-1])
+    if profiles_bf16 is None:
+        profiles_bf16 = isinstance(profiles, torch.Tensor) and profiles.dtype == torch.bfloat16
+    qn = _as_np(q, np.uint16)
+    kn = _as_np(k, np.uint16)
+    vn = _as_np(v, np.uint16)
+    pn = _as_np(profiles, np.uint16 if profiles_bf16 else np.float32)
+    sn = _as_np(sink, np.float32)
+    valid_n = _as_np(valid, np.uint8)
+    if key_valid is None:
+        if Sk != Sq or query_offset != 0:
+            raise ValueError("key_valid is required when keys are not the query tokens")
+        kvalid_n = valid_n
+    else:
+        kvalid_n = _as_np(key_valid, np.uint8)
+    if positions is None:
+        pos_n = np.broadcast_to(np.arange(query_offset, query_offset + Sq, dtype=np.int32),
+                                (B, Sq)).copy()
+    else:
+        pos_n = _as_np(positions, np.int32)
+    if key_positions is None:
+        if Sk == Sq and query_offset == 0:
+            kpos_n = pos_n
+        else:
+            kpos_n = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, Sk)).copy()
+    else:
+        kpos_n = _as_np(key_positions, np.int32)
+    for name, a, shape in (("q", qn, (B, Sq, Hq, D)), ("k", kn, (B, Sk, Hkv, D)),
+                           ("v", vn, (B, Sk, Hkv, D)), ("profiles", pn, (B, Hq, Sq, E)),
+                           ("sink", sn, (B, Sq, Hq)), ("valid", valid_n, (B, Sq)),
+                           ("key_valid", kvalid_n, (B, Sk)), ("positions", pos_n, (B, Sq)),
+                           ("key_positions", kpos_n, (B, Sk))):
+        if tuple(a.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(a.shape)} != {shape}")
+    if rows is None:
+        rows_n = None
+        n = B * Sq
+    else:
+        rows_n = _as_np(rows, np.int64).reshape(-1)
+        n = int(rows_n.shape[0])
+    out = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    cnt = np.empty((n,), dtype=np.int32)
+    w = 0 if window is None else int(window)
+    rc = _load().attn_oracle_fwd(
+        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), int(bool(profiles_bf16)), _ptr(sn),
+        _ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n), w, int(query_offset),
+        B, Sq, Sk, Hq, Hkv, D, E,
+        None if rows_n is None else _ptr(rows_n), n, _ptr(out), _ptr(lse), _ptr(cnt),
+        int(n_threads))
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_fwd failed ({rc})")
+    if rows is None:
+        return out.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq), cnt.reshape(B, Sq)
+    return out, lse, cnt
+
+
+def timed_fwd(inputs: dict, rows, n_threads: int = 0):
+    """Run the oracle on ``rows`` of a generated workload; returns (seconds, result)."""
+    t0 = time.perf_counter()
+    res = attn_fwd(inputs["q"], inputs["k"], inputs["v"], inputs["profiles"], inputs["sink"],
+                   inputs["valid"], inputs.get("key_valid"), inputs.get("positions"),
+                   inputs.get("key_positions"), inputs.get("window"),
+                   inputs.get("query_offset", 0), rows=rows, n_threads=n_threads)
+    return time.perf_counter() - t0, res

@@ -1,0 +1,202 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle of the learned-relative grouped-query
+ * attention forward with per-query sinks.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (pages cited by title and API entry):
+ *
+ *  - "nemo_automodel.components.models.inkling2.flex_attention", class
+ *    Inkling2FlexAttention: the logit scale is head_dim^-0.5; forward combines
+ *    content attention with a learned relative term and a sink; relative
+ *    profiles are laid out [batch, heads, sequence, relative_extent] and no
+ *    sequence-by-sequence bias is ever formed; the result is FP32
+ *    [batch, sequence, heads, head_dim].  Parameter list of forward: q
+ *    [B,S,Hq,D], k/v [B,Sk,Hkv,D], profiles [B,Hq,S,E], sink [B,S,Hq], valid
+ *    [B,S], key_valid [B,Sk], positions [B,S] (logical, restarting at every
+ *    document), key_positions [B,Sk], query_offset (global column of the first
+ *    local query).
+ *  - "nemo_automodel.components.models.inkling2.attention" (v0.4),
+ *    Inkling2Attention.forward: the sink carries no value (a virtual sink whose
+ *    value is zero); Inkling2Attention._eager: a quadratic reference exists and
+ *    leaves its inputs untouched.
+ *  - "nemo_automodel.components.attention.flex_attention", sliding-window
+ *    mask mod and forward's sliding_window / enable_gqa parameters.
+ *
+ * Readings taken where the pages leave a step open (each is stated again in
+ * the repository's design notes):
+ *  - document membership: query i (global column gi = query_offset + i) and
+ *    key j are in the same document iff gi - positions[i] == j - key_positions[j]
+ *    (both sides name the column where the document starts);
+ *  - causal order on global columns: j <= gi;
+ *  - window W > 0 keeps keys whose logical distance r = positions[i] -
+ *    key_positions[j] satisfies r < W (W keys including the query itself);
+ *    W <= 0 means no window;
+ *  - relative bias = profiles[b,h,i,r] for 0 <= r < E, and 0 otherwise;
+ *  - the bias is added unscaled: z = scale * <q,k> + bias;
+ *  - GQA: query head h reads key/value head h / (Hq/Hkv);
+ *  - the sink sigma = sink[b,i,h] is one more logit in the softmax
+ *    denominator, with a zero value vector;
+ *  - lse = ln(exp(sigma) + sum_j exp(z_j)) (natural log, sink included);
+ *  - a row with no allowed key: out = 0 and lse = sigma.
+ *
+ * Precision: every input element is converted exactly to double (bf16 by
+ * placing its 16 bits in the top half of an IEEE single; fp32 by promotion),
+ * and every sum, exponential and logarithm is taken in double in plain
+ * sequential order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Exact conversion of a bf16 bit pattern to double. */
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double profile_at(const void* profiles, int profiles_is_bf16, size_t idx)
+{
+    if (profiles_is_bf16)
+        return bf16_to_double(((const uint16_t*)profiles)[idx]);
+    return (double)((const float*)profiles)[idx];
+}
+
+/*
+ * Is key j visible from query i of batch row b?  Plain statement of the mask:
+ * both tokens real, key not after the query, same document, inside the window.
+ */
+static int allowed(const uint8_t* valid, const uint8_t* key_valid,
+                   const int32_t* positions, const int32_t* key_positions,
+                   int64_t window, int64_t query_offset,
+                   int Sq, int Sk, int b, int i, int j)
+{
+    int64_t gi = query_offset + i;
+    int64_t p_i = positions[(size_t)b * Sq + i];
+    int64_t k_j = key_positions[(size_t)b * Sk + j];
+    if (!valid[(size_t)b * Sq + i]) return 0;
+    if (!key_valid[(size_t)b * Sk + j]) return 0;
+    if ((int64_t)j > gi) return 0;                       /* causal */
+    if (gi - p_i != (int64_t)j - k_j) return 0;         /* same document */
+    if (window > 0 && !(p_i - k_j < window)) return 0;  /* sliding window */
+    return 1;
+}
+
+/*
+ * Forward for the query rows listed in `rows` (flattened b*Sq + i); all rows
+ * when rows == NULL (then n_rows must be B*Sq).  Outputs are compact over the
+ * listed rows: out[n_rows, Hq, D], lse[n_rows, Hq], n_allowed[n_rows].
+ *
+ * q, k, v: bf16 bit patterns.  profiles: fp32 or bf16 (profiles_is_bf16).
+ * Every pointer is a host pointer; nothing is allocated beyond one logit buffer
+ * of Sk doubles per thread.  Returns 0, or -1 on bad arguments / no memory.
+ */
+int attn_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const void* profiles, int profiles_is_bf16,
+                    const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                    const int32_t* positions, const int32_t* key_positions,
+                    int64_t window, int64_t query_offset,
+                    int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                    const int64_t* rows, int64_t n_rows,
+                    double* out, double* lse, int32_t* n_allowed, int n_threads)
+{
+    if (!q || !k || !v || !profiles || !sink || !valid || !key_valid || !positions ||
+        !key_positions || !out || !lse || !n_allowed)
+        return -1;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || E <= 0 || Hq % Hkv)
+        return -1;
+    if (!rows && n_rows != (int64_t)B * Sq) return -1;
+    const int G = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        uint8_t* ok = (uint8_t*)malloc((size_t)(Sk > 0 ? Sk : 1));
+        if (!z || !ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            if (!z || !ok) continue;
+            int64_t row = rows ? rows[t] : t;
+            int b = (int)(row / Sq), i = (int)(row % Sq);
+            int count = 0;
+            for (int j = 0; j < Sk; ++j) {
+                ok[j] = (uint8_t)allowed(valid, key_valid, positions, key_positions,
+                                         window, query_offset, Sq, Sk, b, i, j);
+                count += ok[j];
+            }
+            n_allowed[t] = count;
+            for (int h = 0; h < Hq; ++h) {
+                int g = h / G;
+                double sigma = (double)sink[((size_t)b * Sq + i) * Hq + h];
+                double* o = out + ((size_t)t * Hq + h) * D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                if (count == 0) {
+                    lse[(size_t)t * Hq + h] = sigma;
+                    continue;
+                }
+                const uint16_t* qrow = q + (((size_t)b * Sq + i) * Hq + h) * D;
+                int64_t p_i = positions[(size_t)b * Sq + i];
+                /* pass 1: logits of the allowed keys and their maximum */
+                double M = sigma;
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+                    int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
+                    double bias = 0.0;
+                    if (r >= 0 && r < E)
+                        bias = profile_at(profiles, profiles_is_bf16,
+                                          (((size_t)b * Hq + h) * Sq + i) * (size_t)E + (size_t)r);
+                    z[j] = scale * dot + bias;
+                    if (z[j] > M) M = z[j];
+                }
+                /* pass 2: normaliser (sink included) and value accumulation */
+                double L = exp(sigma - M);
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    double p = exp(z[j] - M);
+                    L += p;
+                    const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    for (int d = 0; d < D; ++d) o[d] += p * bf16_to_double(vrow[d]);
+                }
+                for (int d = 0; d < D; ++d) o[d] /= L;
+                lse[(size_t)t * Hq + h] = M + log(L);
+            }
+        }
+        free(z);
+        free(ok);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Threads the OpenMP runtime will use for a parallel region (reported by callers). */
+int attn_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
