@@ -1,0 +1,176 @@
+/*
+ * inkattn.h -- C ABI of the MI355X (gfx950) learned-relative grouped-query
+ * attention forward with per-query sinks.
+ *
+ * The operation is the forward of Inkling2FlexAttention (page
+ * "nemo_automodel.components.models.inkling2.flex_attention", section API:
+ * the class, its `scale` attribute and its `forward` parameters), with the
+ * zero-valued virtual sink of Inkling2Attention.forward (page
+ * "nemo_automodel.components.models.inkling2.attention", v0.4) and the
+ * sliding-window semantics of the page
+ * "nemo_automodel.components.attention.flex_attention" (sliding-window mask mod
+ * and forward's `sliding_window` parameter).  For query i of batch row b and
+ * query head h (K/V head g = h / (Hq/Hkv)), with gi = query_offset + i:
+ *
+ *   key j is allowed  <=>  valid[b,i] and key_valid[b,j] and j <= gi
+ *                          and gi - positions[b,i] == j - key_positions[b,j]
+ *                          and (window <= 0 or positions[b,i] - key_positions[b,j] < window)
+ *   z_j   = head_dim^-0.5 * <q[b,i,h,:], k[b,j,g,:]> + bias_j
+ *   bias_j = profiles[b,h,i,r] with r = positions[b,i] - key_positions[b,j]
+ *            when 0 <= r < E, and 0 otherwise
+ *   s     = sink[b,i,h]  (one more logit in the denominator, zero value)
+ *   out[b,i,h,:] = sum_j e^{z_j} v[b,j,g,:] / (e^s + sum_j e^{z_j})
+ *   lse[b,i,h]   = ln(e^s + sum_j e^{z_j})            (natural log)
+ *   a row with no allowed key: out = 0, lse = s.
+ *
+ * No sequence-by-sequence score or bias tensor is formed.  The two tokens
+ * of an allowed pair always satisfy r = gi - j (same document start column).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to C-contiguous memory owned by
+ *    the caller; the library allocates nothing and keeps no global mutable
+ *    state, so calls are reentrant.  Inputs are never written.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  A successful return means the work was enqueued.
+ *  - Every argument check runs on the host before any launch; on failure
+ *    nothing is enqueued and a nonzero INKATTN_* status is returned, with a
+ *    description in attn_last_error().  Launch failures return
+ *    INKATTN_ERR_LAUNCH with the HIP error text in attn_last_error().
+ *  - Sizes: B >= 0, Sq >= 0, Sk >= 0, Hq >= 1, Hkv >= 1 with Hq % Hkv == 0,
+ *    D in {64, 128}, E >= 1, B*Sq*Hq*D and B*Hq*Sq*E below 2^40 elements,
+ *    Sq, Sk and query_offset + Sq below 2^30.
+ *  - Preconditions not checked (they would need a device read): positions and
+ *    key_positions hold values in [0, 2^30); bf16 values of v lie within
+ *    +-65504 (v is converted exactly to fp16 for the PV product); inputs at
+ *    tokens that are not valid hold finite values.
+ */
+#ifndef INKATTN_H
+#define INKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Data type of the `profiles` tensor (the projection's fp32 or bf16 output). */
+enum inkattn_dtype { INKATTN_F32 = 0, INKATTN_BF16 = 1 };
+
+/* Status codes. */
+enum inkattn_status {
+    INKATTN_OK = 0,
+    INKATTN_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    INKATTN_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes         */
+    INKATTN_ERR_UNSUPPORTED = 3, /* head_dim / dtype outside what is built     */
+    INKATTN_ERR_ALIGN = 4,       /* a pointer is not aligned as required       */
+    INKATTN_ERR_WORKSPACE = 5,   /* workspace missing or too small             */
+    INKATTN_ERR_LAUNCH = 6       /* a HIP launch reported an error             */
+};
+
+/*
+ * Bytes of device workspace attn_fwd needs for these sizes (per-tile mask
+ * summaries written by the scheduler pre-pass).  Never fails; returns 0 only
+ * when B*Sq == 0 and B*Sk == 0.
+ */
+size_t attn_fwd_workspace_size(int B, int Sq, int Sk);
+
+/*
+ * attn_fwd -- the fused forward (scheduler pre-pass + attention kernel).
+ *
+ *   q          [B, Sq, Hq, D]  bf16, 16-byte aligned
+ *   k, v       [B, Sk, Hkv, D] bf16, 16-byte aligned
+ *   profiles   [B, Hq, Sq, E]  fp32 or bf16 (profiles_dtype), element-aligned
+ *   sink       [B, Sq, Hq]     fp32 (may hold -inf: no sink)
+ *   valid      [B, Sq]         uint8 (0 / nonzero), true for real tokens
+ *   key_valid  [B, Sk]         uint8, or NULL: then `valid` (requires Sk == Sq
+ *                              and query_offset == 0)
+ *   positions  [B, Sq]         int32 logical positions restarting at 0 at each
+ *                              document start, or NULL: gi (one document)
+ *   key_positions [B, Sk]      int32, or NULL: `positions` when Sk == Sq and
+ *                              query_offset == 0, else the key column j
+ *   window     keys a query may see counting itself (distance r < window);
+ *              <= 0: no window
+ *   query_offset  global column of the first local query (0 without context
+ *              parallelism); keys are always global columns 0..Sk-1
+ *   out        [B, Sq, Hq, D]  fp32, 16-byte aligned, written
+ *   lse        [B, Sq, Hq]     fp32, written
+ *   workspace  device buffer of at least attn_fwd_workspace_size(B, Sq, Sk)
+ *              bytes, 16-byte aligned; contents on entry are ignored
+ */
+int attn_fwd(const void* q, const void* k, const void* v,
+             const void* profiles, int profiles_dtype,
+             const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+             const int32_t* positions, const int32_t* key_positions,
+             int64_t window, int64_t query_offset,
+             int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+             float* out, float* lse,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_plan -- the scheduler pre-pass alone: writes the per-tile mask
+ * summaries (document start columns and real-token counts of every 32-token
+ * query block and 64-key tile) into `workspace`.  The summaries depend only on
+ * valid / key_valid / positions / key_positions / query_offset (the masks are
+ * rebuilt from each forward's token validity, as on the flex_attention page,
+ * class description), not on the window or any tensor values, so one plan
+ * serves every attention layer of a forward that shares them.  Arguments as
+ * for attn_fwd.
+ */
+int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
+              const int32_t* positions, const int32_t* key_positions,
+              int64_t query_offset, int B, int Sq, int Sk,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_planned -- the attention kernel alone, reading the summaries that
+ * attn_plan wrote into `workspace` for the same mask arguments (enqueued
+ * earlier on `stream`, or completed).  A workspace planned for other mask
+ * arguments gives undefined results.  attn_fwd == attn_plan + attn_fwd_planned.
+ */
+int attn_fwd_planned(const void* q, const void* k, const void* v,
+                     const void* profiles, int profiles_dtype,
+                     const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                     float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_debug_counts -- number of allowed keys per query row, n_allowed[B, Sq]
+ * (int32), evaluated with the same device mask predicate as attn_fwd.  Same
+ * argument meanings as attn_fwd; used to check the mask exactly.
+ */
+int attn_debug_counts(const uint8_t* valid, const uint8_t* key_valid,
+                      const int32_t* positions, const int32_t* key_positions,
+                      int64_t window, int64_t query_offset, int B, int Sq, int Sk,
+                      int32_t* n_allowed, void* stream);
+
+/*
+ * attn_debug_tiles -- the class attn_fwd gives each (query block, key tile):
+ * tile_class[B, ceil(Sq/32), ceil(Sk/64)] (uint8): 0 = skipped, 1 = masked
+ * element by element, 2 = full (no mask applied).  Uses the same pre-pass
+ * and the same classification code as attn_fwd; `workspace` as for attn_fwd.
+ */
+int attn_debug_tiles(const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset, int B, int Sq, int Sk,
+                     uint8_t* tile_class, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Query-block and key-tile sizes the kernels use (32 and 64). */
+int attn_query_block(void);
+int attn_key_tile(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INKATTN_H */

@@ -63,6 +63,10 @@ def _load():
                 ctypes.c_int, ctypes.c_int,
                 P, ctypes.c_int64, P, P, P, ctypes.c_int]
             lib.attn_oracle_max_threads.restype = ctypes.c_int
+            lib.attn_oracle_mask.restype = ctypes.c_int
+            lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
+                                             ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -91,6 +95,48 @@ def max_threads() -> int:
     return int(_load().attn_oracle_max_threads())
 
 
+def _mask_inputs(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk):
+    """Host arrays of the mask inputs, with the optional ones defaulted."""
+    valid_n = _as_np(valid, np.uint8)
+    if key_valid is None:
+        if Sk != Sq or query_offset != 0:
+            raise ValueError("key_valid is required when keys are not the query tokens")
+        kvalid_n = valid_n
+    else:
+        kvalid_n = _as_np(key_valid, np.uint8)
+    if positions is None:
+        pos_n = np.broadcast_to(np.arange(query_offset, query_offset + Sq, dtype=np.int32),
+                                (B, Sq)).copy()
+    else:
+        pos_n = _as_np(positions, np.int32)
+    if key_positions is None:
+        if Sk == Sq and query_offset == 0:
+            kpos_n = pos_n
+        else:
+            kpos_n = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, Sk)).copy()
+    else:
+        kpos_n = _as_np(key_positions, np.int32)
+    return valid_n, kvalid_n, pos_n, kpos_n
+
+
+def mask(valid, key_valid=None, positions=None, key_positions=None, window=None,
+         query_offset: int = 0, Sk=None, full: bool = False, n_threads: int = 0):
+    """Allowed-key counts [B, Sq] (and the [B, Sq, Sk] mask when ``full``)."""
+    B, Sq = (int(x) for x in valid.shape)
+    if Sk is None:
+        Sk = int(key_valid.shape[1]) if key_valid is not None else Sq
+    valid_n, kvalid_n, pos_n, kpos_n = _mask_inputs(valid, key_valid, positions, key_positions,
+                                                    query_offset, B, Sq, Sk)
+    cnt = np.empty((B, Sq), dtype=np.int32)
+    m = np.empty((B, Sq, Sk), dtype=np.uint8) if full else None
+    rc = _load().attn_oracle_mask(_ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n),
+                                  0 if window is None else int(window), int(query_offset), B, Sq, Sk,
+                                  _ptr(cnt), None if m is None else _ptr(m), int(n_threads))
+    if rc != 0:
+        raise RuntimeError("attn_oracle_mask failed")
+    return (cnt, m) if full else cnt
+
+
 def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
              key_positions=None, window: Optional[int] = None, query_offset: int = 0,
              rows=None, n_threads: int = 0, profiles_bf16: Optional[bool] = None):
@@ -114,25 +160,8 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
     vn = _as_np(v, np.uint16)
     pn = _as_np(profiles, np.uint16 if profiles_bf16 else np.float32)
     sn = _as_np(sink, np.float32)
-    valid_n = _as_np(valid, np.uint8)
-    if key_valid is None:
-        if Sk != Sq or query_offset != 0:
-            raise ValueError("key_valid is required when keys are not the query tokens")
-        kvalid_n = valid_n
-    else:
-        kvalid_n = _as_np(key_valid, np.uint8)
-    if positions is None:
-        pos_n = np.broadcast_to(np.arange(query_offset, query_offset + Sq, dtype=np.int32),
-                                (B, Sq)).copy()
-    else:
-        pos_n = _as_np(positions, np.int32)
-    if key_positions is None:
-        if Sk == Sq and query_offset == 0:
-            kpos_n = pos_n
-        else:
-            kpos_n = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, Sk)).copy()
-    else:
-        kpos_n = _as_np(key_positions, np.int32)
+    valid_n, kvalid_n, pos_n, kpos_n = _mask_inputs(valid, key_valid, positions, key_positions,
+                                                    query_offset, B, Sq, Sk)
     for name, a, shape in (("q", qn, (B, Sq, Hq, D)), ("k", kn, (B, Sk, Hkv, D)),
                            ("v", vn, (B, Sk, Hkv, D)), ("profiles", pn, (B, Hq, Sq, E)),
                            ("sink", sn, (B, Sq, Hq)), ("valid", valid_n, (B, Sq)),

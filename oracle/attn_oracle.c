@@ -200,3 +200,36 @@ int attn_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Mask only: n_allowed[B*Sq] for every query row, and, when `mask` is not
+ * NULL, the whole visibility matrix mask[B, Sq, Sk] (1 = allowed).  Uses the
+ * same `allowed` statement as attn_oracle_fwd.  Returns 0, or -1 on bad
+ * arguments.
+ */
+int attn_oracle_mask(const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset, int B, int Sq, int Sk,
+                     int32_t* n_allowed, uint8_t* mask, int n_threads)
+{
+    if (!valid || !key_valid || !positions || !key_positions || !n_allowed) return -1;
+    if (B < 0 || Sq < 0 || Sk < 0) return -1;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t row = 0; row < (int64_t)B * Sq; ++row) {
+        int b = (int)(row / Sq), i = (int)(row % Sq);
+        int count = 0;
+        for (int j = 0; j < Sk; ++j) {
+            int a = allowed(valid, key_valid, positions, key_positions, window, query_offset,
+                            Sq, Sk, b, i, j);
+            count += a;
+            if (mask) mask[(size_t)row * Sk + j] = (uint8_t)a;
+        }
+        n_allowed[row] = count;
+    }
+    return 0;
+}

@@ -1,0 +1,100 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any launch (no GPU needed).
+
+Fake device addresses are used only in calls that must fail validation; no
+call here reaches a kernel launch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_attention_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "inkattn.h")
+
+A = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = binding.load()
+    names = declared_functions()
+    assert names == sorted(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_sizes():
+    assert binding.attn_status_string(0) == "ok"
+    assert "NULL" in binding.attn_status_string(1)
+    assert binding.attn_query_block() == 32 and binding.attn_key_tile() == 64
+    assert binding.attn_fwd_workspace_size(1, 128, 128) == (4 + 2) * 16
+    assert binding.attn_fwd_workspace_size(2, 33, 65) == (2 * 2 + 2 * 2) * 16
+    assert binding.attn_fwd_workspace_size(0, 10, 10) == 0
+
+
+def call(**over):
+    a = dict(q=A, k=A, v=A, profiles=A, pdt=0, sink=A, valid=A, key_valid=None, positions=None,
+             key_positions=None, window=0, qoff=0, B=1, Sq=64, Sk=64, Hq=4, Hkv=2, D=128, E=16,
+             out=A, lse=A, ws=A, wsb=1 << 20, stream=None)
+    a.update(over)
+    lib = binding.load()
+    return lib.attn_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["profiles"]), a["pdt"], P(a["sink"]),
+                        P(a["valid"]), P(a["key_valid"]), P(a["positions"]), P(a["key_positions"]),
+                        a["window"], a["qoff"], a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"],
+                        a["E"], P(a["out"]), P(a["lse"]), P(a["ws"]), a["wsb"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(sink=None), 1), (dict(out=None), 1), (dict(valid=None), 1),
+    (dict(k=None), 1),
+    (dict(Sk=100), 1),                      # Sk != Sq needs key_valid
+    (dict(qoff=5), 1),                      # query_offset != 0 needs key_valid
+    (dict(Hq=6, Hkv=4), 2), (dict(Hkv=0), 2), (dict(E=0), 2), (dict(Sq=-1), 2),
+    (dict(Sq=1 << 30, Sk=1 << 30), 2), (dict(qoff=-1, key_valid=A), 2),
+    (dict(D=96), 3), (dict(D=256), 3), (dict(pdt=7), 3),
+    (dict(q=A + 8), 4), (dict(out=A + 4), 4), (dict(profiles=A + 2), 4), (dict(positions=A + 2), 4),
+    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(ws=A + 8), 4),
+])
+def test_host_validation_rejects_before_launch(over, status):
+    assert call(**over) == status
+    assert binding.attn_last_error() != ""
+
+
+def test_bf16_profiles_need_only_2_byte_alignment_and_empty_rows_return_ok():
+    # B*Sq == 0 returns OK without touching memory
+    assert call(Sq=0, Sk=0, B=1) == 0
+    assert call(B=0) == 0
+    # bf16 profiles at a 2-byte offset pass the alignment check; a too-small
+    # workspace is what stops the call (still before any launch)
+    assert call(pdt=1, profiles=A + 2, wsb=8) == 5
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.attn_fwd(x, x, x, torch.zeros(1, 2, 4, 8), torch.zeros(1, 4, 2),
+                         torch.ones(1, 4, dtype=torch.bool))
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package and the HIP source never name the oracle."""
+    pkg = os.path.join(ROOT, "transformer_attention_03_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "attn_oracle" not in text, f

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small shapes are compared element by element (every output, several tiles
+and ragged tails); the full-size workloads, in the launch configuration the
+benchmark times, are compared on sampled rows, plus exact properties that hold
+at any size (allowed-key counts of every row, count probe, determinism).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (announce, assert_close, check_full, check_rows, count_probe_inputs,
+                            counts_from_lse, run_hip, run_oracle, to_device)
+from transformer_attention_03_amd import binding
+from transformer_attention_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.load()   # fails loudly when the HIP library is missing
+    yield
+
+
+# ------------------------------------------------------------------------------------------
+# small shapes, whole output
+# ------------------------------------------------------------------------------------------
+SMALL = {
+    "tiny": lambda: W.generate(W.WORKLOADS["tiny"]),
+    "tailpad_G4_D128": lambda: W.custom(B=2, S=300, Hq=8, Hkv=2, D=128, E=64, seed=101,
+                                        structure="tail_pad", max_tail_pad=40),
+    "window_G4_D64": lambda: W.custom(B=1, S=517, Hq=4, Hkv=1, D=64, E=100, window=70, seed=102),
+    "packed_G2_D128": lambda: W.custom(B=1, S=700, Hq=8, Hkv=4, D=128, E=48, seed=103, structure="packed",
+                                       doc_min=20, doc_max=200, invalid_tail=13),
+    "packed_window": lambda: W.custom(B=2, S=400, Hq=4, Hkv=2, D=128, E=30, window=45, seed=104,
+                                      structure="packed", doc_min=5, doc_max=90, invalid_tail=7),
+    "bf16_profiles_sink2": lambda: W.custom(B=1, S=333, Hq=16, Hkv=2, D=128, E=77, seed=105,
+                                            profiles_dtype=torch.bfloat16, sink_std=2.0),
+    "G1": lambda: W.custom(B=1, S=260, Hq=3, Hkv=3, D=128, E=16, seed=106),
+    "G3_hpw3": lambda: W.custom(B=1, S=190, Hq=6, Hkv=2, D=64, E=200, seed=107, window=33),
+    "G16_two_chunks": lambda: W.custom(B=1, S=150, Hq=16, Hkv=1, D=128, E=40, seed=108,
+                                       structure="packed", doc_min=10, doc_max=60),
+    "E1_window1": lambda: W.custom(B=1, S=100, Hq=4, Hkv=2, D=64, E=1, window=1, seed=109),
+    "E_beyond_S": lambda: W.custom(B=1, S=97, Hq=4, Hkv=1, D=128, E=300, seed=110),
+    "S1": lambda: W.custom(B=3, S=1, Hq=4, Hkv=2, D=128, E=5, seed=111),
+    "wide_sink": lambda: W.custom(B=1, S=200, Hq=8, Hkv=2, D=128, E=64, seed=112, sink_std=8.0,
+                                  profile_std=3.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_full_parity(name):
+    x = SMALL[name]()
+    check_full(x, name)
+
+
+def test_determinism_bitwise():
+    x = SMALL["packed_G2_D128"]()
+    d = to_device(x)
+    announce("determinism: attn_fwd x3 on packed_G2_D128")
+    runs = [run_hip(x, d=d) for _ in range(3)]
+    for o, l in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
+
+
+def test_count_probe_small():
+    """Mask inside the hot path: lse = ln(n_allowed) exactly decodes the oracle's counts."""
+    for name in ("packed_window", "tailpad_G4_D128", "window_G4_D64"):
+        x = count_probe_inputs(SMALL[name]())
+        announce(f"count probe: attn_fwd on {name}")
+        _, lse = run_hip(x)
+        cnt = oracle.mask(x["valid"], positions=x["positions"], window=x["window"])
+        got = counts_from_lse(lse)
+        for h in range(got.shape[-1]):
+            assert np.array_equal(got[..., h], cnt), f"{name} head {h}"
+
+
+def test_index_probe_decodes_key():
+    """Profile gather indexing: only distance r*(h,i) carries weight; v encodes the key."""
+    B, S, Hq, Hkv, D, E = 1, 300, 8, 2, 128, 70
+    x = W.custom(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, E=E, seed=120, structure="packed", doc_min=30, doc_max=150)
+    pos = x["positions"].numpy()
+    x["q"].zero_()
+    x["k"].zero_()
+    x["sink"].fill_(-math.inf)
+    h_idx = torch.arange(Hq)[:, None]
+    i_idx = torch.arange(S)[None, :]
+    n_i = torch.from_numpy(pos[0]).long()[None, :] + 1
+    rstar = (7 * h_idx + i_idx) % torch.clamp(n_i, max=E)
+    prof = torch.full((B, Hq, S, E), -30000.0)
+    prof[0].scatter_(2, rstar[..., None], 40.0)
+    x["profiles"] = prof
+    v = torch.zeros(B, S, Hkv, D)
+    j = torch.arange(S, dtype=torch.float32)
+    v[0, :, :, 0] = (j % 256)[:, None]
+    v[0, :, :, 1] = (j // 256)[:, None]
+    v[0, :, :, 2] = torch.arange(Hkv, dtype=torch.float32)[None, :]
+    x["v"] = v.to(torch.bfloat16)
+    announce("index probe: attn_fwd")
+    out, _ = run_hip(x)
+    dec = np.rint(out[0, :, :, 0]) + 256 * np.rint(out[0, :, :, 1])
+    expect = (np.arange(S)[:, None] - rstar.numpy().T)
+    assert np.array_equal(dec, expect)
+    assert np.array_equal(np.rint(out[0, :, :, 2]), np.repeat((np.arange(Hq) // (Hq // Hkv))[None, :], S, 0))
+
+
+def test_garbage_at_invalid_tokens():
+    x = W.custom(B=2, S=260, Hq=8, Hkv=2, D=128, E=50, seed=121, structure="tail_pad", max_tail_pad=60,
+                 window=100)
+    inv = ~x["valid"]
+    g = torch.Generator().manual_seed(9)
+    for name in ("q", "k", "v"):
+        t = x[name]
+        t[inv] = ((torch.rand(t[inv].shape, generator=g) - 0.5) * 2e4).to(t.dtype)
+    x["profiles"].permute(0, 2, 1, 3)[inv] = 1e4
+    x["sink"][inv] = 5e3
+    out, lse, _ = check_full(x, "garbage_invalid")
+    np.testing.assert_array_equal(lse[inv.numpy()], x["sink"].double().numpy()[inv.numpy()])
+
+
+@pytest.mark.parametrize("sink", [-math.inf, 30.0, -30.0])
+def test_sink_extremes(sink):
+    x = W.custom(B=1, S=257, Hq=4, Hkv=1, D=128, E=64, seed=122, structure="tail_pad", max_tail_pad=20)
+    x["sink"].fill_(sink)
+    check_full(x, f"sink={sink}")
+
+
+def test_all_invalid_and_empty_keys():
+    x = W.custom(B=1, S=130, Hq=4, Hkv=2, D=64, E=8, seed=123)
+    x["valid"].zero_()
+    out, lse, _ = check_full(x, "all_invalid")
+    assert np.all(out == 0)
+    # no keys at all (context-parallel call with an empty key range)
+    y = dict(x)
+    y["valid"] = torch.ones_like(x["valid"])
+    y["k"] = x["k"][:, :0].contiguous()
+    y["v"] = x["v"][:, :0].contiguous()
+    y["key_valid"] = torch.ones(1, 0, dtype=torch.bool)
+    y["key_positions"] = torch.zeros(1, 0, dtype=torch.int32)
+    y["query_offset"] = 64
+    announce("empty key range: attn_fwd Sk=0")
+    out, lse = run_hip(y)
+    assert np.all(out == 0)
+    np.testing.assert_allclose(lse, y["sink"].double().numpy(), atol=1e-5, rtol=0)
+
+
+def test_zero_rows_is_a_no_op():
+    x = W.custom(B=1, S=4, Hq=4, Hkv=2, D=128, E=8, seed=124)
+    d = to_device(x)
+    q = d["q"][:, :0].contiguous()
+    announce("B*Sq == 0: attn_fwd")
+    out, lse = binding.attn_fwd(q, d["k"], d["v"], d["profiles"][:, :, :0].contiguous(), d["sink"][:, :0].contiguous(),
+                                d["valid"][:, :0].contiguous(), key_valid=d["valid"], key_positions=d["positions"],
+                                query_offset=4)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and lse.numel() == 0
+
+
+def test_query_slice_with_offset():
+    """Context-parallel contract on one GPU: local queries [a, a+n) against global keys."""
+    x = W.custom(B=2, S=500, Hq=8, Hkv=2, D=128, E=90, seed=125, structure="packed", doc_min=40,
+                 doc_max=220, invalid_tail=9, window=150)
+    full_out, full_lse, _ = check_full(x, "cp_full")
+    a, n = 161, 211
+    y = dict(q=x["q"][:, a:a + n].contiguous(), k=x["k"], v=x["v"],
+             profiles=x["profiles"][:, :, a:a + n].contiguous(), sink=x["sink"][:, a:a + n].contiguous(),
+             valid=x["valid"][:, a:a + n].contiguous(), key_valid=x["valid"],
+             positions=x["positions"][:, a:a + n].contiguous(), key_positions=x["positions"],
+             window=150, query_offset=a)
+    out, lse, _ = check_full(y, "cp_slice")
+    np.testing.assert_allclose(out, full_out[:, a:a + n], atol=1e-6, rtol=0)
+    np.testing.assert_allclose(lse, full_lse[:, a:a + n], atol=1e-6, rtol=0)
+
+
+def test_debug_counts_and_tiles_match_oracle_mask():
+    for name in ("packed_window", "tailpad_G4_D128", "G16_two_chunks", "window_G4_D64"):
+        x = SMALL[name]()
+        d = to_device(x)
+        announce(f"debug counts/tiles: {name}")
+        cnt = binding.attn_debug_counts(d["valid"], positions=d["positions"], window=x["window"]).cpu().numpy()
+        tiles = binding.attn_debug_tiles(d["valid"], positions=d["positions"], window=x["window"]).cpu().numpy()
+        torch.cuda.synchronize()
+        ref_cnt, ref_mask = oracle.mask(x["valid"], positions=x["positions"], window=x["window"], full=True)
+        assert np.array_equal(cnt, ref_cnt), name
+        bm, bn = binding.attn_query_block(), binding.attn_key_tile()
+        B, S = x["valid"].shape
+        for b in range(B):
+            for qb in range(tiles.shape[1]):
+                for kt in range(tiles.shape[2]):
+                    blk = ref_mask[b, qb * bm:(qb + 1) * bm, kt * bn:(kt + 1) * bn]
+                    c = tiles[b, qb, kt]
+                    if c == 0:
+                        assert not blk.any(), f"{name}: skipped tile ({b},{qb},{kt}) holds allowed pairs"
+                    if c == 2:
+                        assert blk.shape == (bm, bn) and blk.all(), f"{name}: full tile ({b},{qb},{kt}) masked"
+
+
+# ------------------------------------------------------------------------------------------
+# full-size workloads, sampled rows (the benchmark's launch configuration)
+# ------------------------------------------------------------------------------------------
+FULL = ["causal_gqa", "local", "full_causal_8k", "packed", "long"]
+
+
+def _sample(x, n=40, seed=7):
+    w = x["workload"]
+    must = [(0, 0), (0, 1), (0, 31), (0, 32), (w.B - 1, w.S - 1), (w.B - 1, w.S - 2), (0, w.S // 2)]
+    for b, starts in enumerate(x["doc_starts"]):
+        for s in starts[:4]:
+            must += [(b, s), (b, min(w.S - 1, s + 1))]
+    valid = x["valid"].numpy()
+    for b in range(w.B):
+        nv = int(valid[b].sum())
+        if 0 < nv < w.S:
+            must += [(b, nv - 1), (b, nv)]
+    return W.sample_rows(w.B, w.S, n, seed, tuple(must))
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows_and_counts(name):
+    x = W.generate(W.WORKLOADS[name])
+    d = to_device(x)
+    rows = _sample(x)
+    check_rows(x, rows, name, d=d)
+    announce(f"{name}: attn_debug_counts all rows")
+    cnt = binding.attn_debug_counts(d["valid"], positions=d["positions"], window=x["window"]).cpu().numpy()
+    ref = oracle.mask(x["valid"], positions=x["positions"], window=x["window"])
+    assert np.array_equal(cnt, ref)
+
+
+@pytest.mark.parametrize("name", ["local", "packed", "causal_gqa"])
+def test_full_size_count_probe(name):
+    """lse = ln(n_allowed) for every row and head at full size: the hot path's mask is exact."""
+    x = count_probe_inputs(W.generate(W.WORKLOADS[name]))
+    announce(f"{name}: count probe attn_fwd full size")
+    _, lse = run_hip(x)
+    ref = oracle.mask(x["valid"], positions=x["positions"], window=x["window"])
+    got = counts_from_lse(lse)
+    assert np.array_equal(got, np.repeat(ref[..., None], got.shape[-1], axis=-1))

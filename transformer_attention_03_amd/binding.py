@@ -1,0 +1,291 @@
+"""Thin ctypes binding of libinkattn.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls (include/inkattn.h).
+PyTorch serves only as the owner of device memory and streams: every step of
+the forward runs in the library's HIP kernels.  There is no fallback: when the
+library is missing, or a tensor is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libinkattn.so")
+
+INKATTN_F32 = 0
+INKATTN_BF16 = 1
+STATUS = {0: "INKATTN_OK", 1: "INKATTN_ERR_NULL", 2: "INKATTN_ERR_SHAPE", 3: "INKATTN_ERR_UNSUPPORTED",
+          4: "INKATTN_ERR_ALIGN", 5: "INKATTN_ERR_WORKSPACE", 6: "INKATTN_ERR_LAUNCH"}
+
+# Every symbol include/inkattn.h declares.
+EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_fwd_planned",
+           "attn_debug_counts", "attn_debug_tiles",
+           "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class InkAttnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: run python -m transformer_attention_03_amd.build")
+            lib = ctypes.CDLL(LIB_PATH)
+            P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+            lib.attn_fwd_workspace_size.restype = SZ
+            lib.attn_fwd_workspace_size.argtypes = [I, I, I]
+            lib.attn_fwd.restype = I
+            lib.attn_fwd.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
+                                     I, I, I, I, I, I, I, P, P, P, SZ, P]
+            lib.attn_fwd_planned.restype = I
+            lib.attn_fwd_planned.argtypes = list(lib.attn_fwd.argtypes)
+            lib.attn_plan.restype = I
+            lib.attn_plan.argtypes = [P, P, P, P, I64, I, I, I, P, SZ, P]
+            lib.attn_debug_counts.restype = I
+            lib.attn_debug_counts.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P]
+            lib.attn_debug_tiles.restype = I
+            lib.attn_debug_tiles.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P, SZ, P]
+            lib.attn_status_string.restype = ctypes.c_char_p
+            lib.attn_status_string.argtypes = [I]
+            lib.attn_last_error.restype = ctypes.c_char_p
+            lib.attn_last_error.argtypes = []
+            lib.attn_query_block.restype = I
+            lib.attn_key_tile.restype = I
+            _lib = lib
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        lib = load()
+        raise InkAttnError(rc, where, lib.attn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtypes, device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _mask_tensor(t, name, device):
+    t = _dev(t, name, (torch.bool, torch.uint8), device)
+    return None if t is None else (t.view(torch.uint8) if t.dtype == torch.bool else t)
+
+
+def _pos_tensor(t, name, device):
+    t = _dev(t, name, (torch.int32, torch.int64), device)
+    if t is not None and t.dtype == torch.int64:
+        t = t.to(torch.int32)   # logical positions are below 2^30 by contract
+    return t
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_fwd_workspace_size(B: int, Sq: int, Sk: int) -> int:
+    return int(load().attn_fwd_workspace_size(B, Sq, Sk))
+
+
+def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_positions, window,
+                 query_offset, out, lse, workspace, stream):
+    dev = q.device
+    q = _dev(q, "q", (torch.bfloat16,), None)
+    k = _dev(k, "k", (torch.bfloat16,), dev)
+    v = _dev(v, "v", (torch.bfloat16,), dev)
+    profiles = _dev(profiles, "profiles", (torch.float32, torch.bfloat16), dev)
+    sink = _dev(sink, "sink", (torch.float32,), dev)
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or profiles.dim() != 4:
+        raise ValueError("q, k, v and profiles must be 4-d")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    E = profiles.shape[3]
+    expect = {"k": (k, (B, Sk, Hkv, D)), "v": (v, (B, Sk, Hkv, D)), "profiles": (profiles, (B, Hq, Sq, E)),
+              "sink": (sink, (B, Sq, Hq)), "valid": (valid_u8, (B, Sq)), "key_valid": (kvalid_u8, (B, Sk)),
+              "positions": (pos, (B, Sq)), "key_positions": (kpos, (B, Sk))}
+    for name, (t, shape) in expect.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        out = _dev(out, "out", (torch.float32,), dev)
+    if lse is None:
+        lse = torch.empty((B, Sq, Hq), dtype=torch.float32, device=dev)
+    else:
+        lse = _dev(lse, "lse", (torch.float32,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk), 16), dtype=torch.uint8, device=dev)
+    pdt = INKATTN_BF16 if profiles.dtype == torch.bfloat16 else INKATTN_F32
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(profiles), pdt, _ptr(sink), _ptr(valid_u8),
+            _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), 0 if window is None else int(window),
+            int(query_offset), B, Sq, Sk, Hq, Hkv, D, E, _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    # keep converted tensors alive until the call is enqueued
+    keep = (q, k, v, profiles, sink, valid_u8, kvalid_u8, pos, kpos, workspace)
+    return args, out, lse, keep
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.Tensor,
+             sink: torch.Tensor, valid: torch.Tensor, key_valid: Optional[torch.Tensor] = None,
+             positions: Optional[torch.Tensor] = None, key_positions: Optional[torch.Tensor] = None,
+             window: Optional[int] = None, query_offset: int = 0,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused forward (plan + attention).  Returns ``(out [B,Sq,Hq,D] fp32, lse [B,Sq,Hq] fp32)``.
+
+    Shapes: q [B,Sq,Hq,D] bf16; k, v [B,Sk,Hkv,D] bf16; profiles [B,Hq,Sq,E]
+    fp32/bf16; sink [B,Sq,Hq] fp32; valid [B,Sq] bool; key_valid [B,Sk] bool;
+    positions [B,Sq] / key_positions [B,Sk] int32/int64.  ``window`` None or
+    <= 0 means no window.  Asynchronous on ``stream`` (default: current).
+    """
+    args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
+                                        key_positions, window, query_offset, out, lse, workspace, stream)
+    _check(load().attn_fwd(*args), "attn_fwd")
+    del keep
+    return out, lse
+
+
+def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=None, key_positions=None,
+                     window=None, query_offset: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """The attention kernel alone, on a workspace filled by :func:`attn_plan` for the same masks."""
+    if workspace is None:
+        raise ValueError("attn_fwd_planned needs the workspace attn_plan filled")
+    args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
+                                        key_positions, window, query_offset, out, lse, workspace, stream)
+    _check(load().attn_fwd_planned(*args), "attn_fwd_planned")
+    del keep
+    return out, lse
+
+
+def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_offset: int = 0,
+              Sk: Optional[int] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Scheduler pre-pass: fills and returns the workspace for :func:`attn_fwd_planned`."""
+    dev = valid.device
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    B, Sq = valid_u8.shape
+    if Sk is None:
+        Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
+    if workspace is None:
+        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk), 16), dtype=torch.uint8, device=dev)
+    rc = load().attn_plan(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), int(query_offset), B, Sq, Sk,
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    _check(rc, "attn_plan")
+    return workspace
+
+
+def attn_debug_counts(valid, key_valid=None, positions=None, key_positions=None, window=None,
+                      query_offset: int = 0, Sk: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Allowed keys per query row, int32 [B, Sq], from the kernels' mask predicate."""
+    dev = valid.device
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    B, Sq = valid_u8.shape
+    if Sk is None:
+        Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
+    n = torch.empty((B, Sq), dtype=torch.int32, device=dev)
+    rc = load().attn_debug_counts(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos),
+                                  0 if window is None else int(window), int(query_offset), B, Sq, Sk,
+                                  _ptr(n), _stream(stream, dev))
+    _check(rc, "attn_debug_counts")
+    return n
+
+
+def attn_debug_tiles(valid, key_valid=None, positions=None, key_positions=None, window=None,
+                     query_offset: int = 0, Sk: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Tile classes uint8 [B, ceil(Sq/32), ceil(Sk/64)]: 0 skip, 1 masked, 2 full."""
+    dev = valid.device
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    B, Sq = valid_u8.shape
+    if Sk is None:
+        Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
+    bm, bn = attn_query_block(), attn_key_tile()
+    cls = torch.empty((B, -(-Sq // bm), -(-Sk // bn)), dtype=torch.uint8, device=dev)
+    need = attn_fwd_workspace_size(B, Sq, Sk)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    rc = load().attn_debug_tiles(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos),
+                                 0 if window is None else int(window), int(query_offset), B, Sq, Sk,
+                                 _ptr(cls), _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check(rc, "attn_debug_tiles")
+    return cls
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def attn_query_block() -> int:
+    return int(load().attn_query_block())
+
+
+def attn_key_tile() -> int:
+    return int(load().attn_key_tile())
+
+
+class LearnedRelativeAttention:
+    """Mirror of the pages' attention op: constructed with (head_dim, window).
+
+    ``forward`` takes the forward's tensors and returns ``(out, lse)``; the
+    logit scale head_dim^-0.5 is applied inside the kernel.
+    """
+
+    def __init__(self, head_dim: int, window: Optional[int]):
+        if head_dim not in (64, 128):
+            raise ValueError("head_dim must be 64 or 128")
+        self.head_dim = head_dim
+        self.window = window
+        self.scale = head_dim ** -0.5
+
+    def forward(self, q, k, v, profiles, sink, valid, key_valid=None, positions=None,
+                key_positions=None, query_offset: int = 0, stream=None):
+        if q.shape[-1] != self.head_dim:
+            raise ValueError(f"q head_dim {q.shape[-1]} != {self.head_dim}")
+        return attn_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_positions,
+                        self.window, query_offset, stream=stream)
+
+    __call__ = forward
