@@ -10,34 +10,41 @@
 // is in include/inkattn.h.
 //
 // Structure of one call:
-//   1. summarize_kernel (scheduler pre-pass): per 32-token query block and per
-//      64-key tile, the min / max document start column over real tokens and
-//      the number of real tokens.  Every skip / full / masked decision of the
-//      main kernel is taken from these summaries.
+//   1. summarize_kernel (scheduler pre-pass, one wave per tile): for every
+//      32-token query block and 64-key tile, the min / max document start
+//      column over real tokens and the number of real tokens.  Every skip /
+//      full / masked decision of the main kernel comes from these summaries.
 //   2. attn_fwd_kernel: one workgroup per (batch row, K/V head, head chunk,
-//      32-token query block), one wave per query head of the chunk.  Each
-//      64-key K/V tile is staged once in LDS and serves every query head of
-//      the group (GQA).  Per wave and tile:
-//        S^T = K Q^T      bf16 MFMA 32x32x16 (keys on M, queries on N), so that
-//                         each lane owns one query column and row reductions
-//                         are in-lane plus one exchange between wave halves;
-//        + relative bias  gathered from the query's own profile row: for a
-//                         32-key sub-tile the distances form one contiguous
-//                         run per row;
+//      group of 32-token query blocks); each wave owns one (query head,
+//      32-token block).  Each 64-key K/V tile is staged once in LDS and
+//      serves every wave of the workgroup, i.e. every query head of the chunk
+//      (GQA).  The next live tile's K/V loads are issued before the current
+//      tile is computed and land in the second LDS buffer (one barrier per
+//      tile).  Per wave and tile:
+//        S^T = K Q^T      bf16 MFMA 32x32x16, keys on M and queries on N, so
+//                         each lane owns one query column: row reductions are
+//                         in-lane plus one exchange between the wave halves;
+//        + relative bias  gathered from the query's own profile row; for a
+//                         32-key sub-tile the distances of a row are one
+//                         contiguous run (loaded 4 at a time);
 //        mask             only on tiles classed as masked;
 //        online softmax   running max / denominator per lane, started from
 //                         the sink logit (the sink's weight enters the
-//                         denominator, never the value sum);
+//                         denominator, never the value sum); the running max
+//                         is only moved when a row's tile max exceeds it by
+//                         more than 8 (log2 units), so probabilities stay
+//                         <= 2^8 and most tiles skip the output rescale;
 //        O^T += V^T P^T   fp16 MFMA 32x32x16; P^T comes straight from the S^T
-//                         accumulator registers (the key order inside each
-//                         16-key step is permuted consistently on both
-//                         operands), V is stored transposed in LDS.
-//      Epilogue: out = O / l, lse = m + ln l.
+//                         accumulator registers (keys inside each 16-key step
+//                         are permuted the same way on both operands) and V^T
+//                         is read from row-major LDS with the transposing
+//                         ds_read_b64_tr_b16.
+//      Epilogue: out = O / l, lse = ln(2) * (m + log2 l).
 #include <hip/hip_runtime.h>
 
 #include <climits>
-#include <cstdarg>
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -48,17 +55,19 @@ namespace {
 
 constexpr int BM = 32;   // query tokens per wave (MFMA N)
 constexpr int BN = 64;   // keys per K/V tile (two MFMA M-blocks of 32)
-constexpr int MAX_HPW = 8;  // query heads (waves) per workgroup, at most
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_u __attribute__((ext_vector_type(4), aligned(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Per-tile summary written by the pre-pass: document start columns of the
 // tile's real tokens (min, max) and how many real tokens it has.
@@ -83,7 +92,6 @@ __device__ __forceinline__ bool key_visible(int gi_eff, int a_q, int j, int c_k,
     return (unsigned)(gi_eff - j) < wlim && c_k == a_q;
 }
 
-// Tile classes.
 enum : int { TILE_SKIP = 0, TILE_MASKED = 1, TILE_FULL = 2 };
 
 // Class of (query block, key tile) from the two summaries and the column
@@ -93,10 +101,10 @@ __device__ __forceinline__ int classify_tile(const TileSummary& qs, int qlo, int
                                              const TileSummary& ks, int j0, int key_hi, int kcount,
                                              int window)
 {
-    if (qs.nvalid == 0 || ks.nvalid == 0) return TILE_SKIP;
-    if (j0 > qhi) return TILE_SKIP;                              // causal
-    if (ks.amax < qs.amin || ks.amin > qs.amax) return TILE_SKIP;  // no common document
-    if (window > 0 && qlo - key_hi >= window) return TILE_SKIP;  // nearest pair outside the window
+    if (qcount <= 0 || qs.nvalid == 0 || ks.nvalid == 0) return TILE_SKIP;
+    if (j0 > qhi) return TILE_SKIP;                                 // causal
+    if (ks.amax < qs.amin || ks.amin > qs.amax) return TILE_SKIP;   // no common document
+    if (window > 0 && qlo - key_hi >= window) return TILE_SKIP;     // nearest pair outside the window
     const bool one_doc = qs.amin == qs.amax && ks.amin == ks.amax && qs.amin == ks.amin;
     const bool all_real = qs.nvalid == qcount && ks.nvalid == kcount && qcount == BM && kcount == BN;
     const bool causal_full = key_hi <= qlo;
@@ -105,30 +113,57 @@ __device__ __forceinline__ int classify_tile(const TileSummary& qs, int qlo, int
 }
 
 // ---------------------------------------------------------------------------
-// Scheduler pre-pass: one thread per (batch row, tile).
+// Scheduler pre-pass: one wave per (batch row, tile); query tiles first, then
+// key tiles, in one launch.
 // ---------------------------------------------------------------------------
-__global__ void summarize_kernel(const uint8_t* __restrict__ valid,
-                                 const int32_t* __restrict__ positions,  // may be NULL: column
-                                 int col0, int S, int B, int tile, int ntiles,
-                                 TileSummary* __restrict__ out)
+__device__ __forceinline__ int wave_min(int x)
 {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= B * ntiles) return;
-    const int b = idx / ntiles, t = idx - b * ntiles;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_max(int x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__global__ __launch_bounds__(256) void summarize_kernel(
+    const uint8_t* __restrict__ valid, const int32_t* __restrict__ positions, int qoff, int Sq, int nQB,
+    const uint8_t* __restrict__ key_valid, const int32_t* __restrict__ key_positions, int Sk, int nKT,
+    int B, TileSummary* __restrict__ qsum, TileSummary* __restrict__ ksum)
+{
+    const int w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int nq = B * nQB;
+    if (w >= nq + B * nKT) return;   // whole wave exits together
+    const bool is_q = w < nq;
+    const int t = is_q ? w : w - nq;
+    const int ntiles = is_q ? nQB : nKT;
+    const int b = t / ntiles, tile = t - b * ntiles;
+    const int size = is_q ? BM : BN;
+    const int S = is_q ? Sq : Sk;
+    const uint8_t* vld = is_q ? valid : key_valid;
+    const int32_t* pos = is_q ? positions : key_positions;
+    const int col0 = is_q ? qoff : 0;
+    const int i = tile * size + lane;
     int amin = INT_MAX, amax = INT_MIN, n = 0;
-    const int lo = t * tile, hi = min(S, lo + tile);
-    for (int i = lo; i < hi; ++i) {
+    if (lane < size && i < S) {
         const size_t o = (size_t)b * S + i;
-        if (!valid[o]) continue;
-        const int col = col0 + i;
-        const int a = positions ? col - positions[o] : 0;
-        amin = min(amin, a);
-        amax = max(amax, a);
-        ++n;
+        if (vld[o]) {
+            const int a = pos ? col0 + i - pos[o] : 0;
+            amin = a; amax = a; n = 1;
+        }
     }
-    TileSummary s;
-    s.amin = amin; s.amax = amax; s.nvalid = n; s.pad = 0;
-    out[idx] = s;
+    amin = wave_min(amin);
+    amax = wave_max(amax);
+    n = __popcll(__builtin_amdgcn_ballot_w64(n != 0));
+    if (lane == 0) {
+        TileSummary s;
+        s.amin = amin; s.amax = amax; s.nvalid = n; s.pad = 0;
+        (is_q ? qsum : ksum)[t] = s;
+    }
 }
 
 struct FwdParams {
@@ -148,49 +183,74 @@ struct FwdParams {
     int B, Sq, Sk, Hq, Hkv, G, E;
     int window;      // <= 0: none
     int qoff;        // query_offset
-    int hpw;         // query heads per workgroup (= waves)
+    int hpw;         // query heads per workgroup
+    int tpw;         // 32-token query blocks per workgroup (hpw * tpw == waves)
     int nchunk;      // head chunks per K/V head (G / hpw)
-    int nQB, nKT;
+    int nQB, nQG, nKT;
     float c_log2;    // head_dim^-0.5 * log2(e)
 };
 
-__device__ __forceinline__ float wave_half_swap(float x)
+// Max / sum of a value and its twin in the other wave half (same query).
+__device__ __forceinline__ float half_max(float x)
 {
-    return __shfl_xor(x, 32, 64);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-template <int D, bool PROF_BF16>
-__global__ __launch_bounds__(64 * MAX_HPW) void attn_fwd_kernel(FwdParams p)
-{
-    constexpr int NKK = D / 16;   // k-steps of S^T = K Q^T
-    constexpr int NDB = D / 32;   // 32-row d-blocks of O^T
-    constexpr int KS = D + 8;     // K row stride in LDS (bf16 elements)
-    constexpr int VTS = BN + 4;   // V^T row stride in LDS (f16 elements)
+// Tile descriptor carried through the software pipeline.
+struct TileDesc {
+    int kt;        // tile index (> kt_hi: none)
+    int my_cls;    // this wave's class
+    int masked;    // some wave of the workgroup masks this tile
+    int partial;   // the tile holds keys that are not real or lie past Sk
+};
 
-    __shared__ __attribute__((aligned(16))) __bf16 k_lds[BN * KS];
-    __shared__ __attribute__((aligned(16))) _Float16 vt_lds[D * VTS];
-    __shared__ __attribute__((aligned(16))) int ca_lds[BN];
+template <int D, bool PROF_BF16, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdParams p)
+{
+    constexpr int NT = 64 * NW;
+    constexpr int NKK = D / 16;            // k-steps of S^T = K Q^T
+    constexpr int NDB = D / 32;            // 32-row d-blocks of O^T
+    constexpr int KS = D + 8;              // K row stride in LDS (bf16): conflict-free b128 reads
+    constexpr int VS = D + 32;             // V row stride in LDS (f16): conflict-free transposing reads
+    constexpr int CPR = D / 8;             // 16-byte chunks per K / V row
+    constexpr int NCH = BN * CPR / NT;     // chunks per thread per tile
+    static_assert(BN * CPR % NT == 0, "tile chunks must divide among threads");
+
+    __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KS];
+    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][BN * VS];
+    __shared__ __attribute__((aligned(16))) int ca_lds[2][BN];
 
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int qi = lane & 31;      // this lane's query within the block
     const int hh = lane >> 5;      // wave half
 
-    // ---- work item: heads fastest so that consecutive workgroups share K/V
-    // in one XCD's L2; query blocks in decreasing order (longest first).
+    // ---- work item: head groups fastest, then batch rows, then query groups in
+    // decreasing order (longest first for causal work).
     int idx = blockIdx.x;
     const int ngroups = p.Hkv * p.nchunk;
     const int hgi = idx % ngroups; idx /= ngroups;
     const int b = idx % p.B; idx /= p.B;
-    const int qb = p.nQB - 1 - idx;
+    const int qg = p.nQG - 1 - idx;
     const int g = hgi / p.nchunk;
-    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + wave;
+    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + wave % p.hpw;
+    const int qb = qg * p.tpw + wave / p.hpw;        // this wave's query block (may be past the end)
     const int i0 = qb * BM;
 
+    // query blocks of the workgroup: qg*tpw .. qg*tpw + tpw - 1
+    const int qb_first = qg * p.tpw;
+    const int qb_last = min(p.nQB - 1, qb_first + p.tpw - 1);
+
     const int i = i0 + qi;
-    const bool qin = i < p.Sq;
+    const bool qin = qb < p.nQB && i < p.Sq;
     const size_t qrow = (size_t)b * p.Sq + i;
     const int gi = p.qoff + i;
     const bool qreal = qin && p.valid[qrow] != 0;
@@ -204,10 +264,7 @@ __global__ __launch_bounds__(64 * MAX_HPW) void attn_fwd_kernel(FwdParams p)
     {
         const __bf16* qp = p.q + (qrow * p.Hq + h) * D + 8 * hh;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            if (qin) qreg[kk] = *(const bf16x8*)(qp + 16 * kk);
-            else qreg[kk] = bf16x8{};
-        }
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = qin ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
     }
 
     // Online-softmax state (log2 units).  The sink's weight e^{s - m} counts
@@ -218,202 +275,256 @@ __global__ __launch_bounds__(64 * MAX_HPW) void attn_fwd_kernel(FwdParams p)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-    // ---- key-tile range of this query block
-    const TileSummary qs = p.qsum[(size_t)b * p.nQB + qb];
-    const int qcount = min(BM, p.Sq - i0);
+    // ---- this wave's block and the workgroup's key-tile range
+    int qcount = 0;
+    if (qb < p.nQB) qcount = min(BM, p.Sq - i0);
     const int qlo = p.qoff + i0, qhi = p.qoff + i0 + qcount - 1;
-    int jlo = 0;
-    if (qs.nvalid > 0) jlo = max(jlo, qs.amin);            // key j >= its start column
-    if (p.window > 0) jlo = max(jlo, qlo - p.window + 1);
-    const int jhi = min(p.Sk - 1, qhi);
-    const int kt_lo = jlo / BN;
-    const int kt_hi = (qs.nvalid > 0 && jhi >= 0) ? jhi / BN : -1;
 
-    const size_t prof_row = ((size_t)b * p.Hq + h) * p.Sq + i;  // row of profiles[b,h,i,:]
+    int jlo = INT_MAX, jhi = -1;
+    for (int x = qb_first; x <= qb_last; ++x) {
+        const TileSummary s = p.qsum[(size_t)b * p.nQB + x];
+        if (s.nvalid == 0) continue;
+        const int xlo = p.qoff + x * BM;
+        const int xhi = p.qoff + min(p.Sq, x * BM + BM) - 1;
+        int lo = max(0, s.amin);                         // key j >= its start column
+        if (p.window > 0) lo = max(lo, xlo - p.window + 1);
+        jlo = min(jlo, lo);
+        jhi = max(jhi, min(p.Sk - 1, xhi));
+    }
+    const int kt_lo = jhi >= 0 ? jlo / BN : 0;
+    const int kt_hi = jhi >= 0 ? jhi / BN : -1;
 
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-        const int j0 = kt * BN;
+    // Next tile after `kt` that some wave of the workgroup needs.
+    auto next_live = [&](int kt) -> TileDesc {
+        TileDesc d;
+        for (++kt; kt <= kt_hi; ++kt) {
+            const int j0 = kt * BN;
+            const int kcount = min(BN, p.Sk - j0);
+            const TileSummary ks = p.ksum[(size_t)b * p.nKT + kt];
+            int any = 0, masked = 0, mine = TILE_SKIP;
+            for (int x = qb_first; x <= qb_last; ++x) {
+                const TileSummary s = p.qsum[(size_t)b * p.nQB + x];
+                const int xc = min(BM, p.Sq - x * BM);
+                const int xlo = p.qoff + x * BM;
+                const int c = classify_tile(s, xlo, xlo + xc - 1, xc, ks, j0, j0 + kcount - 1, kcount, p.window);
+                any |= c != TILE_SKIP;
+                masked |= c == TILE_MASKED;
+                if (x == qb) mine = c;
+            }
+            if (any) {
+                d.kt = kt; d.my_cls = mine; d.masked = masked;
+                d.partial = ks.nvalid != BN || kcount != BN;
+                return d;
+            }
+        }
+        d.kt = kt_hi + 1; d.my_cls = TILE_SKIP; d.masked = 0; d.partial = 0;
+        return d;
+    };
+
+    // K / V chunk c of a tile: row c / CPR, 8 elements at column 8 * (c % CPR).
+    bf16x8 kreg[NCH], vreg[NCH];
+    int careg = INT_MIN;
+    auto issue_loads = [&](const TileDesc& d) {
+        const int j0 = d.kt * BN;
         const int kcount = min(BN, p.Sk - j0);
-        const TileSummary ks = p.ksum[(size_t)b * p.nKT + kt];
-        const int cls = classify_tile(qs, qlo, qhi, qcount, ks, j0, j0 + kcount - 1, kcount, p.window);
-        if (cls == TILE_SKIP) continue;   // uniform over the workgroup
-
-        // ---- stage K (row-major, padded) and V^T (fp16) for this tile
-        __syncthreads();
-        {
-            constexpr int CPR = D / 8;   // 16-byte chunks per K row
-            for (int c = tid; c < BN * CPR; c += nthr) {
-                const int row = c / CPR, col = c - row * CPR;
-                const int j = j0 + row;
-                bf16x8 val = bf16x8{};
-                if (row < kcount)
-                    val = *(const bf16x8*)(p.k + (((size_t)b * p.Sk + j) * p.Hkv + g) * D + 8 * col);
-                *(bf16x8*)(k_lds + row * KS + 8 * col) = val;
-            }
-            for (int u = tid; u < (BN / 4) * (D / 8); u += nthr) {
-                const int kg = u & 15, dg = u >> 4;
-                bf16x8 rows[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int jl = 4 * kg + rr;
-                    const int j = j0 + jl;
-                    bool ok = jl < kcount;
-                    if (ok && cls != TILE_FULL) ok = p.key_valid[(size_t)b * p.Sk + j] != 0;
-                    rows[rr] = ok ? *(const bf16x8*)(p.v + (((size_t)b * p.Sk + j) * p.Hkv + g) * D + 8 * dg)
-                                  : bf16x8{};
-                }
-#pragma unroll
-                for (int dd = 0; dd < 8; ++dd) {
-                    f16x4 col;
-                    col[0] = (_Float16)(float)rows[0][dd];
-                    col[1] = (_Float16)(float)rows[1][dd];
-                    col[2] = (_Float16)(float)rows[2][dd];
-                    col[3] = (_Float16)(float)rows[3][dd];
-                    *(f16x4*)(vt_lds + (8 * dg + dd) * VTS + 4 * kg) = col;
-                }
-            }
-            if (cls == TILE_MASKED) {
-                for (int t = tid; t < BN; t += nthr) {
-                    const int j = j0 + t;
-                    int c = INT_MIN;
-                    if (t < kcount) {
-                        const size_t o = (size_t)b * p.Sk + j;
-                        if (p.key_valid[o]) c = p.key_positions ? j - p.key_positions[o] : 0;
-                    }
-                    ca_lds[t] = c;
-                }
+        for (int u = 0; u < NCH; ++u) {
+            const int c = tid + u * NT;
+            const int row = c / CPR, col = c - row * CPR;
+            const int j = j0 + row;
+            bool ok = row < kcount;
+            const size_t off = (((size_t)b * p.Sk + j) * p.Hkv + g) * D + 8 * col;
+            kreg[u] = ok ? *(const bf16x8*)(p.k + off) : bf16x8{};
+            if (ok && d.partial) ok = p.key_valid[(size_t)b * p.Sk + j] != 0;   // zero values of keys that are not real
+            vreg[u] = ok ? *(const bf16x8*)(p.v + off) : bf16x8{};
+        }
+        if (d.masked && tid < BN) {
+            careg = INT_MIN;
+            if (tid < kcount) {
+                const int j = j0 + tid;
+                const size_t o = (size_t)b * p.Sk + j;
+                if (p.key_valid[o]) careg = p.key_positions ? j - p.key_positions[o] : 0;
             }
         }
-        __syncthreads();
-
-        // ---- S^T = K Q^T for the two 32-key sub-tiles
-        f32x16 sacc[2];
+    };
+    auto store_lds = [&](const TileDesc& d, int buf) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            sacc[s] = f32x16{};
-            const __bf16* kp = k_lds + (32 * s + qi) * KS + 8 * hh;
+        for (int u = 0; u < NCH; ++u) {
+            const int c = tid + u * NT;
+            const int row = c / CPR, col = c - row * CPR;
+            *(bf16x8*)(&k_lds[buf][row * KS + 8 * col]) = kreg[u];
+            f16x8 vh;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const bf16x8 a = *(const bf16x8*)(kp + 16 * kk);
-                sacc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[s], 0, 0, 0);
-            }
+            for (int e = 0; e < 8; ++e) vh[e] = (_Float16)(float)vreg[u][e];
+            *(f16x8*)(&v_lds[buf][row * VS + 8 * col]) = vh;
         }
+        if (d.masked && tid < BN) ca_lds[buf][tid] = careg;
+    };
 
-        // ---- logits in log2 units: u = (scale * s + bias) * log2(e)
-        // Element (s, jj, e) is key j0 + 32 s + 8 jj + 4 hh + e.
-        float u[2][16];
+    const size_t prof_row = ((size_t)b * p.Hq + h) * p.Sq + i;   // row of profiles[b,h,i,:]
+    // V^T operand addressing for the transposing read: lane supplies row
+    // (lane%16)/4 of its 4-key group and column 4*(lane%4) of its 16-wide
+    // d-half; the read hands lane l the 4 keys of d = 16*((l/16)%2) + l%16.
+    const int v_lane_off = (4 * hh + (lane & 15) / 4) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    TileDesc cur = next_live(kt_lo - 1);
+    if (cur.kt <= kt_hi) {
+        issue_loads(cur);
+        store_lds(cur, 0);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (cur.kt <= kt_hi) {
+        const TileDesc nxt = next_live(cur.kt);
+        const int j0 = cur.kt * BN;
+
+        if (cur.my_cls != TILE_SKIP) {
+            // ---- relative bias for both 32-key sub-tiles (issued before the prefetch)
+            float bias[2][16];
+            bool has_bias[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int js = j0 + 32 * s;
-            const int rmin = qlo - (js + 31), rmax = qhi - js;   // distance range of the sub-tile
-            const int R = gi - js;                               // this lane's distance to key js
-            float bias[16];
+            for (int s = 0; s < 2; ++s) {
+                const int js = j0 + 32 * s;
+                const int rmin = qlo - (js + 31), rmax = qhi - js;   // distance range of the sub-tile
+                const int R = gi - js;                               // this lane's distance to key js
+                has_bias[s] = rmin < p.E;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) bias[t] = 0.0f;
-            if (rmin < p.E) {
-                if (rmin >= 0 && rmax < p.E) {
-                    // every distance of the sub-tile lies inside [0, E): one run per 4 keys
-                    if (qin) {
+                for (int t = 0; t < 16; ++t) bias[s][t] = 0.0f;
+                if (rmin < p.E && qin) {
+                    if (rmin >= 0 && rmax < p.E) {
+                        // every distance of the sub-tile lies inside [0, E): one run per 4 keys
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
                             const int rb = R - 8 * jj - 4 * hh - 3;
                             if (PROF_BF16) {
                                 const __bf16* pr = (const __bf16*)p.profiles + prof_row * p.E + rb;
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) bias[4 * jj + e] = (float)pr[3 - e];
+                                for (int e = 0; e < 4; ++e) bias[s][4 * jj + e] = (float)pr[3 - e];
                             } else {
                                 const f32x4_u w = *(const f32x4_u*)((const float*)p.profiles + prof_row * p.E + rb);
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) bias[4 * jj + e] = w[3 - e];
+                                for (int e = 0; e < 4; ++e) bias[s][4 * jj + e] = w[3 - e];
                             }
                         }
-                    }
-                } else if (qin) {
+                    } else {
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
+                        for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int r = R - 8 * jj - 4 * hh - e;
-                            if (r >= 0 && r < p.E) {
-                                if (PROF_BF16)
-                                    bias[4 * jj + e] = (float)((const __bf16*)p.profiles)[prof_row * p.E + r];
-                                else
-                                    bias[4 * jj + e] = ((const float*)p.profiles)[prof_row * p.E + r];
+                            for (int e = 0; e < 4; ++e) {
+                                const int r = R - 8 * jj - 4 * hh - e;
+                                if (r >= 0 && r < p.E) {
+                                    if (PROF_BF16)
+                                        bias[s][4 * jj + e] = (float)((const __bf16*)p.profiles)[prof_row * p.E + r];
+                                    else
+                                        bias[s][4 * jj + e] = ((const float*)p.profiles)[prof_row * p.E + r];
+                                }
                             }
                         }
                     }
                 }
             }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) u[s][t] = sacc[s][t] * p.c_log2 + bias[t] * LOG2E;
-        }
 
-        if (cls == TILE_MASKED) {
+            if (nxt.kt <= kt_hi) issue_loads(nxt);
+
+            // ---- S^T = K Q^T for the two 32-key sub-tiles
+            f32x16 sacc[2] = {f32x16{}, f32x16{}};
+            const __bf16* kp = &k_lds[buf][qi * KS + 8 * hh];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const bf16x8 a0 = *(const bf16x8*)(kp + 16 * kk);
+                const bf16x8 a1 = *(const bf16x8*)(kp + 32 * KS + 16 * kk);
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], sacc[1], 0, 0, 0);
+            }
+
+            // ---- logits in log2 units.  Element (s, jj, e) is key j0 + 32 s + 8 jj + 4 hh + e.
+            float u[2][16];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (has_bias[s]) {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) u[s][t] = __builtin_fmaf(sacc[s][t], p.c_log2, bias[s][t] * LOG2E);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) u[s][t] = sacc[s][t] * p.c_log2;
+                }
+            }
+            if (cur.my_cls == TILE_MASKED) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int kl = 32 * s + 8 * jj + 4 * hh;
+                        const i32x4 c4 = *(const i32x4*)(&ca_lds[buf][kl]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (!key_visible(gi_eff, a_q, j0 + kl + e, c4[e], wlim)) u[s][4 * jj + e] = -INFINITY;
+                    }
+                }
+            }
+
+            // ---- online softmax (sink-initialised, lazily rescaled)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) mx = fmaxf(mx, u[s][t]);
+            mx = half_max(mx);
+            const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
+            const float m_new = move ? mx : m;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+            }
+            m = m_new;
+            float lsum = 0.0f;
+            f16x8 pb[2][2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int kl = 32 * s + 8 * jj + 4 * hh;
-                    const i32x4 c4 = *(const i32x4*)(ca_lds + kl);
+                for (int t = 0; t < 16; ++t) {
+                    const float pv = __builtin_amdgcn_exp2f(u[s][t] - m_use);
+                    lsum += pv;
+                    // 16-key step c of sub-tile s takes elements jj = 2c, 2c+1
+                    pb[s][t >> 3][t & 7] = (_Float16)pv;
+                }
+            }
+            l += lsum;
+
+            // ---- O^T += V^T P^T
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (!key_visible(gi_eff, a_q, j0 + kl + e, c4[e], wlim)) u[s][4 * jj + e] = -INFINITY;
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const _Float16* vb = &v_lds[buf][(32 * s + 16 * c) * VS + v_lane_off];
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 32 * db));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 32 * db + 8 * VS));
+                        // whole-vector reinterpretation: keys 4hh+0..3 then 8+4hh+0..3
+                        const s16x8 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const f16x8 a = __builtin_bit_cast(f16x8, lohi);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[s][c], oacc[db], 0, 0, 0);
                     }
                 }
             }
+        } else if (nxt.kt <= kt_hi) {
+            issue_loads(nxt);
         }
 
-        // ---- online softmax (sink-initialised)
-        float mx = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int t = 0; t < 16; ++t) mx = fmaxf(mx, u[s][t]);
-        mx = fmaxf(mx, wave_half_swap(mx));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        float lsum = 0.0f;
-        f16x8 pb[2][2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const float pv = __builtin_amdgcn_exp2f(u[s][t] - m_use);
-                lsum += pv;
-                // 16-key step c of sub-tile s takes elements jj = 2c, 2c+1
-                pb[s][t >> 3][t & 7] = (_Float16)pv;
-            }
-        }
-        l = l * alpha + lsum;
-        if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-        }
-        m = m_new;
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int kb = 32 * s + 16 * c + 4 * hh;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const _Float16* vp = vt_lds + (32 * db + qi) * VTS + kb;
-                    const f16x4 lo = *(const f16x4*)(vp);
-                    const f16x4 hi = *(const f16x4*)(vp + 8);
-                    const f16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[s][c], oacc[db], 0, 0, 0);
-                }
-            }
-        }
+        if (nxt.kt <= kt_hi) store_lds(nxt, buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
     }
 
     // ---- epilogue
-    const float l_tot = l + wave_half_swap(l);
+    const float l_tot = half_sum(l);
     if (!qin) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     float* op = p.out + (qrow * p.Hq + h) * D;
@@ -520,8 +631,8 @@ struct MaskArgs {
 };
 
 int resolve_mask_args(const uint8_t* valid, const uint8_t* key_valid, const int32_t* positions,
-                      const int32_t* key_positions, int64_t window, int64_t query_offset,
-                      int B, int Sq, int Sk, MaskArgs* outa)
+                      const int32_t* key_positions, int64_t query_offset, int B, int Sq, int Sk,
+                      MaskArgs* outa)
 {
     if (B < 0 || Sq < 0 || Sk < 0) return fail(INKATTN_ERR_SHAPE, "negative size (B=%d Sq=%d Sk=%d)", B, Sq, Sk);
     if (Sq >= (1 << 30) || Sk >= (1 << 30)) return fail(INKATTN_ERR_SHAPE, "Sq / Sk must be below 2^30");
@@ -553,31 +664,73 @@ int check_launch(const char* what)
     return INKATTN_OK;
 }
 
+int check_workspace(void* workspace, size_t workspace_bytes, int B, int Sq, int Sk)
+{
+    const size_t need = summaries_bytes(B, Sq, Sk);
+    if (!workspace || workspace_bytes < need)
+        return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+    if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
+    return INKATTN_OK;
+}
+
 int launch_summaries(const uint8_t* valid, const int32_t* positions, const uint8_t* key_valid,
                      const int32_t* key_positions, int qoff, int B, int Sq, int Sk,
                      TileSummary* qsum, TileSummary* ksum, hipStream_t st)
 {
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
-    if (B * nQB > 0) {
-        const int n = B * nQB;
-        hipLaunchKernelGGL(summarize_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st,
-                           valid, positions, qoff, Sq, B, BM, nQB, qsum);
-        if (int rc = check_launch("summarize_kernel(queries)")) return rc;
-    }
-    if (B * nKT > 0) {
-        const int n = B * nKT;
-        hipLaunchKernelGGL(summarize_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st,
-                           key_valid, key_positions, 0, Sk, B, BN, nKT, ksum);
-        if (int rc = check_launch("summarize_kernel(keys)")) return rc;
-    }
+    const long long waves = (long long)B * (nQB + nKT);
+    if (waves == 0) return INKATTN_OK;
+    if (waves >= (1LL << 31)) return fail(INKATTN_ERR_SHAPE, "too many tiles");
+    const int blocks = (int)((waves + 3) / 4);
+    hipLaunchKernelGGL(summarize_kernel, dim3(blocks), dim3(256), 0, st, valid, positions, qoff, Sq, nQB,
+                       key_valid, key_positions, Sk, nKT, B, qsum, ksum);
+    return check_launch("summarize_kernel");
+}
+
+// Checks of attn_fwd / attn_fwd_planned that need no device access.
+int check_fwd_args(const void* q, const void* k, const void* v, const void* profiles, int profiles_dtype,
+                   const float* sink, int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                   float* out, float* lse)
+{
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(INKATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+    if (E < 1) return fail(INKATTN_ERR_SHAPE, "relative extent E=%d must be >= 1", E);
+    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
+    if (profiles_dtype != INKATTN_F32 && profiles_dtype != INKATTN_BF16)
+        return fail(INKATTN_ERR_UNSUPPORTED, "profiles dtype %d unknown", profiles_dtype);
+    const size_t nq_elems = (size_t)B * Sq * Hq * D;
+    const size_t np_elems = (size_t)B * Hq * Sq * E;
+    if (nq_elems >= (size_t(1) << 40) || np_elems >= (size_t(1) << 40))
+        return fail(INKATTN_ERR_SHAPE, "tensor too large");
+    if ((size_t)B * Sq == 0) return INKATTN_OK;
+    if (!q || !profiles || !sink || !out || !lse) return fail(INKATTN_ERR_NULL, "q/profiles/sink/out/lse is NULL");
+    if (Sk > 0 && (!k || !v)) return fail(INKATTN_ERR_NULL, "k or v is NULL");
+    if (!aligned(q, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))) || !aligned(out, 16))
+        return fail(INKATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+    if (!aligned(profiles, profiles_dtype == INKATTN_F32 ? 4 : 2) || !aligned(sink, 4) || !aligned(lse, 4))
+        return fail(INKATTN_ERR_ALIGN, "profiles / sink / lse misaligned");
     return INKATTN_OK;
 }
 
-int heads_per_workgroup(int G)
+// Workgroup shape: 4 waves; heads per workgroup hpw divides G; hpw * tpw = 4.
+struct Shape {
+    int nw, hpw, tpw;
+};
+
+Shape choose_shape(int G)
 {
-    for (int d = MAX_HPW; d >= 1; --d)
-        if (G % d == 0) return d;
-    return 1;
+    Shape s;
+    s.nw = 4;
+    s.hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    s.tpw = s.nw / s.hpw;
+    return s;
+}
+
+template <int D, bool PB>
+void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
+{
+    (void)sh;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PB, 4>), grid, dim3(256), 0, st, p);
 }
 
 }  // namespace
@@ -616,13 +769,10 @@ int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
 {
     g_last_error[0] = '\0';
     MaskArgs ma;
-    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, 0, query_offset, B, Sq, Sk, &ma))
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
-    if ((size_t)B * (Sq + Sk) == 0) return INKATTN_OK;
-    const size_t need = summaries_bytes(B, Sq, Sk);
-    if (!workspace || workspace_bytes < need)
-        return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
+    if ((size_t)B * ((size_t)Sq + Sk) == 0) return INKATTN_OK;
+    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
     const int nQB = ceil_div(Sq, BM);
     TileSummary* qsum = (TileSummary*)workspace;
     TileSummary* ksum = qsum + (size_t)B * nQB;
@@ -640,37 +790,18 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
                      void* workspace, size_t workspace_bytes, void* stream)
 {
     g_last_error[0] = '\0';
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-        return fail(INKATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
-    if (E < 1) return fail(INKATTN_ERR_SHAPE, "relative extent E=%d must be >= 1", E);
-    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
-    if (profiles_dtype != INKATTN_F32 && profiles_dtype != INKATTN_BF16)
-        return fail(INKATTN_ERR_UNSUPPORTED, "profiles dtype %d unknown", profiles_dtype);
+    if (int rc = check_fwd_args(q, k, v, profiles, profiles_dtype, sink, B, Sq, Sk, Hq, Hkv, D, E, out, lse))
+        return rc;
     MaskArgs ma;
-    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, window, query_offset,
-                                   B, Sq, Sk, &ma))
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if (window >= (int64_t(1) << 31) || window < 0) window = 0;
-    const size_t nq_elems = (size_t)B * Sq * Hq * D;
-    const size_t np_elems = (size_t)B * Hq * Sq * E;
-    if (nq_elems >= (size_t(1) << 40) || np_elems >= (size_t(1) << 40))
-        return fail(INKATTN_ERR_SHAPE, "tensor too large");
     if ((size_t)B * Sq == 0) return INKATTN_OK;   // nothing to write
-    if (!q || !profiles || !sink || !out || !lse) return fail(INKATTN_ERR_NULL, "q/profiles/sink/out/lse is NULL");
-    if (Sk > 0 && (!k || !v)) return fail(INKATTN_ERR_NULL, "k or v is NULL");
-    if (!aligned(q, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))) || !aligned(out, 16))
-        return fail(INKATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
-    if (!aligned(profiles, profiles_dtype == INKATTN_F32 ? 4 : 2) || !aligned(sink, 4) || !aligned(lse, 4))
-        return fail(INKATTN_ERR_ALIGN, "profiles / sink / lse misaligned");
-    const size_t need = summaries_bytes(B, Sq, Sk);
-    if (!workspace || workspace_bytes < need)
-        return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
 
     hipStream_t st = (hipStream_t)stream;
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
-    TileSummary* qsum = (TileSummary*)workspace;
-    TileSummary* ksum = qsum + (size_t)B * nQB;
+    const Shape sh = choose_shape(Hq / Hkv);
 
     FwdParams p;
     p.q = (const __bf16*)q;
@@ -682,28 +813,29 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
     p.key_valid = ma.key_valid;
     p.positions = positions;
     p.key_positions = ma.key_positions;
-    p.qsum = qsum;
-    p.ksum = ksum;
+    p.qsum = (const TileSummary*)workspace;
+    p.ksum = p.qsum + (size_t)B * nQB;
     p.out = out;
     p.lse = lse;
     p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.E = E;
     p.window = (int)window;
     p.qoff = (int)query_offset;
-    p.hpw = heads_per_workgroup(p.G);
+    p.hpw = sh.hpw;
+    p.tpw = sh.tpw;
     p.nchunk = p.G / p.hpw;
-    p.nQB = nQB; p.nKT = nKT;
+    p.nQB = nQB; p.nQG = ceil_div(nQB, sh.tpw); p.nKT = nKT;
     p.c_log2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
 
-    const size_t nblocks = (size_t)nQB * B * Hkv * p.nchunk;
+    const size_t nblocks = (size_t)p.nQG * B * Hkv * p.nchunk;
     if (nblocks >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
-    const dim3 grid((unsigned)nblocks), block(64 * p.hpw);
+    const dim3 grid((unsigned)nblocks);
     const bool pb = profiles_dtype == INKATTN_BF16;
     if (D == 128) {
-        if (pb) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid, block, 0, st, p);
+        if (pb) launch_fwd<128, true>(sh, grid, st, p);
+        else launch_fwd<128, false>(sh, grid, st, p);
     } else {
-        if (pb) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid, block, 0, st, p);
+        if (pb) launch_fwd<64, true>(sh, grid, st, p);
+        else launch_fwd<64, false>(sh, grid, st, p);
     }
     return check_launch("attn_fwd_kernel");
 }
@@ -719,27 +851,13 @@ int attn_fwd(const void* q, const void* k, const void* v,
 {
     // Validate everything before enqueuing the pre-pass: a rejected call enqueues nothing.
     g_last_error[0] = '\0';
-    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-        return fail(INKATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
-    if (E < 1) return fail(INKATTN_ERR_SHAPE, "relative extent E=%d must be >= 1", E);
-    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
-    if (profiles_dtype != INKATTN_F32 && profiles_dtype != INKATTN_BF16)
-        return fail(INKATTN_ERR_UNSUPPORTED, "profiles dtype %d unknown", profiles_dtype);
+    if (int rc = check_fwd_args(q, k, v, profiles, profiles_dtype, sink, B, Sq, Sk, Hq, Hkv, D, E, out, lse))
+        return rc;
     MaskArgs ma;
-    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, window, query_offset,
-                                   B, Sq, Sk, &ma))
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if ((size_t)B * Sq == 0) return INKATTN_OK;
-    if (!q || !profiles || !sink || !out || !lse) return fail(INKATTN_ERR_NULL, "q/profiles/sink/out/lse is NULL");
-    if (Sk > 0 && (!k || !v)) return fail(INKATTN_ERR_NULL, "k or v is NULL");
-    if (!aligned(q, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))) || !aligned(out, 16))
-        return fail(INKATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
-    if (!aligned(profiles, profiles_dtype == INKATTN_F32 ? 4 : 2) || !aligned(sink, 4) || !aligned(lse, 4))
-        return fail(INKATTN_ERR_ALIGN, "profiles / sink / lse misaligned");
-    const size_t need = summaries_bytes(B, Sq, Sk);
-    if (!workspace || workspace_bytes < need)
-        return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
     if (int rc = attn_plan(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, workspace,
                            workspace_bytes, stream))
         return rc;
@@ -755,8 +873,7 @@ int attn_debug_counts(const uint8_t* valid, const uint8_t* key_valid,
 {
     g_last_error[0] = '\0';
     MaskArgs ma;
-    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, window, query_offset,
-                                   B, Sq, Sk, &ma))
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if (window >= (int64_t(1) << 31) || window < 0) window = 0;
     if ((size_t)B * Sq == 0) return INKATTN_OK;
@@ -777,18 +894,14 @@ int attn_debug_tiles(const uint8_t* valid, const uint8_t* key_valid,
 {
     g_last_error[0] = '\0';
     MaskArgs ma;
-    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, window, query_offset,
-                                   B, Sq, Sk, &ma))
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if (window >= (int64_t(1) << 31) || window < 0) window = 0;
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
     const size_t n = (size_t)B * nQB * nKT;
     if (n == 0) return INKATTN_OK;
     if (!tile_class) return fail(INKATTN_ERR_NULL, "tile_class is NULL");
-    const size_t need = summaries_bytes(B, Sq, Sk);
-    if (!workspace || workspace_bytes < need)
-        return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-    if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
     if (n >= (size_t(1) << 40)) return fail(INKATTN_ERR_SHAPE, "too many tiles");
     hipStream_t st = (hipStream_t)stream;
     TileSummary* qsum = (TileSummary*)workspace;
