@@ -2,8 +2,8 @@
 """Benchmark of the learned-relative GQA attention forward on one MI355X.
 
 One step = one whole forward over the workload: the scheduler pre-pass
-(``attn_plan``) and the attention kernel (``attn_fwd_planned``), inputs
-already resident in HBM.  Prints ONE JSON line:
+(``attn_plan``), the fp16 value copy (``attn_stage_values``) and the attention
+kernel (``attn_fwd_planned``), inputs already resident in HBM.  Prints ONE JSON line:
 
 * ``value``: effective attention TFLOP/s, counting 4*D flops per unmasked
   (query, key, head) pair (2*D for q.k, 2*D for p.v) over the step's wall time;
@@ -126,7 +126,19 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes (calibrates HBM counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel()}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the forward shards by head group or by query range, which is not built here.", file=sys.stderr)
@@ -148,7 +160,8 @@ def main():
          for k in ("q", "k", "v", "profiles", "sink", "valid", "positions")}
     out = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.S, w.Hq), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(16, binding.attn_fwd_workspace_size(w.B, w.S, w.S)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, binding.attn_fwd_workspace_size(w.B, w.S, w.S, w.Hkv, w.D)), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream(dev)
 
     # the mask counts the kernels use must equal the closed form above
@@ -158,6 +171,7 @@ def main():
 
     def step(ev0=None, ev1=None):
         binding.attn_plan(d["valid"], positions=d["positions"], workspace=ws, stream=stream)
+        binding.attn_stage_values(d["v"], d["valid"], workspace=ws, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
         binding.attn_fwd_planned(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"],

@@ -38,7 +38,9 @@
  *    INKATTN_ERR_LAUNCH with the HIP error text in attn_last_error().
  *  - Sizes: B >= 0, Sq >= 0, Sk >= 0, Hq >= 1, Hkv >= 1 with Hq % Hkv == 0,
  *    D in {64, 128}, E >= 1, B*Sq*Hq*D and B*Hq*Sq*E below 2^40 elements,
- *    Sq, Sk and query_offset + Sq below 2^30.
+ *    Sq, Sk and query_offset + Sq below 2^30; one batch row of k / v
+ *    (Sk*Hkv*D*2 bytes) and one (batch row, head) block of profiles (Sq*E
+ *    entries) below 4 GiB each.
  *  - Preconditions not checked (they would need a device read): positions and
  *    key_positions hold values in [0, 2^30); bf16 values of v lie within
  *    +-65504 (v is converted exactly to fp16 for the PV product); inputs at
@@ -69,11 +71,13 @@ enum inkattn_status {
 };
 
 /*
- * Bytes of device workspace attn_fwd needs for these sizes (per-tile mask
- * summaries written by the scheduler pre-pass).  Never fails; returns 0 only
- * when B*Sq == 0 and B*Sk == 0.
+ * Bytes of device workspace attn_fwd needs for these sizes: what the
+ * scheduler pre-pass writes (per-tile mask summaries, 16 bytes per 32-token
+ * query block and per 64-key tile, then one int32 document start column per
+ * key, padded to whole 64-key tiles; each part rounded up to 256 bytes), followed by an fp16 copy of the
+ * values, B*Sk*Hkv*D*2 bytes.  Never fails; returns 0 for non-positive B.
  */
-size_t attn_fwd_workspace_size(int B, int Sq, int Sk);
+size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D);
 
 /*
  * attn_fwd -- the fused forward (scheduler pre-pass + attention kernel).
@@ -95,8 +99,8 @@ size_t attn_fwd_workspace_size(int B, int Sq, int Sk);
  *              parallelism); keys are always global columns 0..Sk-1
  *   out        [B, Sq, Hq, D]  fp32, 16-byte aligned, written
  *   lse        [B, Sq, Hq]     fp32, written
- *   workspace  device buffer of at least attn_fwd_workspace_size(B, Sq, Sk)
- *              bytes, 16-byte aligned; contents on entry are ignored
+ *   workspace  device buffer of at least attn_fwd_workspace_size(B, Sq, Sk,
+ *              Hkv, D) bytes, 16-byte aligned; contents on entry are ignored
  */
 int attn_fwd(const void* q, const void* k, const void* v,
              const void* profiles, int profiles_dtype,
@@ -123,10 +127,25 @@ int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_stage_values -- converts v [B, Sk, Hkv, D] (bf16) into the fp16 copy
+ * the attention kernel stages from, in `workspace` after the summaries.  Each
+ * value is saturated to +-65504; values of keys whose key_valid is 0 are
+ * written as 0.  The probabilities multiply the values in fp16 MFMA (fp16
+ * keeps 11 significant bits where bf16 keeps 8; a bf16 value inside the fp16
+ * range converts exactly).  key_valid defaults as in attn_fwd.  One call per
+ * layer (the values differ per layer).
+ */
+int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_valid, int64_t query_offset,
+                      int B, int Sq, int Sk, int Hkv, int D, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * attn_fwd_planned -- the attention kernel alone, reading the summaries that
  * attn_plan wrote into `workspace` for the same mask arguments (enqueued
  * earlier on `stream`, or completed).  A workspace planned for other mask
- * arguments gives undefined results.  attn_fwd == attn_plan + attn_fwd_planned.
+ * arguments gives undefined results, and reading the fp16 values that
+ * attn_stage_values wrote there for this v (v itself is not read).
+ * attn_fwd == attn_plan + attn_stage_values + attn_fwd_planned.
  */
 int attn_fwd_planned(const void* q, const void* k, const void* v,
                      const void* profiles, int profiles_dtype,

@@ -39,9 +39,12 @@ def test_status_strings_and_sizes():
     assert binding.attn_status_string(0) == "ok"
     assert "NULL" in binding.attn_status_string(1)
     assert binding.attn_query_block() == 32 and binding.attn_key_tile() == 64
-    assert binding.attn_fwd_workspace_size(1, 128, 128) == (4 + 2) * 16
-    assert binding.attn_fwd_workspace_size(2, 33, 65) == (2 * 2 + 2 * 2) * 16
-    assert binding.attn_fwd_workspace_size(0, 10, 10) == 0
+    # tile summaries (16 B per query block / key tile) + key start columns (4 B per key),
+    # each rounded up to 256 B, then the fp16 values
+    assert binding.attn_fwd_workspace_size(1, 128, 128, 2, 64) == 256 + 512 + 128 * 2 * 64 * 2
+    assert binding.attn_fwd_workspace_size(2, 33, 65, 1, 128) == 256 + 1024 + 2 * 65 * 128 * 2
+    assert binding.attn_fwd_workspace_size(40, 64, 64, 1, 64) == 2048 + 40 * 64 * 4 + 40 * 64 * 64 * 2
+    assert binding.attn_fwd_workspace_size(0, 10, 10, 1, 64) == 0
 
 
 def call(**over):
@@ -65,7 +68,8 @@ def call(**over):
     (dict(Sq=1 << 30, Sk=1 << 30), 2), (dict(qoff=-1, key_valid=A), 2),
     (dict(D=96), 3), (dict(D=256), 3), (dict(pdt=7), 3),
     (dict(q=A + 8), 4), (dict(out=A + 4), 4), (dict(profiles=A + 2), 4), (dict(positions=A + 2), 4),
-    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(ws=A + 8), 4),
+    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(wsb=256 + 256 + 64 * 2 * 128 * 2 - 1), 5), (dict(ws=A + 8), 4),
+    (dict(Sq=1 << 20, Sk=1 << 20, Hkv=16, Hq=16, key_valid=A), 2),   # one k/v row of 4 GiB
 ])
 def test_host_validation_rejects_before_launch(over, status):
     assert call(**over) == status

@@ -23,7 +23,7 @@ STATUS = {0: "INKATTN_OK", 1: "INKATTN_ERR_NULL", 2: "INKATTN_ERR_SHAPE", 3: "IN
           4: "INKATTN_ERR_ALIGN", 5: "INKATTN_ERR_WORKSPACE", 6: "INKATTN_ERR_LAUNCH"}
 
 # Every symbol include/inkattn.h declares.
-EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_fwd_planned",
+EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
            "attn_debug_counts", "attn_debug_tiles",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
@@ -47,7 +47,9 @@ def load() -> ctypes.CDLL:
             lib = ctypes.CDLL(LIB_PATH)
             P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
             lib.attn_fwd_workspace_size.restype = SZ
-            lib.attn_fwd_workspace_size.argtypes = [I, I, I]
+            lib.attn_fwd_workspace_size.argtypes = [I, I, I, I, I]
+            lib.attn_stage_values.restype = I
+            lib.attn_stage_values.argtypes = [P, P, P, I64, I, I, I, I, I, P, SZ, P]
             lib.attn_fwd.restype = I
             lib.attn_fwd.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
                                      I, I, I, I, I, I, I, P, P, P, SZ, P]
@@ -112,8 +114,8 @@ def _stream(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def attn_fwd_workspace_size(B: int, Sq: int, Sk: int) -> int:
-    return int(load().attn_fwd_workspace_size(B, Sq, Sk))
+def attn_fwd_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
+    return int(load().attn_fwd_workspace_size(B, Sq, Sk, Hkv, D))
 
 
 def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_positions, window,
@@ -148,7 +150,8 @@ def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_posit
     else:
         lse = _dev(lse, "lse", (torch.float32,), dev)
     if workspace is None:
-        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk), 16), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
+                                device=dev)
     pdt = INKATTN_BF16 if profiles.dtype == torch.bfloat16 else INKATTN_F32
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(profiles), pdt, _ptr(sink), _ptr(valid_u8),
             _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), 0 if window is None else int(window),
@@ -181,7 +184,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.
 
 def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=None, key_positions=None,
                      window=None, query_offset: int = 0, out=None, lse=None, workspace=None, stream=None):
-    """The attention kernel alone, on a workspace filled by :func:`attn_plan` for the same masks."""
+    """The attention kernel alone, on a workspace filled by :func:`attn_plan` (same masks) and
+    :func:`attn_stage_values` (same values)."""
     if workspace is None:
         raise ValueError("attn_fwd_planned needs the workspace attn_plan filled")
     args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
@@ -192,8 +196,9 @@ def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=N
 
 
 def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_offset: int = 0,
-              Sk: Optional[int] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Scheduler pre-pass: fills and returns the workspace for :func:`attn_fwd_planned`."""
+              Sk: Optional[int] = None, workspace: Optional[torch.Tensor] = None, Hkv: int = 0, D: int = 0,
+              stream=None) -> torch.Tensor:
+    """Scheduler pre-pass: fills the mask summaries of ``workspace`` (allocated for (Hkv, D) if None)."""
     dev = valid.device
     valid_u8 = _mask_tensor(valid, "valid", dev)
     kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
@@ -203,10 +208,31 @@ def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_o
     if Sk is None:
         Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
     if workspace is None:
-        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk), 16), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
+                                device=dev)
     rc = load().attn_plan(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), int(query_offset), B, Sq, Sk,
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     _check(rc, "attn_plan")
+    return workspace
+
+
+def attn_stage_values(v, valid, key_valid=None, query_offset: int = 0, Sq: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp16 copy of the values into ``workspace`` (after the summaries) for :func:`attn_fwd_planned`."""
+    dev = v.device
+    v = _dev(v, "v", (torch.bfloat16,), None)
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    B, Sk, Hkv, D = v.shape
+    if Sq is None:
+        Sq = valid_u8.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
+                                device=dev)
+    rc = load().attn_stage_values(_ptr(v), _ptr(valid_u8), _ptr(kvalid_u8), int(query_offset), B, Sq, Sk, Hkv, D,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream, dev))
+    _check(rc, "attn_stage_values")
     return workspace
 
 
@@ -242,7 +268,7 @@ def attn_debug_tiles(valid, key_valid=None, positions=None, key_positions=None, 
         Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
     bm, bn = attn_query_block(), attn_key_tile()
     cls = torch.empty((B, -(-Sq // bm), -(-Sk // bn)), dtype=torch.uint8, device=dev)
-    need = attn_fwd_workspace_size(B, Sq, Sk)
+    need = attn_fwd_workspace_size(B, Sq, Sk, 0, 0)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     rc = load().attn_debug_tiles(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos),
                                  0 if window is None else int(window), int(query_offset), B, Sq, Sk,

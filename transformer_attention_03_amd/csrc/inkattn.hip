@@ -12,28 +12,32 @@
 // Structure of one call:
 //   1. summarize_kernel (scheduler pre-pass, one wave per tile): for every
 //      32-token query block and 64-key tile, the min / max document start
-//      column over real tokens and the number of real tokens.  Every skip /
-//      full / masked decision of the main kernel comes from these summaries.
-//   2. attn_fwd_kernel: one workgroup per (batch row, K/V head, head chunk,
+//      column over real tokens and the number of real tokens, plus each key's
+//      start column.  Every skip / full / masked decision of the main kernel
+//      comes from these summaries.
+//   2. stage_values_kernel: v (bf16) -> fp16 copy, zero at keys that are not
+//      real (the probabilities multiply the values in fp16).
+//   3. attn_fwd_kernel: one workgroup per (batch row, K/V head, head chunk,
 //      group of 32-token query blocks); each wave owns one (query head,
-//      32-token block).  Each 64-key K/V tile is staged once in LDS and
-//      serves every wave of the workgroup, i.e. every query head of the chunk
-//      (GQA).  The next live tile's K/V loads are issued before the current
-//      tile is computed and land in the second LDS buffer (one barrier per
-//      tile).  Per wave and tile:
+//      32-token block).  Each 64-key K/V tile is staged once in LDS by DMA
+//      (buffer_load ... lds, XOR-swizzled rows) and serves every wave of the
+//      workgroup, i.e. every query head of the chunk (GQA).  The next live
+//      tile's DMA is issued before the current tile is computed and lands in
+//      the second buffer (one barrier per tile).  Per wave, each 32-key half
+//      of a tile is processed in turn:
 //        S^T = K Q^T      bf16 MFMA 32x32x16, keys on M and queries on N, so
 //                         each lane owns one query column: row reductions are
 //                         in-lane plus one exchange between the wave halves;
-//        + relative bias  gathered from the query's own profile row; for a
-//                         32-key sub-tile the distances of a row are one
-//                         contiguous run (loaded 4 at a time);
+//                         the accumulator starts from the relative bias
+//                         (scaled by sqrt(D)), gathered from the query's own
+//                         profile row as contiguous 4-entry runs;
 //        mask             only on tiles classed as masked;
 //        online softmax   running max / denominator per lane, started from
 //                         the sink logit (the sink's weight enters the
 //                         denominator, never the value sum); the running max
-//                         is only moved when a row's tile max exceeds it by
-//                         more than 8 (log2 units), so probabilities stay
-//                         <= 2^8 and most tiles skip the output rescale;
+//                         moves only when a row's tile max exceeds it by more
+//                         than 8 (log2 units), so probabilities stay <= 2^8
+//                         and most tiles skip the output rescale;
 //        O^T += V^T P^T   fp16 MFMA 32x32x16; P^T comes straight from the S^T
 //                         accumulator registers (keys inside each 16-key step
 //                         are permuted the same way on both operands) and V^T
@@ -68,6 +72,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4_u __attribute__((ext_vector_type(4), aligned(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // Per-tile summary written by the pre-pass: document start columns of the
 // tile's real tokens (min, max) and how many real tokens it has.
@@ -132,7 +138,7 @@ __device__ __forceinline__ int wave_max(int x)
 __global__ __launch_bounds__(256) void summarize_kernel(
     const uint8_t* __restrict__ valid, const int32_t* __restrict__ positions, int qoff, int Sq, int nQB,
     const uint8_t* __restrict__ key_valid, const int32_t* __restrict__ key_positions, int Sk, int nKT,
-    int B, TileSummary* __restrict__ qsum, TileSummary* __restrict__ ksum)
+    int B, TileSummary* __restrict__ qsum, TileSummary* __restrict__ ksum, int* __restrict__ kanchor)
 {
     const int w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -156,6 +162,9 @@ __global__ __launch_bounds__(256) void summarize_kernel(
             amin = a; amax = a; n = 1;
         }
     }
+    // per-key start column for the masked tiles, INT_MIN for keys that are not
+    // real and for the padding of the last tile
+    if (!is_q) kanchor[(size_t)b * ntiles * BN + i] = n ? amin : INT_MIN;
     amin = wave_min(amin);
     amax = wave_max(amax);
     n = __popcll(__builtin_amdgcn_ballot_w64(n != 0));
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(256) void summarize_kernel(
 struct FwdParams {
     const __bf16* q;
     const __bf16* k;
-    const __bf16* v;
+    const _Float16* v16;           // values converted to fp16 (zero at keys that are not real)
     const void* profiles;
     const float* sink;
     const uint8_t* valid;
@@ -178,6 +187,7 @@ struct FwdParams {
     const int32_t* key_positions;  // NULL: key column
     const TileSummary* qsum;       // [B, nQB]
     const TileSummary* ksum;       // [B, nKT]
+    const int* kanchor;            // [B, Sk] key start column j - key_positions[j], INT_MIN if not real
     float* out;
     float* lse;
     int B, Sq, Sk, Hq, Hkv, G, E;
@@ -207,29 +217,59 @@ struct TileDesc {
     int kt;        // tile index (> kt_hi: none)
     int my_cls;    // this wave's class
     int masked;    // some wave of the workgroup masks this tile
-    int partial;   // the tile holds keys that are not real or lie past Sk
 };
+
+// LDS layout of one staged K / V tile.  Each 16-byte DMA instruction writes
+// 1 KB of LDS contiguously, i.e. RPI whole rows, so rows cannot be padded
+// one by one; instead rows come in groups of RPI (pitch KGP / VGP bytes) and
+// the 16-byte chunks of a row are XOR-swizzled.  Both choices make the MFMA
+// operand reads (16 rows x 16 B per phase for K, 4 rows x 64 B per phase
+// for the transposing V reads) bank-conflict free on the 64-bank LDS.
+template <int D> struct TileLayout;
+template <> struct TileLayout<128> {
+    static constexpr int RPI = 4, KGP = 1088, VGP = 1024;
+    __device__ static constexpr int ksw(int t) { return t; }
+    __device__ static constexpr int vsw(int t) { return 4 * t; }
+};
+template <> struct TileLayout<64> {
+    static constexpr int RPI = 8, KGP = 1088, VGP = 1024;
+    __device__ static constexpr int ksw(int t) { return t >> 1; }
+    __device__ static constexpr int vsw(int t) { return 4 * ((t >> 1) & 1); }
+};
+
+enum : int { BIAS_NONE = 0, BIAS_FAST = 1, BIAS_EDGE = 2 };
+
+// Relative-bias class of a 32-key sub-tile starting at key js for the query
+// columns qlo..qhi: no distance below E (no bias), every distance inside
+// [0, E) (one contiguous 4-element run per lane and 4 keys), or mixed.
+__device__ __forceinline__ int bias_class(int qlo, int qhi, int js, int E)
+{
+    const int rmin = qlo - (js + 31), rmax = qhi - js;
+    if (rmin >= E) return BIAS_NONE;
+    if (rmin >= 0 && rmax < E) return BIAS_FAST;
+    return BIAS_EDGE;
+}
 
 template <int D, bool PROF_BF16, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p)
 {
-    constexpr int NT = 64 * NW;
-    constexpr int NKK = D / 16;            // k-steps of S^T = K Q^T
-    constexpr int NDB = D / 32;            // 32-row d-blocks of O^T
-    constexpr int KS = D + 8;              // K row stride in LDS (bf16): conflict-free b128 reads
-    constexpr int VS = D + 32;             // V row stride in LDS (f16): conflict-free transposing reads
-    constexpr int CPR = D / 8;             // 16-byte chunks per K / V row
-    constexpr int NCH = BN * CPR / NT;     // chunks per thread per tile
-    static_assert(BN * CPR % NT == 0, "tile chunks must divide among threads");
+    using L = TileLayout<D>;
+    constexpr int NKK = D / 16;              // k-steps of S^T = K Q^T
+    constexpr int NDB = D / 32;              // 32-row d-blocks of O^T
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int NGRP = BN / L::RPI;        // DMA groups per tile (per tensor)
+    constexpr int GPW = NGRP / NW;           // DMA groups per wave
+    static_assert(NGRP % NW == 0, "DMA groups must divide among waves");
+    constexpr int KBYTES = NGRP * L::KGP;
+    constexpr int VBYTES = NGRP * L::VGP;
+    constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 2 * VBYTES;
 
-    __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][BN * VS];
-    __shared__ __attribute__((aligned(16))) int ca_lds[2][BN];
+    __shared__ __attribute__((aligned(1024))) char smem[CA_OFF + 2 * BN * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qi = lane & 31;      // this lane's query within the block
     const int hh = lane >> 5;      // wave half
 
@@ -313,65 +353,139 @@ void attn_fwd_kernel(FwdParams p)
             }
             if (any) {
                 d.kt = kt; d.my_cls = mine; d.masked = masked;
-                d.partial = ks.nvalid != BN || kcount != BN;
                 return d;
             }
         }
-        d.kt = kt_hi + 1; d.my_cls = TILE_SKIP; d.masked = 0; d.partial = 0;
+        d.kt = kt_hi + 1; d.my_cls = TILE_SKIP; d.masked = 0;
         return d;
     };
 
-    // K / V chunk c of a tile: row c / CPR, 8 elements at column 8 * (c % CPR).
-    bf16x8 kreg[NCH], vreg[NCH];
-    int careg = INT_MIN;
-    auto issue_loads = [&](const TileDesc& d) {
+    // ---- K / V staging by LDS DMA.  The buffer resources cover rows 0..Sk-1
+    // of this (batch row, K/V head); rows past Sk read as zero.
+    const int krow = p.Hkv * D * 2;                     // bytes between consecutive keys
+    const unsigned nrec = p.Sk > 0 ? (unsigned)((size_t)(p.Sk - 1) * krow + D * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.k + ((size_t)b * p.Sk * p.Hkv + g) * D), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.v16 + ((size_t)b * p.Sk * p.Hkv + g) * D), 0, nrec, 0x00020000);
+    // lane -> (row t of its DMA group, LDS chunk slot pc): it fetches the chunk that lands there
+    const int dt = lane / CPR, dpc = lane % CPR;
+    const int kvoff = dt * krow + 16 * (dpc ^ L::ksw(dt));
+    const int vvoff = (dt ^ 3) * krow + 16 * (dpc ^ L::vsw(dt));   // V row dt ^ 3 -> slot dt
+    // key start columns of this batch row, padded to whole tiles with INT_MIN
+    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.kanchor + (size_t)b * p.nKT * BN), 0, (unsigned)p.nKT * BN * 4u, 0x00020000);
+    auto issue_tile = [&](const TileDesc& d, int bufsel) {
         const int j0 = d.kt * BN;
-        const int kcount = min(BN, p.Sk - j0);
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int c = tid + u * NT;
-            const int row = c / CPR, col = c - row * CPR;
-            const int j = j0 + row;
-            bool ok = row < kcount;
-            const size_t off = (((size_t)b * p.Sk + j) * p.Hkv + g) * D + 8 * col;
-            kreg[u] = ok ? *(const bf16x8*)(p.k + off) : bf16x8{};
-            if (ok && d.partial) ok = p.key_valid[(size_t)b * p.Sk + j] != 0;   // zero values of keys that are not real
-            vreg[u] = ok ? *(const bf16x8*)(p.v + off) : bf16x8{};
+        for (int u = 0; u < GPW; ++u) {
+            const int a = wave + NW * u;                   // DMA group (uniform)
+            const int soff = (j0 + a * L::RPI) * krow;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krsrc, (lds_void*)(smem + K_OFF + bufsel * KBYTES + a * L::KGP), 16, kvoff, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrsrc, (lds_void*)(smem + V_OFF + bufsel * VBYTES + a * L::VGP), 16, vvoff, soff, 0, 0);
         }
-        if (d.masked && tid < BN) {
-            careg = INT_MIN;
-            if (tid < kcount) {
-                const int j = j0 + tid;
-                const size_t o = (size_t)b * p.Sk + j;
-                if (p.key_valid[o]) careg = p.key_positions ? j - p.key_positions[o] : 0;
+        if (d.masked && wave == 0)   // 64 start columns: one dword per lane
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                arsrc, (lds_void*)(smem + CA_OFF + bufsel * BN * 4), 4, 4 * lane, j0 * 4, 0, 0);
+    };
+
+    // Per-lane LDS byte offsets of the MFMA operands within one buffer.  The
+    // K swizzle XORs at most the two low bits of the chunk index, so the
+    // chunk of k-step kk sits at 32*kk from one of two lane bases (even / odd kk).
+    // Accumulator element (jj, e) of a 32-key half is key 8 jj + 4 hh + (e ^ 3): the
+    // K row a lane supplies is qi ^ 3 and the DMA stores V row t of each 4-row quad
+    // at slot t ^ 3, so that keys 4k..4k+3 appear in decreasing order, the order of
+    // increasing distance, i.e. the memory order of a profile run.
+    const int krow_lane = qi ^ 3;
+    const int kt_row = krow_lane % L::RPI;
+    const int ksw = L::ksw(kt_row);
+    const int krowbase = (krow_lane / L::RPI) * L::KGP + kt_row * (2 * D) + 16 * (hh ^ (ksw & 1));
+    const int kbase_even = krowbase + 32 * (ksw >> 1);
+    const int kbase_odd = krowbase - 32 * (ksw >> 1);
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int r = 4 * hh + (lane & 15) / 4;                // row within an 8-key half-step
+        const int t = r % L::RPI;
+        const int e = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // fp16 element in the row
+        voff[db] = (r / L::RPI) * L::VGP + t * (2 * D) + 16 * (((2 * e) / 16) ^ L::vsw(t)) + (2 * e) % 16;
+    }
+
+    // ---- relative bias.  sacc[s][4*jj+e] is the profile entry of key
+    // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance R - 8 jj - 4 hh - (e ^ 3)
+    // with R = gi - (j0 + 32 s).  All loads go through a buffer resource over this
+    // (batch row, head)'s [Sq, E] block: one 32-bit lane offset, immediate
+    // offsets per entry, and reads outside the block return 0.
+    constexpr int PE = PROF_BF16 ? 2 : 4;               // bytes per profile entry
+    const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)p.profiles + ((size_t)b * p.Hq + h) * p.Sq * p.E * PE), 0,
+        (unsigned)((size_t)p.Sq * p.E * PE), 0x00020000);
+    // Byte offset of distance gi - 4 hh - 30 in this lane's row, in wrapping
+    // 32-bit arithmetic (it may lie before the row: every entry read below is
+    // at most 30 entries after it).  The buffer hardware range-checks the
+    // offset register as an unsigned value, so every register offset handed to
+    // it is the exact offset of an entry (never a base to be completed by the
+    // constant operand), and offsets before the block wrap out of range.
+    const unsigned prow_off = ((unsigned)i * (unsigned)p.E + (unsigned)(gi - 4 * hh - 30)) * PE;
+    // sacc[s] first receives sub-tile s's raw profile entries, then (scaled by
+    // sqrt(D)) serves as the initial accumulator of S^T = K Q^T, so that
+    // head_dim^-0.5 * log2(e) * sacc = scale*log2e*q.k + log2e*bias.
+    f32x16 sacc[2];
+    constexpr float INV_SCALE = D == 128 ? 11.313708498984761f : 8.0f;   // sqrt(D)
+    // fp32 sub-tiles whose distances all lie in [0, E): 4 runs of 4 entries,
+    // the run of jj starting at distance R - 8 jj - 4 hh - 3 (element e: + e)
+    auto load_bias_fast = [&](int js, int s) {
+        // lowest distance read (run of jj = 3), >= 0 on such sub-tiles
+        const unsigned vo = prow_off + (3 - js) * PE;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                prsrc, vo, (24 - 8 * jj) * PE, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[s][4 * jj + e] = w[e];
+        }
+    };
+    // any sub-tile, entry by entry; 0 outside [0, E)
+    auto load_bias_edge = [&](int js, int s) {
+        const unsigned vo = prow_off - (unsigned)js * PE;
+        const int R = gi - js;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const unsigned off = vo + (30 - 8 * jj - (e ^ 3)) * PE;
+                float v;
+                if (PROF_BF16) {
+                    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
+                    v = __uint_as_float((unsigned)u << 16);
+                } else {
+                    v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(prsrc, off, 0, 0));
+                }
+                const unsigned r = (unsigned)(R - 8 * jj - 4 * hh - (e ^ 3));
+                sacc[s][4 * jj + e] = r < (unsigned)p.E ? v : 0.0f;
             }
         }
     };
-    auto store_lds = [&](const TileDesc& d, int buf) {
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int c = tid + u * NT;
-            const int row = c / CPR, col = c - row * CPR;
-            *(bf16x8*)(&k_lds[buf][row * KS + 8 * col]) = kreg[u];
-            f16x8 vh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vh[e] = (_Float16)(float)vreg[u][e];
-            *(f16x8*)(&v_lds[buf][row * VS + 8 * col]) = vh;
-        }
-        if (d.masked && tid < BN) ca_lds[buf][tid] = careg;
+    // Bias loads of sub-tile s of tile d (returns how many load instructions
+    // were issued: 4 runs, 16 entries, or none).
+    auto load_bias = [&](const TileDesc& d, int s) -> int {
+        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return 0;
+        const int js = d.kt * BN + 32 * s;
+        const int bc = bias_class(qlo, qhi, js, p.E);
+        if (bc == BIAS_FAST && !PROF_BF16) { load_bias_fast(js, s); return 4; }
+        if (bc != BIAS_NONE) { load_bias_edge(js, s); return 16; }
+        return 0;
     };
-
-    const size_t prof_row = ((size_t)b * p.Hq + h) * p.Sq + i;   // row of profiles[b,h,i,:]
-    // V^T operand addressing for the transposing read: lane supplies row
-    // (lane%16)/4 of its 4-key group and column 4*(lane%4) of its 16-wide
-    // d-half; the read hands lane l the 4 keys of d = 16*((l/16)%2) + l%16.
-    const int v_lane_off = (4 * hh + (lane & 15) / 4) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
+    auto forget = [&](int s) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sacc[s][t] = __builtin_nondeterministic_value(sacc[s][t]);
+    };
     TileDesc cur = next_live(kt_lo - 1);
-    if (cur.kt <= kt_hi) {
-        issue_loads(cur);
-        store_lds(cur, 0);
-    }
+    forget(0);
+    forget(1);
+    if (cur.kt <= kt_hi) issue_tile(cur, 0);
     __syncthreads();
     int buf = 0;
     while (cur.kt <= kt_hi) {
@@ -379,146 +493,110 @@ void attn_fwd_kernel(FwdParams p)
         const int j0 = cur.kt * BN;
 
         if (cur.my_cls != TILE_SKIP) {
-            // ---- relative bias for both 32-key sub-tiles (issued before the prefetch)
-            float bias[2][16];
-            bool has_bias[2];
+            // Sub-tile 0's bias loads go out first, then the DMA of the next
+            // tile, then sub-tile 1's bias loads (needed half a tile later).
+            const int bc0 = bias_class(qlo, qhi, j0, p.E);
+            const int bc1 = bias_class(qlo, qhi, j0 + 32, p.E);
+            if (load_bias(cur, 0) == 0) forget(0);
+            asm volatile("" ::: "memory");
+            if (nxt.kt <= kt_hi) issue_tile(nxt, buf ^ 1);
+            asm volatile("" ::: "memory");
+            if (load_bias(cur, 1) == 0) forget(1);
+            asm volatile("" ::: "memory");
+
+            const char* kb = smem + K_OFF + buf * KBYTES;
+            const char* vb = smem + V_OFF + buf * VBYTES;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int js = j0 + 32 * s;
-                const int rmin = qlo - (js + 31), rmax = qhi - js;   // distance range of the sub-tile
-                const int R = gi - js;                               // this lane's distance to key js
-                has_bias[s] = rmin < p.E;
+                // ---- S^T = K Q^T (+ bias * sqrt(D)) for keys j0 + 32 s .. + 31
+                const bool hb = (s == 0 ? bc0 : bc1) != BIAS_NONE;
+                f32x16 acc;
+                if (hb) {
 #pragma unroll
-                for (int t = 0; t < 16; ++t) bias[s][t] = 0.0f;
-                if (rmin < p.E && qin) {
-                    if (rmin >= 0 && rmax < p.E) {
-                        // every distance of the sub-tile lies inside [0, E): one run per 4 keys
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const int rb = R - 8 * jj - 4 * hh - 3;
-                            if (PROF_BF16) {
-                                const __bf16* pr = (const __bf16*)p.profiles + prof_row * p.E + rb;
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) bias[s][4 * jj + e] = (float)pr[3 - e];
-                            } else {
-                                const f32x4_u w = *(const f32x4_u*)((const float*)p.profiles + prof_row * p.E + rb);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) bias[s][4 * jj + e] = w[3 - e];
-                            }
-                        }
-                    } else {
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int r = R - 8 * jj - 4 * hh - e;
-                                if (r >= 0 && r < p.E) {
-                                    if (PROF_BF16)
-                                        bias[s][4 * jj + e] = (float)((const __bf16*)p.profiles)[prof_row * p.E + r];
-                                    else
-                                        bias[s][4 * jj + e] = ((const float*)p.profiles)[prof_row * p.E + r];
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-
-            if (nxt.kt <= kt_hi) issue_loads(nxt);
-
-            // ---- S^T = K Q^T for the two 32-key sub-tiles
-            f32x16 sacc[2] = {f32x16{}, f32x16{}};
-            const __bf16* kp = &k_lds[buf][qi * KS + 8 * hh];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const bf16x8 a0 = *(const bf16x8*)(kp + 16 * kk);
-                const bf16x8 a1 = *(const bf16x8*)(kp + 32 * KS + 16 * kk);
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], sacc[1], 0, 0, 0);
-            }
-
-            // ---- logits in log2 units.  Element (s, jj, e) is key j0 + 32 s + 8 jj + 4 hh + e.
-            float u[2][16];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (has_bias[s]) {
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) u[s][t] = __builtin_fmaf(sacc[s][t], p.c_log2, bias[s][t] * LOG2E);
+                    for (int t = 0; t < 16; ++t) acc[t] = sacc[s][t] * INV_SCALE;
                 } else {
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) u[s][t] = sacc[s][t] * p.c_log2;
+                    acc = f32x16{};
                 }
-            }
-            if (cur.my_cls == TILE_MASKED) {
+                // consumed: the registers carry nothing into later tiles
+                forget(s);
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk + s * (32 / L::RPI) * L::KGP;
+                    const bf16x8 a = *(const bf16x8*)(kb + ko);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], acc, 0, 0, 0);
+                }
+
+                // ---- mask.  Element (jj, e) is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
+                if (cur.my_cls == TILE_MASKED) {
+                    const int* ca = (const int*)(smem + CA_OFF + buf * BN * 4);
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int kl = 32 * s + 8 * jj + 4 * hh;
-                        const i32x4 c4 = *(const i32x4*)(&ca_lds[buf][kl]);
+                        const i32x4 c4 = *(const i32x4*)(ca + kl);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (!key_visible(gi_eff, a_q, j0 + kl + e, c4[e], wlim)) u[s][4 * jj + e] = -INFINITY;
+                            if (!key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
+                                acc[4 * jj + e] = -INFINITY;
                     }
                 }
-            }
 
-            // ---- online softmax (sink-initialised, lazily rescaled)
-            float mx = -INFINITY;
+                // ---- online softmax (sink-initialised, lazily rescaled), log2 units
+                float mx = -INFINITY;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                for (int t = 0; t < 16; ++t) mx = fmaxf(mx, acc[t]);
+                mx = half_max(mx * p.c_log2);
+                const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
+                const float m_new = move ? mx : m;
+                const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+                if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                    const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
+                    l *= alpha;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) mx = fmaxf(mx, u[s][t]);
-            mx = half_max(mx);
-            const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
-            const float m_new = move ? mx : m;
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {
-                const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
-                l *= alpha;
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-            }
-            m = m_new;
-            float lsum = 0.0f;
-            f16x8 pb[2][2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
+                        for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+                }
+                m = m_new;
+                f16x8 pb[2];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    const float pv = __builtin_amdgcn_exp2f(u[s][t] - m_use);
-                    lsum += pv;
-                    // 16-key step c of sub-tile s takes elements jj = 2c, 2c+1
-                    pb[s][t >> 3][t & 7] = (_Float16)pv;
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], p.c_log2, -m_use));
+                    // 16-key step c takes elements jj = 2c, 2c+1 (keys in the same order as V's rows)
+                    pb[t >> 3][t & 7] = (_Float16)pv;
                 }
-            }
-            l += lsum;
-
-            // ---- O^T += V^T P^T
+                // the denominator sums the fp16-rounded weights the PV product uses
+                float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    ls0 = __builtin_amdgcn_fdot2(half2_t{pb[0][2 * q2], pb[0][2 * q2 + 1]},
+                                                 half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
+                    ls1 = __builtin_amdgcn_fdot2(half2_t{pb[1][2 * q2], pb[1][2 * q2 + 1]},
+                                                 half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
+                }
+                l += ls0 + ls1;
+
+                // ---- O^T += V^T P^T
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const _Float16* vb = &v_lds[buf][(32 * s + 16 * c) * VS + v_lane_off];
+                    constexpr int HALF = (8 / L::RPI) * L::VGP;   // +8 keys
+                    const int step = ((32 * s + 16 * c) / L::RPI) * L::VGP;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 32 * db));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 32 * db + 8 * VS));
-                        // whole-vector reinterpretation: keys 4hh+0..3 then 8+4hh+0..3
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + step + voff[db]));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + step + HALF + voff[db]));
+                        // whole-vector reinterpretation: keys 4hh+(3..0) then 8+4hh+(3..0)
                         const s16x8 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const f16x8 a = __builtin_bit_cast(f16x8, lohi);
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[s][c], oacc[db], 0, 0, 0);
+                        const f16x8 av = __builtin_bit_cast(f16x8, lohi);
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], oacc[db], 0, 0, 0);
                     }
                 }
             }
         } else if (nxt.kt <= kt_hi) {
-            issue_loads(nxt);
+            issue_tile(nxt, buf ^ 1);
         }
 
-        if (nxt.kt <= kt_hi) store_lds(nxt, buf ^ 1);
-        __syncthreads();
+        // this wave's DMA of the next tile has landed; then every wave's has
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         buf ^= 1;
         cur = nxt;
     }
@@ -545,6 +623,30 @@ void attn_fwd_kernel(FwdParams p)
         else lse = -INFINITY;
         p.lse[qrow * p.Hq + h] = lse;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Value staging: v (bf16) -> fp16, saturated to the fp16 range, zero at keys
+// that are not real, so that a masked key's weight 0 never meets a value that
+// fp16 cannot hold.  One thread per 8 elements.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restrict__ v,
+                                                           const uint8_t* __restrict__ key_valid,
+                                                           int B, int Sk, int HD, _Float16* __restrict__ v16)
+{
+    const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t nchunks = (size_t)B * Sk * HD / 8;
+    if (c >= nchunks) return;
+    const size_t row = c / (HD / 8);                   // b * Sk + j
+    const bf16x8 x = *(const bf16x8*)(v + 8 * c);
+    f16x8 y;
+    if (key_valid[row]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
+    } else {
+        y = f16x8{};
+    }
+    *(f16x8*)(v16 + 8 * c) = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -616,11 +718,24 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-size_t summaries_bytes(int B, int Sq, int Sk)
+// Workspace layout: [tile summaries][key start columns, int32 B*Sk][values in fp16, B*Sk*Hkv*D],
+// the first two parts each rounded up to 256 bytes.  summaries_bytes covers the
+// first two parts (what the pre-pass writes).
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+size_t tile_summary_bytes(int B, int Sq, int Sk)
 {
     const size_t nq = (size_t)B * ceil_div(Sq, BM);
     const size_t nk = (size_t)B * ceil_div(Sk, BN);
-    return (nq + nk) * sizeof(TileSummary);
+    return round256((nq + nk) * sizeof(TileSummary));
+}
+size_t summaries_bytes(int B, int Sq, int Sk)
+{
+    return tile_summary_bytes(B, Sq, Sk) + round256((size_t)B * ceil_div(Sk, BN) * BN * sizeof(int));
+}
+
+size_t values_bytes(int B, int Sk, int Hkv, int D)
+{
+    return (size_t)B * Sk * Hkv * D * sizeof(_Float16);
 }
 
 // Defaults of the optional arguments and the checks shared by every entry point.
@@ -664,9 +779,8 @@ int check_launch(const char* what)
     return INKATTN_OK;
 }
 
-int check_workspace(void* workspace, size_t workspace_bytes, int B, int Sq, int Sk)
+int check_workspace(void* workspace, size_t workspace_bytes, size_t need)
 {
-    const size_t need = summaries_bytes(B, Sq, Sk);
     if (!workspace || workspace_bytes < need)
         return fail(INKATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
     if (!aligned(workspace, 16)) return fail(INKATTN_ERR_ALIGN, "workspace not 16-byte aligned");
@@ -675,15 +789,18 @@ int check_workspace(void* workspace, size_t workspace_bytes, int B, int Sq, int 
 
 int launch_summaries(const uint8_t* valid, const int32_t* positions, const uint8_t* key_valid,
                      const int32_t* key_positions, int qoff, int B, int Sq, int Sk,
-                     TileSummary* qsum, TileSummary* ksum, hipStream_t st)
+                     void* workspace, hipStream_t st)
 {
+    TileSummary* qsum = (TileSummary*)workspace;
+    TileSummary* ksum = qsum + (size_t)B * ceil_div(Sq, BM);
+    int* kanchor = (int*)((char*)workspace + tile_summary_bytes(B, Sq, Sk));
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
     const long long waves = (long long)B * (nQB + nKT);
     if (waves == 0) return INKATTN_OK;
     if (waves >= (1LL << 31)) return fail(INKATTN_ERR_SHAPE, "too many tiles");
     const int blocks = (int)((waves + 3) / 4);
     hipLaunchKernelGGL(summarize_kernel, dim3(blocks), dim3(256), 0, st, valid, positions, qoff, Sq, nQB,
-                       key_valid, key_positions, Sk, nKT, B, qsum, ksum);
+                       key_valid, key_positions, Sk, nKT, B, qsum, ksum, kanchor);
     return check_launch("summarize_kernel");
 }
 
@@ -702,6 +819,8 @@ int check_fwd_args(const void* q, const void* k, const void* v, const void* prof
     const size_t np_elems = (size_t)B * Hq * Sq * E;
     if (nq_elems >= (size_t(1) << 40) || np_elems >= (size_t(1) << 40))
         return fail(INKATTN_ERR_SHAPE, "tensor too large");
+    if ((size_t)Sq * E * (profiles_dtype == INKATTN_F32 ? 4 : 2) >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one (batch row, head) block of profiles must stay below 4 GiB");
     if ((size_t)B * Sq == 0) return INKATTN_OK;
     if (!q || !profiles || !sink || !out || !lse) return fail(INKATTN_ERR_NULL, "q/profiles/sink/out/lse is NULL");
     if (Sk > 0 && (!k || !v)) return fail(INKATTN_ERR_NULL, "k or v is NULL");
@@ -737,10 +856,10 @@ void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
 
 extern "C" {
 
-size_t attn_fwd_workspace_size(int B, int Sq, int Sk)
+size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D)
 {
-    if (B <= 0 || Sq < 0 || Sk < 0) return 0;
-    return summaries_bytes(B, Sq, Sk);
+    if (B <= 0 || Sq < 0 || Sk < 0 || Hkv < 0 || D < 0) return 0;
+    return summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D);
 }
 
 int attn_query_block(void) { return BM; }
@@ -772,12 +891,32 @@ int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
     if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if ((size_t)B * ((size_t)Sq + Sk) == 0) return INKATTN_OK;
-    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
-    const int nQB = ceil_div(Sq, BM);
-    TileSummary* qsum = (TileSummary*)workspace;
-    TileSummary* ksum = qsum + (size_t)B * nQB;
+    if (int rc = check_workspace(workspace, workspace_bytes, summaries_bytes(B, Sq, Sk))) return rc;
     return launch_summaries(valid, positions, ma.key_valid, ma.key_positions, (int)query_offset, B, Sq, Sk,
-                            qsum, ksum, (hipStream_t)stream);
+                            workspace, (hipStream_t)stream);
+}
+
+int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_valid, int64_t query_offset,
+                      int B, int Sq, int Sk, int Hkv, int D, void* workspace, size_t workspace_bytes,
+                      void* stream)
+{
+    g_last_error[0] = '\0';
+    if (Hkv < 1) return fail(INKATTN_ERR_SHAPE, "Hkv=%d must be >= 1", Hkv);
+    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(valid, key_valid, nullptr, nullptr, query_offset, B, Sq, Sk, &ma)) return rc;
+    if ((size_t)B * Sk == 0) return INKATTN_OK;
+    if (!v) return fail(INKATTN_ERR_NULL, "v is NULL");
+    if (!aligned(v, 16)) return fail(INKATTN_ERR_ALIGN, "v must be 16-byte aligned");
+    if (int rc = check_workspace(workspace, workspace_bytes,
+                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
+        return rc;
+    const size_t chunks = (size_t)B * Sk * Hkv * D / 8;
+    if ((chunks + 255) / 256 >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
+    _Float16* v16 = (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk));
+    hipLaunchKernelGGL(stage_values_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, (const __bf16*)v, ma.key_valid, B, Sk, Hkv * D, v16);
+    return check_launch("stage_values_kernel");
 }
 
 int attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -797,7 +936,11 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
         return rc;
     if (window >= (int64_t(1) << 31) || window < 0) window = 0;
     if ((size_t)B * Sq == 0) return INKATTN_OK;   // nothing to write
-    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
+    if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
+    if (int rc = check_workspace(workspace, workspace_bytes,
+                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
+        return rc;
 
     hipStream_t st = (hipStream_t)stream;
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
@@ -806,7 +949,8 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
     FwdParams p;
     p.q = (const __bf16*)q;
     p.k = (const __bf16*)k;
-    p.v = (const __bf16*)v;
+    (void)v;   // read through the fp16 copy attn_stage_values wrote
+    p.v16 = (const _Float16*)((const char*)workspace + summaries_bytes(B, Sq, Sk));
     p.profiles = profiles;
     p.sink = sink;
     p.valid = valid;
@@ -815,6 +959,7 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
     p.key_positions = ma.key_positions;
     p.qsum = (const TileSummary*)workspace;
     p.ksum = p.qsum + (size_t)B * nQB;
+    p.kanchor = (const int*)((const char*)workspace + tile_summary_bytes(B, Sq, Sk));
     p.out = out;
     p.lse = lse;
     p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.E = E;
@@ -857,9 +1002,16 @@ int attn_fwd(const void* q, const void* k, const void* v,
     if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
         return rc;
     if ((size_t)B * Sq == 0) return INKATTN_OK;
-    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
+    if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
+    if (int rc = check_workspace(workspace, workspace_bytes,
+                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
+        return rc;
     if (int rc = attn_plan(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, workspace,
                            workspace_bytes, stream))
+        return rc;
+    if (int rc = attn_stage_values(v, valid, key_valid, query_offset, B, Sq, Sk, Hkv, D, workspace,
+                                   workspace_bytes, stream))
         return rc;
     return attn_fwd_planned(q, k, v, profiles, profiles_dtype, sink, valid, key_valid, positions, key_positions,
                             window, query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, lse, workspace, workspace_bytes,
@@ -901,13 +1053,13 @@ int attn_debug_tiles(const uint8_t* valid, const uint8_t* key_valid,
     const size_t n = (size_t)B * nQB * nKT;
     if (n == 0) return INKATTN_OK;
     if (!tile_class) return fail(INKATTN_ERR_NULL, "tile_class is NULL");
-    if (int rc = check_workspace(workspace, workspace_bytes, B, Sq, Sk)) return rc;
+    if (int rc = check_workspace(workspace, workspace_bytes, summaries_bytes(B, Sq, Sk))) return rc;
     if (n >= (size_t(1) << 40)) return fail(INKATTN_ERR_SHAPE, "too many tiles");
     hipStream_t st = (hipStream_t)stream;
     TileSummary* qsum = (TileSummary*)workspace;
     TileSummary* ksum = qsum + (size_t)B * nQB;
     if (int rc = launch_summaries(valid, positions, ma.key_valid, ma.key_positions, (int)query_offset,
-                                  B, Sq, Sk, qsum, ksum, st))
+                                  B, Sq, Sk, workspace, st))
         return rc;
     hipLaunchKernelGGL(debug_tiles_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, qsum, ksum,
                        (int)window, (int)query_offset, B, Sq, Sk, nQB, nKT, tile_class);
