@@ -98,23 +98,31 @@ def traffic_from_profiles(workload: str):
 
 
 def cpu_baseline(x, target_s: float, seed: int = 11):
-    """The oracle as it stands, on a bounded random sample of the workload's rows."""
+    """The oracle as it stands, on a bounded random sample of the workload's rows.
+
+    The sample grows by 4x from 64 rows until one timing is long enough to
+    extrapolate from, then is sized to about ``target_s`` seconds.
+    """
+    import torch
     import oracle
     from transformer_attention_03_amd import workloads as W
     w = x["workload"]
-    cnt = allowed_counts(x).reshape(-1)
-    probe = W.sample_rows(w.B, w.S, 4, seed)
-    t, _ = oracle.timed_fwd(x, probe)
-    per_pair = t / max(1, int(cnt[probe.numpy()].sum()))
-    budget_pairs = target_s / max(per_pair, 1e-12)
-    mean_pairs = max(1.0, float(cnt.mean()))
-    n = int(max(8, min(w.B * w.S, budget_pairs / mean_pairs)))
-    rows = W.sample_rows(w.B, w.S, n, seed + 1)
+    total = w.B * w.S
+    n = min(64, total)
+    while True:
+        t, _ = oracle.timed_fwd(x, W.sample_rows(w.B, w.S, n, seed))
+        if t >= target_s / 8 or n >= total:
+            break
+        n = min(total, n * 4)
+    if n < total and t < 0.75 * target_s:
+        n = int(min(total, max(n, n * target_s / max(t, 1e-9))))
+    rows = torch.arange(total) if n >= total else W.sample_rows(w.B, w.S, n, seed + 1)
     t, _ = oracle.timed_fwd(x, rows)
+    cnt = allowed_counts(x).reshape(-1)
     pairs = int(cnt[rows.numpy()].sum()) * w.Hq
     flops = 4.0 * w.D * pairs
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{rows.numel()} random query rows of {w.B * w.S} (all heads), {pairs} unmasked pairs, "
+            "sample": f"{rows.numel()} {'(all)' if n >= total else 'random'} query rows of {total} (all {w.Hq} heads), {pairs} unmasked pairs, "
                       f"{t:.1f} s wall, fp64"}
 
 
