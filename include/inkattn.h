@@ -74,8 +74,9 @@ enum inkattn_status {
  * Bytes of device workspace attn_fwd needs for these sizes: what the
  * scheduler pre-pass writes (per-tile mask summaries, 16 bytes per 32-token
  * query block and per 64-key tile, then one int32 document start column per
- * key, padded to whole 64-key tiles; each part rounded up to 256 bytes), followed by an fp16 copy of the
- * values, B*Sk*Hkv*D*2 bytes.  Never fails; returns 0 for non-positive B.
+ * key, padded to whole 64-key tiles; each part rounded up to 256 bytes),
+ * followed by an fp16 copy of the values in whole 64-key tiles,
+ * B*Hkv*ceil(Sk/64)*64*D*2 bytes.  Never fails; returns 0 for non-positive B.
  */
 size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D);
 
@@ -128,9 +129,12 @@ int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
 
 /*
  * attn_stage_values -- converts v [B, Sk, Hkv, D] (bf16) into the fp16 copy
- * the attention kernel stages from, in `workspace` after the summaries.  Each
- * value is saturated to +-65504; values of keys whose key_valid is 0 are
- * written as 0.  The probabilities multiply the values in fp16 MFMA (fp16
+ * the attention kernel stages from, in `workspace` after the summaries: per
+ * (batch row, K/V head, 64-key tile) the tile's values transposed, D rows of
+ * 64 keys, the keys of each row in the order the kernel's PV product consumes
+ * them (a layout private to this library).  Each value is saturated to
+ * +-65504; values of keys whose key_valid is 0, and of the padding past Sk,
+ * are written as 0.  The probabilities multiply the values in fp16 MFMA (fp16
  * keeps 11 significant bits where bf16 keeps 8; a bf16 value inside the fp16
  * range converts exactly).  key_valid defaults as in attn_fwd.  One call per
  * layer (the values differ per layer).

@@ -42,7 +42,8 @@ def test_status_strings_and_sizes():
     # tile summaries (16 B per query block / key tile) + key start columns (4 B per key),
     # each rounded up to 256 B, then the fp16 values
     assert binding.attn_fwd_workspace_size(1, 128, 128, 2, 64) == 256 + 512 + 128 * 2 * 64 * 2
-    assert binding.attn_fwd_workspace_size(2, 33, 65, 1, 128) == 256 + 1024 + 2 * 65 * 128 * 2
+    # values are staged in whole 64-key tiles: 65 keys take two
+    assert binding.attn_fwd_workspace_size(2, 33, 65, 1, 128) == 256 + 1024 + 2 * 128 * 128 * 2
     assert binding.attn_fwd_workspace_size(40, 64, 64, 1, 64) == 2048 + 40 * 64 * 4 + 40 * 64 * 64 * 2
     assert binding.attn_fwd_workspace_size(0, 10, 10, 1, 64) == 0
 

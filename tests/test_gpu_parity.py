@@ -179,6 +179,22 @@ def test_query_slice_with_offset():
     np.testing.assert_allclose(lse, full_lse[:, a:a + n], atol=1e-6, rtol=0)
 
 
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("a", [31, 63, 95, 130])
+def test_query_slice_first_rows_bias(a, pdt):
+    """A query slice starting just past a key tile: the first local rows read
+    profile runs that start at distance 0..3 of their row, in the first row of
+    the profile block."""
+    n = 70
+    x = W.custom(B=1, S=a + n, Hq=4, Hkv=1, D=128, E=200, seed=126, profiles_dtype=pdt)
+    y = dict(q=x["q"][:, a:].contiguous(), k=x["k"], v=x["v"],
+             profiles=x["profiles"][:, :, a:].contiguous(), sink=x["sink"][:, a:].contiguous(),
+             valid=x["valid"][:, a:].contiguous(), key_valid=x["valid"],
+             positions=x["positions"][:, a:].contiguous(), key_positions=x["positions"],
+             window=None, query_offset=a)
+    check_full(y, f"cp_first_rows_{a}")
+
+
 def test_debug_counts_and_tiles_match_oracle_mask():
     for name in ("packed_window", "tailpad_G4_D128", "G16_two_chunks", "window_G4_D64"):
         x = SMALL[name]()

@@ -15,34 +15,35 @@
 //      column over real tokens and the number of real tokens, plus each key's
 //      start column.  Every skip / full / masked decision of the main kernel
 //      comes from these summaries.
-//   2. stage_values_kernel: v (bf16) -> fp16 copy, zero at keys that are not
-//      real (the probabilities multiply the values in fp16).
+//   2. stage_values_kernel: v (bf16) -> fp16 V^T per 64-key tile, keys in the
+//      order the PV product consumes them, zero at keys that are not real
+//      (the probabilities multiply the values in fp16).
 //   3. attn_fwd_kernel: one workgroup per (batch row, K/V head, head chunk,
 //      group of 32-token query blocks); each wave owns one (query head,
-//      32-token block).  Each 64-key K/V tile is staged once in LDS by DMA
+//      32-token block).  Each 64-key K / V^T tile is staged once in LDS by DMA
 //      (buffer_load ... lds, XOR-swizzled rows) and serves every wave of the
 //      workgroup, i.e. every query head of the chunk (GQA).  The next live
-//      tile's DMA is issued before the current tile is computed and lands in
-//      the second buffer (one barrier per tile).  Per wave, each 32-key half
-//      of a tile is processed in turn:
-//        S^T = K Q^T      bf16 MFMA 32x32x16, keys on M and queries on N, so
-//                         each lane owns one query column: row reductions are
+//      tile's DMA and this wave's bias for it are issued at the start of the
+//      current tile (one barrier per tile).  Per wave and tile:
+//        S^T = K Q^T      bf16 MFMA 32x32x16 as two interleaved chains (one per
+//                         32-key half), keys on M and queries on N, so each
+//                         lane owns one query column: row reductions are
 //                         in-lane plus one exchange between the wave halves;
-//                         the accumulator starts from the relative bias
-//                         (scaled by sqrt(D)), gathered from the query's own
-//                         profile row as contiguous 4-entry runs;
+//                         each chain starts from the relative bias (scaled by
+//                         sqrt(D)), gathered from the query's own profile row
+//                         as contiguous 4-entry runs one tile ahead, or from 0;
 //        mask             only on tiles classed as masked;
-//        online softmax   running max / denominator per lane, started from
-//                         the sink logit (the sink's weight enters the
-//                         denominator, never the value sum); the running max
-//                         moves only when a row's tile max exceeds it by more
-//                         than 8 (log2 units), so probabilities stay <= 2^8
-//                         and most tiles skip the output rescale;
+//        online softmax   running max / denominator per lane over the 64 keys,
+//                         started from the sink logit (the sink's weight
+//                         enters the denominator, never the value sum); the
+//                         running max moves only when a row's tile max
+//                         exceeds it by more than 8 (log2 units), so
+//                         probabilities stay <= 2^8 and most tiles skip the
+//                         output rescale;
 //        O^T += V^T P^T   fp16 MFMA 32x32x16; P^T comes straight from the S^T
-//                         accumulator registers (keys inside each 16-key step
-//                         are permuted the same way on both operands) and V^T
-//                         is read from row-major LDS with the transposing
-//                         ds_read_b64_tr_b16.
+//                         accumulator registers and V^T is one 16-byte LDS
+//                         read per lane and MFMA (the staging pass put the
+//                         keys in the same order as P^T's).
 //      Epilogue: out = O / l, lse = ln(2) * (m + log2 l).
 #include <hip/hip_runtime.h>
 
@@ -62,6 +63,8 @@ constexpr int BN = 64;   // keys per K/V tile (two MFMA M-blocks of 32)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
+// s_waitcnt operand: vmcnt(0) lgkmcnt(0), expcnt not waited on
+constexpr int WAIT_VM_LGKM = 0x0070;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -200,6 +203,29 @@ struct FwdParams {
     float c_log2;    // head_dim^-0.5 * log2(e)
 };
 
+// A value the compiler may not look through (no constant is split off it and
+// no two loads using such offsets are merged).  The empty asm only exists in
+// the device pass; the host pass never generates kernel code.
+__device__ __forceinline__ unsigned opaque(unsigned x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(x));
+#endif
+    return x;
+}
+
+// Wait for every outstanding memory operation of the wave, then meet the
+// workgroup.  The wait is the builtin so that the compiler's own wait counting
+// knows of it; the barrier is an asm statement with a memory clobber so that
+// no memory access moves across it.
+__device__ __forceinline__ void wait_all_and_barrier()
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM);
+#endif
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Max / sum of a value and its twin in the other wave half (same query).
 __device__ __forceinline__ float half_max(float x)
 {
@@ -219,23 +245,34 @@ struct TileDesc {
     int masked;    // some wave of the workgroup masks this tile
 };
 
-// LDS layout of one staged K / V tile.  Each 16-byte DMA instruction writes
+// LDS layout of one staged K tile.  Each 16-byte DMA instruction writes
 // 1 KB of LDS contiguously, i.e. RPI whole rows, so rows cannot be padded
-// one by one; instead rows come in groups of RPI (pitch KGP / VGP bytes) and
-// the 16-byte chunks of a row are XOR-swizzled.  Both choices make the MFMA
-// operand reads (16 rows x 16 B per phase for K, 4 rows x 64 B per phase
-// for the transposing V reads) bank-conflict free on the 64-bank LDS.
+// one by one; instead rows come in groups of RPI (pitch KGP bytes) and the
+// 16-byte chunks of a row are XOR-swizzled, which makes the MFMA operand
+// reads (16 rows x 16 B per phase) bank-conflict free on the 64-bank LDS.
 template <int D> struct TileLayout;
 template <> struct TileLayout<128> {
-    static constexpr int RPI = 4, KGP = 1088, VGP = 1024;
+    static constexpr int RPI = 4, KGP = 1088;
     __device__ static constexpr int ksw(int t) { return t; }
-    __device__ static constexpr int vsw(int t) { return 4 * t; }
 };
 template <> struct TileLayout<64> {
-    static constexpr int RPI = 8, KGP = 1088, VGP = 1024;
+    static constexpr int RPI = 8, KGP = 1088;
     __device__ static constexpr int ksw(int t) { return t >> 1; }
-    __device__ static constexpr int vsw(int t) { return 4 * ((t >> 1) & 1); }
 };
+
+// Staged value tiles.  The staging pass writes, per (batch row, K/V head,
+// 64-key tile), V^T as D rows of 64 fp16 values (128 B), the keys of each
+// 16-key step in the order the PV MFMA consumes them: slot 8 hh + t of a step
+// holds key 8 (t / 4) + 4 hh + ((t % 4) ^ 3), the key order of the P^T
+// operand taken from the S^T accumulator.  A lane then reads its 8 keys of a
+// step as one 16-byte chunk.  In LDS the 16-byte chunk c of row d sits at
+// chunk c ^ vt_swz(d), which spreads the 16 rows of one read phase over all
+// 64 banks.
+__host__ __device__ constexpr int vt_slot(int key)   // key within the tile -> slot
+{
+    return 16 * (key / 16) + 8 * ((key / 4) % 2) + 4 * ((key % 16) / 8) + ((key % 4) ^ 3);
+}
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
 
 enum : int { BIAS_NONE = 0, BIAS_FAST = 1, BIAS_EDGE = 2 };
 
@@ -262,7 +299,9 @@ void attn_fwd_kernel(FwdParams p)
     constexpr int GPW = NGRP / NW;           // DMA groups per wave
     static_assert(NGRP % NW == 0, "DMA groups must divide among waves");
     constexpr int KBYTES = NGRP * L::KGP;
-    constexpr int VBYTES = NGRP * L::VGP;
+    constexpr int VBYTES = D * 128;          // one V^T tile: D rows of 64 fp16
+    constexpr int NVG = D / 8;               // 1 KB DMA groups per V^T tile (8 rows each)
+    static_assert(NVG % NW == 0 && NW % 2 == 0, "V^T DMA groups must divide among an even number of waves");
     constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 2 * VBYTES;
 
     __shared__ __attribute__((aligned(1024))) char smem[CA_OFF + 2 * BN * 4];
@@ -360,18 +399,22 @@ void attn_fwd_kernel(FwdParams p)
         return d;
     };
 
-    // ---- K / V staging by LDS DMA.  The buffer resources cover rows 0..Sk-1
-    // of this (batch row, K/V head); rows past Sk read as zero.
+    // ---- K / V staging by LDS DMA.  The K resource covers rows 0..Sk-1 of
+    // this (batch row, K/V head), rows past Sk read as zero; the V^T resource
+    // covers the staged tiles of this (batch row, K/V head).
     const int krow = p.Hkv * D * 2;                     // bytes between consecutive keys
     const unsigned nrec = p.Sk > 0 ? (unsigned)((size_t)(p.Sk - 1) * krow + D * 2) : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.k + ((size_t)b * p.Sk * p.Hkv + g) * D), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.v16 + ((size_t)b * p.Sk * p.Hkv + g) * D), 0, nrec, 0x00020000);
-    // lane -> (row t of its DMA group, LDS chunk slot pc): it fetches the chunk that lands there
+        (void*)(p.v16 + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(D * BN)), 0,
+        (unsigned)p.nKT * (unsigned)VBYTES, 0x00020000);
+    // K: lane -> (row t of its DMA group, LDS chunk slot pc): it fetches the chunk that lands there
     const int dt = lane / CPR, dpc = lane % CPR;
     const int kvoff = dt * krow + 16 * (dpc ^ L::ksw(dt));
-    const int vvoff = (dt ^ 3) * krow + 16 * (dpc ^ L::vsw(dt));   // V row dt ^ 3 -> slot dt
+    // V^T: lane -> (row 8 a + lane / 8 of DMA group a, LDS chunk lane % 8); the
+    // groups of a wave all have the parity of the wave (NW is even)
+    const int vvoff = (lane / 8) * 128 + 16 * ((lane % 8) ^ vt_swz(8 * (wave & 1) + lane / 8));
     // key start columns of this batch row, padded to whole tiles with INT_MIN
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.kanchor + (size_t)b * p.nKT * BN), 0, (unsigned)p.nKT * BN * 4u, 0x00020000);
@@ -380,11 +423,19 @@ void attn_fwd_kernel(FwdParams p)
 #pragma unroll
         for (int u = 0; u < GPW; ++u) {
             const int a = wave + NW * u;                   // DMA group (uniform)
+            // (the offsets are named values: an expression written into the
+            // builtin's argument list keeps the host pass from emitting the
+            // kernel's launch stub)
             const int soff = (j0 + a * L::RPI) * krow;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 krsrc, (lds_void*)(smem + K_OFF + bufsel * KBYTES + a * L::KGP), 16, kvoff, soff, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NVG / NW; ++u) {
+            const int a = wave + NW * u;
+            const int soff = d.kt * VBYTES + a * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vrsrc, (lds_void*)(smem + V_OFF + bufsel * VBYTES + a * L::VGP), 16, vvoff, soff, 0, 0);
+                vrsrc, (lds_void*)(smem + V_OFF + bufsel * VBYTES + a * 1024), 16, vvoff, soff, 0, 0);
         }
         if (d.masked && wave == 0)   // 64 start columns: one dword per lane
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -395,23 +446,19 @@ void attn_fwd_kernel(FwdParams p)
     // K swizzle XORs at most the two low bits of the chunk index, so the
     // chunk of k-step kk sits at 32*kk from one of two lane bases (even / odd kk).
     // Accumulator element (jj, e) of a 32-key half is key 8 jj + 4 hh + (e ^ 3): the
-    // K row a lane supplies is qi ^ 3 and the DMA stores V row t of each 4-row quad
-    // at slot t ^ 3, so that keys 4k..4k+3 appear in decreasing order, the order of
-    // increasing distance, i.e. the memory order of a profile run.
+    // K row a lane supplies is qi ^ 3, so that keys 4k..4k+3 appear in
+    // decreasing order, the order of increasing distance, i.e. the memory
+    // order of a profile run.
     const int krow_lane = qi ^ 3;
     const int kt_row = krow_lane % L::RPI;
     const int ksw = L::ksw(kt_row);
     const int krowbase = (krow_lane / L::RPI) * L::KGP + kt_row * (2 * D) + 16 * (hh ^ (ksw & 1));
     const int kbase_even = krowbase + 32 * (ksw >> 1);
     const int kbase_odd = krowbase - 32 * (ksw >> 1);
-    int voff[NDB];
+    // V^T operand of 16-key step c: row qi (+ 32 per d-block), chunk 2 c + hh
+    int voff[4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        const int r = 4 * hh + (lane & 15) / 4;                // row within an 8-key half-step
-        const int t = r % L::RPI;
-        const int e = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // fp16 element in the row
-        voff[db] = (r / L::RPI) * L::VGP + t * (2 * D) + 16 * (((2 * e) / 16) ^ L::vsw(t)) + (2 * e) % 16;
-    }
+    for (int c = 0; c < 4; ++c) voff[c] = qi * 128 + 16 * ((2 * c + hh) ^ vt_swz(qi));
 
     // ---- relative bias.  sacc[s][4*jj+e] is the profile entry of key
     // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance R - 8 jj - 4 hh - (e ^ 3)
@@ -437,8 +484,9 @@ void attn_fwd_kernel(FwdParams p)
     // fp32 sub-tiles whose distances all lie in [0, E): 4 runs of 4 entries,
     // the run of jj starting at distance R - 8 jj - 4 hh - 3 (element e: + e)
     auto load_bias_fast = [&](int js, int s) {
-        // lowest distance read (run of jj = 3), >= 0 on such sub-tiles
-        const unsigned vo = prow_off + (3 - js) * PE;
+        // lowest distance read (run of jj = 3), >= 0 on such sub-tiles; kept
+        // opaque so that no constant is split off into the instruction offset
+        const unsigned vo = opaque(prow_off + (3 - js) * PE);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -447,156 +495,181 @@ void attn_fwd_kernel(FwdParams p)
             for (int e = 0; e < 4; ++e) sacc[s][4 * jj + e] = w[e];
         }
     };
-    // any sub-tile, entry by entry; 0 outside [0, E)
+    // any sub-tile, entry by entry (raw fp32 bits, or the bf16 bits in the low
+    // half).  Distances outside [0, E) are zeroed when the accumulator is
+    // initialised, so that nothing waits for these loads before then.
     auto load_bias_edge = [&](int js, int s) {
         const unsigned vo = prow_off - (unsigned)js * PE;
-        const int R = gi - js;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const unsigned off = vo + (30 - 8 * jj - (e ^ 3)) * PE;
-                float v;
-                if (PROF_BF16) {
-                    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
-                    v = __uint_as_float((unsigned)u << 16);
-                } else {
-                    v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(prsrc, off, 0, 0));
-                }
-                const unsigned r = (unsigned)(R - 8 * jj - 4 * hh - (e ^ 3));
-                sacc[s][4 * jj + e] = r < (unsigned)p.E ? v : 0.0f;
+                // the exact entry offset, opaque: loads of neighbouring entries
+                // must not merge into one wider load whose first entry may lie
+                // before the block (which would read the whole load as 0)
+                const unsigned off = opaque(vo + (30 - 8 * jj - (e ^ 3)) * PE);
+                unsigned u;
+                if (PROF_BF16) u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
+                else u = __builtin_amdgcn_raw_buffer_load_b32(prsrc, off, 0, 0);
+                sacc[s][4 * jj + e] = __uint_as_float(u);
             }
         }
     };
-    // Bias loads of sub-tile s of tile d (returns how many load instructions
-    // were issued: 4 runs, 16 entries, or none).
+    // Initial accumulator of sub-tile s (keys js .. js + 31) from the bias
+    // registers: the profile entry times sqrt(D), 0 at distances outside [0, E).
+    auto bias_init = [&](int bc, int js, int s) -> f32x16 {
+        f32x16 c;
+        if (bc == BIAS_FAST && !PROF_BF16) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) c[t] = sacc[s][t] * INV_SCALE;
+        } else {
+            const int R = gi - js;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned r = (unsigned)(R - 8 * jj - 4 * hh - (e ^ 3));
+                    const float raw = sacc[s][4 * jj + e];
+                    const float v = PROF_BF16 ? __uint_as_float(__float_as_uint(raw) << 16) : raw;
+                    c[4 * jj + e] = r < (unsigned)p.E ? v * INV_SCALE : 0.0f;
+                }
+        }
+        return c;
+    };
+    // Bias loads of sub-tile s of tile d into sacc[s]; returns the sub-tile's
+    // bias class (BIAS_NONE: nothing loaded, the accumulator starts at zero).
     auto load_bias = [&](const TileDesc& d, int s) -> int {
-        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return 0;
+        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE;
         const int js = d.kt * BN + 32 * s;
         const int bc = bias_class(qlo, qhi, js, p.E);
-        if (bc == BIAS_FAST && !PROF_BF16) { load_bias_fast(js, s); return 4; }
-        if (bc != BIAS_NONE) { load_bias_edge(js, s); return 16; }
-        return 0;
+        if (bc == BIAS_FAST && !PROF_BF16) load_bias_fast(js, s);
+        else if (bc != BIAS_NONE) load_bias_edge(js, s);
+        return bc;
     };
-    auto forget = [&](int s) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) sacc[s][t] = __builtin_nondeterministic_value(sacc[s][t]);
-    };
+
+    // Software pipeline, per 64-key tile: the DMA of the next live tile and the
+    // bias of this wave's part of it are issued first; then both 32-key halves
+    // of the current tile run S^T = K Q^T as two interleaved MFMA chains, one
+    // softmax step covers the 64 keys, and O^T += V^T P^T follows.  One
+    // barrier per tile.
     TileDesc cur = next_live(kt_lo - 1);
-    forget(0);
-    forget(1);
-    if (cur.kt <= kt_hi) issue_tile(cur, 0);
-    __syncthreads();
+    int bc0 = BIAS_NONE, bc1 = BIAS_NONE;   // bias classes of the current tile's halves
+    if (cur.kt <= kt_hi) {
+        issue_tile(cur, 0);
+        bc0 = load_bias(cur, 0);
+        bc1 = load_bias(cur, 1);
+    }
+    wait_all_and_barrier();
     int buf = 0;
     while (cur.kt <= kt_hi) {
         const TileDesc nxt = next_live(cur.kt);
         const int j0 = cur.kt * BN;
+        const bool compute = cur.my_cls != TILE_SKIP;
 
-        if (cur.my_cls != TILE_SKIP) {
-            // Sub-tile 0's bias loads go out first, then the DMA of the next
-            // tile, then sub-tile 1's bias loads (needed half a tile later).
-            const int bc0 = bias_class(qlo, qhi, j0, p.E);
-            const int bc1 = bias_class(qlo, qhi, j0 + 32, p.E);
-            if (load_bias(cur, 0) == 0) forget(0);
-            asm volatile("" ::: "memory");
-            if (nxt.kt <= kt_hi) issue_tile(nxt, buf ^ 1);
-            asm volatile("" ::: "memory");
-            if (load_bias(cur, 1) == 0) forget(1);
-            asm volatile("" ::: "memory");
+        // ---- accumulators start from this tile's bias (scaled by sqrt(D)),
+        // which frees the bias registers for the next tile
+        f32x16 acc[2];
+        if (compute) {
+            if (bc0 != BIAS_NONE) acc[0] = bias_init(bc0, j0, 0);
+            if (bc1 != BIAS_NONE) acc[1] = bias_init(bc1, j0 + 32, 1);
+        }
+        asm volatile("" ::: "memory");
+        if (nxt.kt <= kt_hi) issue_tile(nxt, buf ^ 1);
+        asm volatile("" ::: "memory");
+        const int nb0 = load_bias(nxt, 0);
+        const int nb1 = load_bias(nxt, 1);
+        asm volatile("" ::: "memory");
 
+        if (compute) {
             const char* kb = smem + K_OFF + buf * KBYTES;
             const char* vb = smem + V_OFF + buf * VBYTES;
+            constexpr int KHALF = (32 / L::RPI) * L::KGP;   // +32 keys in the K buffer
+            // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains
+            {
+                const bf16x8 a0 = *(const bf16x8*)(kb + kbase_even);
+                const bf16x8 a1 = *(const bf16x8*)(kb + kbase_even + KHALF);
+                acc[0] = bc0 != BIAS_NONE ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], acc[0], 0, 0, 0)
+                                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
+                acc[1] = bc1 != BIAS_NONE ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], acc[1], 0, 0, 0)
+                                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
+            }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // ---- S^T = K Q^T (+ bias * sqrt(D)) for keys j0 + 32 s .. + 31
-                const bool hb = (s == 0 ? bc0 : bc1) != BIAS_NONE;
-                f32x16 acc;
-                if (hb) {
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) acc[t] = sacc[s][t] * INV_SCALE;
-                } else {
-                    acc = f32x16{};
-                }
-                // consumed: the registers carry nothing into later tiles
-                forget(s);
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk + s * (32 / L::RPI) * L::KGP;
-                    const bf16x8 a = *(const bf16x8*)(kb + ko);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], acc, 0, 0, 0);
-                }
+            for (int kk = 1; kk < NKK; ++kk) {
+                const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk;
+                const bf16x8 a0 = *(const bf16x8*)(kb + ko);
+                const bf16x8 a1 = *(const bf16x8*)(kb + ko + KHALF);
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
+            }
 
-                // ---- mask.  Element (jj, e) is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
-                if (cur.my_cls == TILE_MASKED) {
-                    const int* ca = (const int*)(smem + CA_OFF + buf * BN * 4);
+            // ---- mask.  Element (jj, e) of half s is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
+            if (cur.my_cls == TILE_MASKED) {
+                const int* ca = (const int*)(smem + CA_OFF + buf * BN * 4);
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int kl = 32 * s + 8 * jj + 4 * hh;
+                        const int kl = 32 * s2 + 8 * jj + 4 * hh;
                         const i32x4 c4 = *(const i32x4*)(ca + kl);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (!key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
-                                acc[4 * jj + e] = -INFINITY;
+                                acc[s2][4 * jj + e] = -INFINITY;
                     }
-                }
+            }
 
-                // ---- online softmax (sink-initialised, lazily rescaled), log2 units
-                float mx = -INFINITY;
+            // ---- online softmax over the 64 keys (sink-initialised, lazily rescaled), log2 units
+            float mx = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) mx = fmaxf(mx, acc[t]);
-                mx = half_max(mx * p.c_log2);
-                const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
-                const float m_new = move ? mx : m;
-                const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-                if (__builtin_amdgcn_ballot_w64(move) != 0) {
-                    const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
-                    l *= alpha;
+            for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(acc[0][t], acc[1][t]));
+            mx = half_max(mx * p.c_log2);
+            const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
+            const float m_new = move ? mx : m;
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
+                l *= alpha;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                        for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-                }
-                m = m_new;
-                f16x8 pb[2];
+                    for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+            }
+            m = m_new;
+            // pb[2 s + c]: 16-key step c of half s (keys in the same order as V's rows)
+            f16x8 pb[4];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], p.c_log2, -m_use));
-                    // 16-key step c takes elements jj = 2c, 2c+1 (keys in the same order as V's rows)
-                    pb[t >> 3][t & 7] = (_Float16)pv;
-                }
-                // the denominator sums the fp16-rounded weights the PV product uses
-                float ls0 = 0.0f, ls1 = 0.0f;
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    pb[2 * s2 + (t >> 3)][t & 7] =
+                        (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(acc[s2][t], p.c_log2, -m_use));
+            // the denominator sums the fp16-rounded weights the PV product uses
+            float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) {
-                    ls0 = __builtin_amdgcn_fdot2(half2_t{pb[0][2 * q2], pb[0][2 * q2 + 1]},
-                                                 half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
-                    ls1 = __builtin_amdgcn_fdot2(half2_t{pb[1][2 * q2], pb[1][2 * q2 + 1]},
-                                                 half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
+                    const half2_t w2 = half2_t{pb[c][2 * q2], pb[c][2 * q2 + 1]};
+                    if (q2 & 1) ls1 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
+                    else ls0 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
                 }
-                l += ls0 + ls1;
+            l += ls0 + ls1;
 
-                // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T (d-block db: rows 32 db .. 32 db + 31 of V^T)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    constexpr int HALF = (8 / L::RPI) * L::VGP;   // +8 keys
-                    const int step = ((32 * s + 16 * c) / L::RPI) * L::VGP;
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + step + voff[db]));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + step + HALF + voff[db]));
-                        // whole-vector reinterpretation: keys 4hh+(3..0) then 8+4hh+(3..0)
-                        const s16x8 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        const f16x8 av = __builtin_bit_cast(f16x8, lohi);
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], oacc[db], 0, 0, 0);
-                    }
+                for (int db = 0; db < NDB; ++db) {
+                    const f16x8 av = *(const f16x8*)(vb + voff[c] + db * 32 * 128);
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], oacc[db], 0, 0, 0);
                 }
-            }
-        } else if (nxt.kt <= kt_hi) {
-            issue_tile(nxt, buf ^ 1);
         }
 
-        // this wave's DMA of the next tile has landed; then every wave's has
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // the next tile's DMA (this wave's part) and bias have landed; then
+        // every wave's DMA has
+        wait_all_and_barrier();
+        bc0 = nb0;
+        bc1 = nb1;
         buf ^= 1;
         cur = nxt;
     }
@@ -630,23 +703,40 @@ void attn_fwd_kernel(FwdParams p)
 // that are not real, so that a masked key's weight 0 never meets a value that
 // fp16 cannot hold.  One thread per 8 elements.
 // ---------------------------------------------------------------------------
+// One workgroup per (batch row, K/V head, 64-key tile): v (bf16) -> V^T
+// (fp16, saturated to +-65504, 0 at keys that are not real or lie past Sk),
+// the keys of each row in vt_slot order.
+template <int D>
 __global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restrict__ v,
                                                            const uint8_t* __restrict__ key_valid,
-                                                           int B, int Sk, int HD, _Float16* __restrict__ v16)
+                                                           int Sk, int Hkv, int nKT, _Float16* __restrict__ vt)
 {
-    const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t nchunks = (size_t)B * Sk * HD / 8;
-    if (c >= nchunks) return;
-    const size_t row = c / (HD / 8);                   // b * Sk + j
-    const bf16x8 x = *(const bf16x8*)(v + 8 * c);
-    f16x8 y;
-    if (key_valid[row]) {
+    constexpr int CH = D / 8;                 // 16-byte chunks per key row
+    constexpr int PITCH = BN + 8;             // fp16 per transposed LDS row
+    __shared__ __attribute__((aligned(16))) _Float16 tile[D * PITCH];
+    const int t = blockIdx.x;                 // ((b * Hkv + g) * nKT + kt)
+    const int kt = t % nKT;
+    const int g = (t / nKT) % Hkv;
+    const int b = t / (nKT * Hkv);
+    for (int c = threadIdx.x; c < BN * CH; c += blockDim.x) {
+        const int key = c / CH, dc = c % CH;
+        const int j = kt * BN + key;
+        f16x8 y = f16x8{};
+        if (j < Sk && key_valid[(size_t)b * Sk + j]) {
+            const bf16x8 x = *(const bf16x8*)(v + (((size_t)b * Sk + j) * Hkv + g) * D + 8 * dc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
-    } else {
-        y = f16x8{};
+            for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
+        }
+        const int slot = vt_slot(key);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[(8 * dc + e) * PITCH + slot] = y[e];
     }
-    *(f16x8*)(v16 + 8 * c) = y;
+    __syncthreads();
+    _Float16* dst = vt + (size_t)t * D * BN;
+    for (int c = threadIdx.x; c < D * (BN / 8); c += blockDim.x) {
+        const int d = c / (BN / 8), sc = c % (BN / 8);
+        *(f16x8*)(dst + d * BN + 8 * sc) = *(const f16x8*)(tile + d * PITCH + 8 * sc);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -735,7 +825,7 @@ size_t summaries_bytes(int B, int Sq, int Sk)
 
 size_t values_bytes(int B, int Sk, int Hkv, int D)
 {
-    return (size_t)B * Sk * Hkv * D * sizeof(_Float16);
+    return (size_t)B * Hkv * ceil_div(Sk, BN) * BN * D * sizeof(_Float16);
 }
 
 // Defaults of the optional arguments and the checks shared by every entry point.
@@ -911,11 +1001,15 @@ int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_va
     if (int rc = check_workspace(workspace, workspace_bytes,
                                  summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
         return rc;
-    const size_t chunks = (size_t)B * Sk * Hkv * D / 8;
-    if ((chunks + 255) / 256 >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
+    const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
+    if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
     _Float16* v16 = (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk));
-    hipLaunchKernelGGL(stage_values_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                       (hipStream_t)stream, (const __bf16*)v, ma.key_valid, B, Sk, Hkv * D, v16);
+    if (D == 128)
+        hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream,
+                           (const __bf16*)v, ma.key_valid, Sk, Hkv, ceil_div(Sk, BN), v16);
+    else
+        hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream,
+                           (const __bf16*)v, ma.key_valid, Sk, Hkv, ceil_div(Sk, BN), v16);
     return check_launch("stage_values_kernel");
 }
 
