@@ -621,7 +621,10 @@ void attn_fwd_kernel(FwdParams p)
             // ---- online softmax over the 64 keys (sink-initialised, lazily rescaled), log2 units
             float mx = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fmaxf(acc[0][t], acc[1][t]));
+            for (int t = 0; t < 16; ++t) {
+                mx = fmaxf(mx, acc[0][t]);
+                mx = fmaxf(mx, acc[1][t]);
+            }
             mx = half_max(mx * p.c_log2);
             const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
             const float m_new = move ? mx : m;
@@ -635,34 +638,55 @@ void attn_fwd_kernel(FwdParams p)
                     for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
             }
             m = m_new;
-            // pb[2 s + c]: 16-key step c of half s (keys in the same order as V's rows)
+
+            // ---- P^T and O^T += V^T P^T, one 16-key step c at a time: the
+            // weights of step c + 1 are computed while step c's MFMAs run.
+            // pb[c] holds keys 16 c + ... in the order of V^T's staged rows.
             f16x8 pb[4];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    pb[2 * s2 + (t >> 3)][t & 7] =
-                        (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(acc[s2][t], p.c_log2, -m_use));
-            // the denominator sums the fp16-rounded weights the PV product uses
             float ls0 = 0.0f, ls1 = 0.0f;
+            auto make_p = [&](int c) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+                for (int t = 0; t < 8; ++t)
+                    pb[c][t] = (_Float16)__builtin_amdgcn_exp2f(
+                        __builtin_fmaf(acc[c >> 1][8 * (c & 1) + t], p.c_log2, -m_use));
+                // the denominator sums the fp16-rounded weights the PV product uses
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) {
                     const half2_t w2 = half2_t{pb[c][2 * q2], pb[c][2 * q2 + 1]};
                     if (q2 & 1) ls1 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
                     else ls0 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
                 }
-            l += ls0 + ls1;
-
-            // ---- O^T += V^T P^T (d-block db: rows 32 db .. 32 db + 31 of V^T)
+            };
+            // V^T operands of step c + 1 are read while step c's MFMAs run
+            f16x8 avn[NDB];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vb + voff[0] + db * 32 * 128);
+            make_p(0);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const f16x8 av = *(const f16x8*)(vb + voff[c] + db * 32 * 128);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], oacc[db], 0, 0, 0);
+            for (int c = 0; c < 4; ++c) {
+                f16x8 av[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) av[db] = avn[db];
+                if (c < 3) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        avn[db] = *(const f16x8*)(vb + voff[c + 1] + db * 32 * 128);
+                    make_p(c + 1);
                 }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pb[c], oacc[db], 0, 0, 0);
+                if (c < 3) {
+                    // the next step's reads first, then one MFMA per share of its VALU work
+                    __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+                    }
+                }
+            }
+            l += ls0 + ls1;
         }
 
         // the next tile's DMA (this wave's part) and bias have landed; then
