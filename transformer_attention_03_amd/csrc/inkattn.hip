@@ -226,6 +226,24 @@ __device__ __forceinline__ void wait_all_and_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// As wait_all_and_barrier, but the last n_after vector-memory loads of the
+// wave (n_after in {0, 4, 8, 16, 20, 32}) may still be in flight.  s_waitcnt
+// operand: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8.
+__device__ __forceinline__ void wait_dma_and_barrier(int n_after)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    switch (n_after) {
+    case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4074); break;
+    case 32: __builtin_amdgcn_s_waitcnt(0x8070); break;
+    default: __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM); break;
+    }
+#endif
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Max / sum of a value and its twin in the other wave half (same query).
 __device__ __forceinline__ float half_max(float x)
 {
@@ -437,9 +455,13 @@ void attn_fwd_kernel(FwdParams p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 vrsrc, (lds_void*)(smem + V_OFF + bufsel * VBYTES + a * 1024), 16, vvoff, soff, 0, 0);
         }
-        if (d.masked && wave == 0)   // 64 start columns: one dword per lane
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                arsrc, (lds_void*)(smem + CA_OFF + bufsel * BN * 4), 4, 4 * lane, j0 * 4, 0, 0);
+        // the tile's 64 key start columns, one dword per lane; every wave
+        // writes the same values, so that each wave's sequence of memory
+        // instructions is the same on every path (the compiler then counts
+        // the outstanding ones exactly)
+        const int asoff = j0 * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            arsrc, (lds_void*)(smem + CA_OFF + bufsel * BN * 4), 4, 4 * lane, asoff, 0, 0);
     };
 
     // Per-lane LDS byte offsets of the MFMA operands within one buffer.  The
@@ -483,10 +505,9 @@ void attn_fwd_kernel(FwdParams p)
     constexpr float INV_SCALE = D == 128 ? 11.313708498984761f : 8.0f;   // sqrt(D)
     // fp32 sub-tiles whose distances all lie in [0, E): 4 runs of 4 entries,
     // the run of jj starting at distance R - 8 jj - 4 hh - 3 (element e: + e)
-    auto load_bias_fast = [&](int js, int s) {
-        // lowest distance read (run of jj = 3), >= 0 on such sub-tiles; kept
-        // opaque so that no constant is split off into the instruction offset
-        const unsigned vo = opaque(prow_off + (3 - js) * PE);
+    // vo: byte offset of the lowest distance read (run of jj = 3), >= 0 on
+    // such sub-tiles
+    auto load_bias_fast = [&](unsigned vo, int s) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -515,13 +536,12 @@ void attn_fwd_kernel(FwdParams p)
             }
         }
     };
-    // Initial accumulator of sub-tile s (keys js .. js + 31) from the bias
-    // registers: the profile entry times sqrt(D), 0 at distances outside [0, E).
-    auto bias_init = [&](int bc, int js, int s) -> f32x16 {
-        f32x16 c;
+    // Adds sub-tile s's bias (keys js .. js + 31) to its S^T accumulator: the
+    // profile entry times sqrt(D), nothing at distances outside [0, E).
+    auto bias_add = [&](int bc, int js, int s, f32x16& a) {
         if (bc == BIAS_FAST && !PROF_BF16) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) c[t] = sacc[s][t] * INV_SCALE;
+            for (int t = 0; t < 16; ++t) a[t] = __builtin_fmaf(sacc[s][t], INV_SCALE, a[t]);
         } else {
             const int R = gi - js;
 #pragma unroll
@@ -531,10 +551,13 @@ void attn_fwd_kernel(FwdParams p)
                     const unsigned r = (unsigned)(R - 8 * jj - 4 * hh - (e ^ 3));
                     const float raw = sacc[s][4 * jj + e];
                     const float v = PROF_BF16 ? __uint_as_float(__float_as_uint(raw) << 16) : raw;
-                    c[4 * jj + e] = r < (unsigned)p.E ? v * INV_SCALE : 0.0f;
+                    a[4 * jj + e] = __builtin_fmaf(r < (unsigned)p.E ? v : 0.0f, INV_SCALE, a[4 * jj + e]);
                 }
         }
-        return c;
+    };
+    // Load instructions load_bias issues for a class.
+    auto bias_loads = [&](int bc) -> int {
+        return bc == BIAS_NONE ? 0 : (bc == BIAS_FAST && !PROF_BF16) ? 4 : 16;
     };
     // Bias loads of sub-tile s of tile d into sacc[s]; returns the sub-tile's
     // bias class (BIAS_NONE: nothing loaded, the accumulator starts at zero).
@@ -542,16 +565,21 @@ void attn_fwd_kernel(FwdParams p)
         if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE;
         const int js = d.kt * BN + 32 * s;
         const int bc = bias_class(qlo, qhi, js, p.E);
-        if (bc == BIAS_FAST && !PROF_BF16) load_bias_fast(js, s);
+        // the fast path's base is formed before the branch, so that the fast
+        // path writes no register before its loads (a register the other
+        // path loads into would make it wait for those loads)
+        const unsigned vo_fast = opaque(prow_off + (3 - js) * PE);
+        if (bc == BIAS_FAST && !PROF_BF16) load_bias_fast(vo_fast, s);
         else if (bc != BIAS_NONE) load_bias_edge(js, s);
         return bc;
     };
 
-    // Software pipeline, per 64-key tile: the DMA of the next live tile and the
-    // bias of this wave's part of it are issued first; then both 32-key halves
-    // of the current tile run S^T = K Q^T as two interleaved MFMA chains, one
-    // softmax step covers the 64 keys, and O^T += V^T P^T follows.  One
-    // barrier per tile.
+    // Software pipeline, per 64-key tile t: the DMA of the next live tile is
+    // issued first; S^T = K Q^T of both 32-key halves runs as two interleaved
+    // MFMA chains; then tile t's bias (loaded during tile t - 1) is added and
+    // the bias loads of tile t + 1 go out, so that they stay in flight across
+    // the end-of-tile barrier, which waits for the DMA alone; one softmax step
+    // covers the 64 keys and O^T += V^T P^T follows.
     TileDesc cur = next_live(kt_lo - 1);
     int bc0 = BIAS_NONE, bc1 = BIAS_NONE;   // bias classes of the current tile's halves
     if (cur.kt <= kt_hi) {
@@ -566,32 +594,23 @@ void attn_fwd_kernel(FwdParams p)
         const int j0 = cur.kt * BN;
         const bool compute = cur.my_cls != TILE_SKIP;
 
-        // ---- accumulators start from this tile's bias (scaled by sqrt(D)),
-        // which frees the bias registers for the next tile
+        // (after the last tile the current one is fetched again into the free
+        // buffer, which nothing reads, so that every iteration issues the same
+        // memory instructions)
+        asm volatile("" ::: "memory");
+        issue_tile(nxt.kt <= kt_hi ? nxt : cur, buf ^ 1);
+        asm volatile("" ::: "memory");
+        const char* kb = smem + K_OFF + buf * KBYTES;
+        const char* vb = smem + V_OFF + buf * VBYTES;
         f32x16 acc[2];
         if (compute) {
-            if (bc0 != BIAS_NONE) acc[0] = bias_init(bc0, j0, 0);
-            if (bc1 != BIAS_NONE) acc[1] = bias_init(bc1, j0 + 32, 1);
-        }
-        asm volatile("" ::: "memory");
-        if (nxt.kt <= kt_hi) issue_tile(nxt, buf ^ 1);
-        asm volatile("" ::: "memory");
-        const int nb0 = load_bias(nxt, 0);
-        const int nb1 = load_bias(nxt, 1);
-        asm volatile("" ::: "memory");
-
-        if (compute) {
-            const char* kb = smem + K_OFF + buf * KBYTES;
-            const char* vb = smem + V_OFF + buf * VBYTES;
             constexpr int KHALF = (32 / L::RPI) * L::KGP;   // +32 keys in the K buffer
             // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains
             {
                 const bf16x8 a0 = *(const bf16x8*)(kb + kbase_even);
                 const bf16x8 a1 = *(const bf16x8*)(kb + kbase_even + KHALF);
-                acc[0] = bc0 != BIAS_NONE ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], acc[0], 0, 0, 0)
-                                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
-                acc[1] = bc1 != BIAS_NONE ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], acc[1], 0, 0, 0)
-                                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
             }
 #pragma unroll
             for (int kk = 1; kk < NKK; ++kk) {
@@ -601,7 +620,16 @@ void attn_fwd_kernel(FwdParams p)
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
             }
+            // ---- + bias * sqrt(D); the bias registers then take the next tile's
+            if (bc0 != BIAS_NONE) bias_add(bc0, j0, 0, acc[0]);
+            if (bc1 != BIAS_NONE) bias_add(bc1, j0 + 32, 1, acc[1]);
+        }
+        asm volatile("" ::: "memory");
+        const int nb0 = load_bias(nxt, 0);   // bias classes of the next tile's halves
+        const int nb1 = load_bias(nxt, 1);
+        asm volatile("" ::: "memory");
 
+        if (compute) {
             // ---- mask.  Element (jj, e) of half s is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
             if (cur.my_cls == TILE_MASKED) {
                 const int* ca = (const int*)(smem + CA_OFF + buf * BN * 4);
@@ -689,9 +717,9 @@ void attn_fwd_kernel(FwdParams p)
             l += ls0 + ls1;
         }
 
-        // the next tile's DMA (this wave's part) and bias have landed; then
-        // every wave's DMA has
-        wait_all_and_barrier();
+        // this wave's part of the next tile's DMA has landed (the bias loads
+        // issued after it may still be in flight); then every wave's has
+        wait_dma_and_barrier(bias_loads(nb0) + bias_loads(nb1));
         bc0 = nb0;
         bc1 = nb1;
         buf ^= 1;
