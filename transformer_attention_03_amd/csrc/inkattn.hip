@@ -60,6 +60,7 @@ namespace {
 
 constexpr int BM = 32;   // query tokens per wave (MFMA N)
 constexpr int BN = 64;   // keys per K/V tile (two MFMA M-blocks of 32)
+constexpr int NWAVES = 8; // waves per attention workgroup (one workgroup per CU)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
@@ -981,8 +982,8 @@ struct Shape {
 Shape choose_shape(int G)
 {
     Shape s;
-    s.nw = 4;
-    s.hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    s.nw = NWAVES;
+    s.hpw = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     s.tpw = s.nw / s.hpw;
     return s;
 }
@@ -991,7 +992,7 @@ template <int D, bool PB>
 void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
 {
     (void)sh;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PB, 4>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PB, NWAVES>), grid, dim3(64 * NWAVES), 0, st, p);
 }
 
 }  // namespace
