@@ -64,8 +64,10 @@ constexpr int NWAVES = 8; // waves per attention workgroup (one workgroup per CU
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
-// s_waitcnt operand: vmcnt(0) lgkmcnt(0), expcnt not waited on
+// s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// vmcnt(0) lgkmcnt(0); lgkmcnt(0) alone
 constexpr int WAIT_VM_LGKM = 0x0070;
+constexpr int WAIT_LGKM = 0xC07F;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -245,6 +247,16 @@ __device__ __forceinline__ void wait_dma_and_barrier(int n_after)
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Waits until at most n (3 or 5) vector-memory instructions of the wave are outstanding.
+__device__ __forceinline__ void wait_vm_keep(int n)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (n == 3) __builtin_amdgcn_s_waitcnt(0x0F73);
+    else if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+}
+
 // Max / sum of a value and its twin in the other wave half (same query).
 __device__ __forceinline__ float half_max(float x)
 {
@@ -322,8 +334,14 @@ void attn_fwd_kernel(FwdParams p)
     constexpr int NVG = D / 8;               // 1 KB DMA groups per V^T tile (8 rows each)
     static_assert(NVG % NW == 0 && NW % 2 == 0, "V^T DMA groups must divide among an even number of waves");
     constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 2 * VBYTES;
+    // fp32 bias strips staged by DMA: per wave 32 rows x 64 distances (8 KB)
+    constexpr int BSTRIP = BM * BN * 4;
+    constexpr int B_OFF = CA_OFF + 2 * BN * 4;
+    constexpr int LDS_BYTES = B_OFF + (PROF_BF16 ? 0 : NW * BSTRIP);
+    // vector-memory instructions of one tile's K / V / start-column DMA (per wave)
+    constexpr int N_KV_DMA = NGRP / NW + NVG / NW + 1;
 
-    __shared__ __attribute__((aligned(1024))) char smem[CA_OFF + 2 * BN * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -483,11 +501,11 @@ void attn_fwd_kernel(FwdParams p)
 #pragma unroll
     for (int c = 0; c < 4; ++c) voff[c] = qi * 128 + 16 * ((2 * c + hh) ^ vt_swz(qi));
 
-    // ---- relative bias.  sacc[s][4*jj+e] is the profile entry of key
-    // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance R - 8 jj - 4 hh - (e ^ 3)
-    // with R = gi - (j0 + 32 s).  All loads go through a buffer resource over this
-    // (batch row, head)'s [Sq, E] block: one 32-bit lane offset, immediate
-    // offsets per entry, and reads outside the block return 0.
+    // ---- relative bias.  Element (jj, e) of half s of a tile's S^T
+    // accumulator is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance
+    // R - 8 jj - 4 hh - (e ^ 3) with R = gi - (j0 + 32 s).  All loads go through
+    // a buffer resource over this (batch row, head)'s [Sq, E] block, and reads
+    // outside the block return 0.
     constexpr int PE = PROF_BF16 ? 2 : 4;               // bytes per profile entry
     const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const char*)p.profiles + ((size_t)b * p.Hq + h) * p.Sq * p.E * PE), 0,
@@ -499,28 +517,38 @@ void attn_fwd_kernel(FwdParams p)
     // it is the exact offset of an entry (never a base to be completed by the
     // constant operand), and offsets before the block wrap out of range.
     const unsigned prow_off = ((unsigned)i * (unsigned)p.E + (unsigned)(gi - 4 * hh - 30)) * PE;
-    // sacc[s] first receives sub-tile s's raw profile entries, then (scaled by
-    // sqrt(D)) serves as the initial accumulator of S^T = K Q^T, so that
-    // head_dim^-0.5 * log2(e) * sacc = scale*log2e*q.k + log2e*bias.
-    f32x16 sacc[2];
     constexpr float INV_SCALE = D == 128 ? 11.313708498984761f : 8.0f;   // sqrt(D)
-    // fp32 sub-tiles whose distances all lie in [0, E): 4 runs of 4 entries,
-    // the run of jj starting at distance R - 8 jj - 4 hh - 3 (element e: + e)
-    // vo: byte offset of the lowest distance read (run of jj = 3), >= 0 on
-    // such sub-tiles
-    auto load_bias_fast = [&](unsigned vo, int s) {
+    constexpr int BIAS_DMA = 16;   // code bit: the tile's strip was copied row by row
+
+    // fp32 profiles: every bias value reaches the accumulators through this
+    // wave's 8 KB LDS strip, filled by DMA (buffer_load ... lds) one tile ahead.
+    // Layouts, by the tile's bias code:
+    //  - BIAS_DMA (both halves fast): 32 rows x 64 distances, copied row by
+    //    row: lane (row r, slot c) of instruction u, r = 4 u + lane / 16,
+    //    fetches 16-byte chunk c ^ (r % 16) of row r's strip (distances
+    //    R_r - 63 .. R_r), which makes the column-wise reads conflict free;
+    //  - otherwise half s uses bytes 4096 s .. + 4095: a fast half (every
+    //    distance in [0, E)) as 4 runs of 4 entries, run jj of lane l at
+    //    1024 jj + 16 l; an edge half entry by entry, entry 4 jj + e of lane l
+    //    at 256 (4 jj + e) + 4 l, zeroed outside [0, E) on reading.
+    // bf16 profiles: entries are gathered into the registers bias_reg[s]
+    // instead (bf16 tiles are edge halves, loaded entry by entry).
+    char* bstrip = smem + B_OFF + wave * BSTRIP;
+    const int brow = lane >> 4;   // row of the lane within a row-copy instruction (+ 4 u)
+    const unsigned bdma_lane = (unsigned)brow * (unsigned)(p.E + 1) * 4u;
+    f32x16 bias_reg[2];           // bf16 profiles only
+
+    // loads of a fast half: vo = exact offset of its lowest distance (run jj = 3)
+    auto fetch_fast_half = [&](unsigned vo, int s) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                prsrc, vo, (24 - 8 * jj) * PE, 0));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sacc[s][4 * jj + e] = w[e];
+            const int soff = (24 - 8 * jj) * PE;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bstrip + 4096 * s + 1024 * jj), 16, vo,
+                                                     soff, 0, 0);
         }
     };
-    // any sub-tile, entry by entry (raw fp32 bits, or the bf16 bits in the low
-    // half).  Distances outside [0, E) are zeroed when the accumulator is
-    // initialised, so that nothing waits for these loads before then.
-    auto load_bias_edge = [&](int js, int s) {
+    // loads of an edge half (keys js .. js + 31), entry by entry
+    auto fetch_edge_half = [&](int js, int s) {
         const unsigned vo = prow_off - (unsigned)js * PE;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -530,49 +558,119 @@ void attn_fwd_kernel(FwdParams p)
                 // must not merge into one wider load whose first entry may lie
                 // before the block (which would read the whole load as 0)
                 const unsigned off = opaque(vo + (30 - 8 * jj - (e ^ 3)) * PE);
-                unsigned u;
-                if (PROF_BF16) u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
-                else u = __builtin_amdgcn_raw_buffer_load_b32(prsrc, off, 0, 0);
-                sacc[s][4 * jj + e] = __uint_as_float(u);
+                if constexpr (PROF_BF16) {
+                    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
+                    bias_reg[s][4 * jj + e] = __uint_as_float((unsigned)u);
+                } else {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        prsrc, (lds_void*)(bstrip + 4096 * s + 256 * (4 * jj + e)), 4, off, 0, 0, 0);
+                }
             }
         }
     };
-    // Adds sub-tile s's bias (keys js .. js + 31) to its S^T accumulator: the
-    // profile entry times sqrt(D), nothing at distances outside [0, E).
-    auto bias_add = [&](int bc, int js, int s, f32x16& a) {
-        if (bc == BIAS_FAST && !PROF_BF16) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) a[t] = __builtin_fmaf(sacc[s][t], INV_SCALE, a[t]);
+    // Issues the bias loads of this wave's part of tile d; returns the tile's
+    // code: the classes of its two 32-key halves (bits 0-1, 2-3), plus BIAS_DMA.
+    auto load_bias = [&](const TileDesc& d) -> int {
+        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE | (BIAS_NONE << 2);
+        const int j0n = d.kt * BN;
+        const int c0 = bias_class(qlo, qhi, j0n, p.E);
+        const int c1 = bias_class(qlo, qhi, j0n + 32, p.E);
+        if constexpr (PROF_BF16) {
+            if (c0 != BIAS_NONE) fetch_edge_half(j0n, 0);
+            if (c1 != BIAS_NONE) fetch_edge_half(j0n + 32, 1);
+            return c0 | (c1 << 2);
         } else {
-            const int R = gi - js;
+            if (c0 == BIAS_NONE && c1 == BIAS_NONE) return 0;
+            __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // earlier reads of the strip are done
+            if (c0 == BIAS_FAST && c1 == BIAS_FAST) {
+                // row i0 + r, distance qlo + r - j0n - 63 + 4 c': the strip of row r
+                const unsigned tile_off = (unsigned)((i0 * p.E + qlo - j0n - 63) * 4);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const unsigned r = (unsigned)(R - 8 * jj - 4 * hh - (e ^ 3));
-                    const float raw = sacc[s][4 * jj + e];
-                    const float v = PROF_BF16 ? __uint_as_float(__float_as_uint(raw) << 16) : raw;
-                    a[4 * jj + e] = __builtin_fmaf(r < (unsigned)p.E ? v : 0.0f, INV_SCALE, a[4 * jj + e]);
+                for (int u = 0; u < 8; ++u) {
+                    const int r = 4 * u + brow;
+                    const unsigned voff = opaque(tile_off + (unsigned)(4 * u) * (unsigned)(p.E + 1) * 4u +
+                                                 bdma_lane + 16u * (unsigned)((lane & 15) ^ (r & 15)));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bstrip + 1024 * u), 16, voff, 0,
+                                                             0, 0);
                 }
+                return c0 | (c1 << 2) | BIAS_DMA;
+            }
+            const unsigned vo0 = opaque(prow_off + (3 - j0n) * PE);
+            const unsigned vo1 = opaque(prow_off + (3 - j0n - 32) * PE);
+            if (c0 == BIAS_FAST) fetch_fast_half(vo0, 0);
+            else if (c0 != BIAS_NONE) fetch_edge_half(j0n, 0);
+            if (c1 == BIAS_FAST) fetch_fast_half(vo1, 1);
+            else if (c1 != BIAS_NONE) fetch_edge_half(j0n + 32, 1);
+            return c0 | (c1 << 2);
         }
     };
-    // Load instructions load_bias issues for a class.
-    auto bias_loads = [&](int bc) -> int {
-        return bc == BIAS_NONE ? 0 : (bc == BIAS_FAST && !PROF_BF16) ? 4 : 16;
+    // Vector-memory instructions load_bias issued for a code.
+    auto bias_loads = [&](int code) -> int {
+        if (code & BIAS_DMA) return 8;
+        auto per_half = [](int c) { return c == BIAS_NONE ? 0 : (c == BIAS_FAST && !PROF_BF16) ? 4 : 16; };
+        return per_half(code & 3) + per_half((code >> 2) & 3);
     };
-    // Bias loads of sub-tile s of tile d into sacc[s]; returns the sub-tile's
-    // bias class (BIAS_NONE: nothing loaded, the accumulator starts at zero).
-    auto load_bias = [&](const TileDesc& d, int s) -> int {
-        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE;
-        const int js = d.kt * BN + 32 * s;
-        const int bc = bias_class(qlo, qhi, js, p.E);
-        // the fast path's base is formed before the branch, so that the fast
-        // path writes no register before its loads (a register the other
-        // path loads into would make it wait for those loads)
-        const unsigned vo_fast = opaque(prow_off + (3 - js) * PE);
-        if (bc == BIAS_FAST && !PROF_BF16) load_bias_fast(vo_fast, s);
-        else if (bc != BIAS_NONE) load_bias_edge(js, s);
-        return bc;
+    // a + the entry (jj, e) of the half starting at key js times sqrt(D), or a
+    // outside [0, E).
+    auto add_edge = [&](int js, int jj, int e, float raw, float a) -> float {
+        const unsigned r = (unsigned)(gi - js - 8 * jj - 4 * hh - (e ^ 3));
+        return __builtin_fmaf(r < (unsigned)p.E ? raw : 0.0f, INV_SCALE, a);
+    };
+    // Adds tile j0t's bias (code as load_bias returned it) to the accumulators.
+    // Its loads were issued before this wave's DMA of the next K / V tile,
+    // which may stay outstanding (N_KV_DMA instructions).
+    auto bias_add_tile = [&](int code, int j0t, f32x16* a) {
+        if constexpr (PROF_BF16) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (((code >> (2 * s2)) & 3) == BIAS_NONE) continue;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a[s2][4 * jj + e] = add_edge(
+                            j0t + 32 * s2, jj, e, __uint_as_float(__float_as_uint(bias_reg[s2][4 * jj + e]) << 16),
+                            a[s2][4 * jj + e]);
+            }
+        } else {
+            if ((code & 15) == 0) return;
+            wait_vm_keep(N_KV_DMA);
+            if (code & BIAS_DMA) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int k = 15 - 8 * s2 - 2 * jj - hh;   // distances R - 32 s - 8 jj - 4 hh - 3 ..
+                        const f32x4 w = *(const f32x4*)(bstrip + qi * 256 + 16 * (k ^ (qi & 15)));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+                    }
+                return;
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int c = (code >> (2 * s2)) & 3;
+                if (c == BIAS_FAST) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const f32x4 w = *(const f32x4*)(bstrip + 4096 * s2 + 1024 * jj + 16 * lane);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+                    }
+                } else if (c == BIAS_EDGE) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            a[s2][4 * jj + e] = add_edge(
+                                j0t + 32 * s2, jj, e,
+                                *(const float*)(bstrip + 4096 * s2 + 256 * (4 * jj + e) + 4 * lane),
+                                a[s2][4 * jj + e]);
+                }
+            }
+        }
     };
 
     // Software pipeline, per 64-key tile t: the DMA of the next live tile is
@@ -582,11 +680,10 @@ void attn_fwd_kernel(FwdParams p)
     // the end-of-tile barrier, which waits for the DMA alone; one softmax step
     // covers the 64 keys and O^T += V^T P^T follows.
     TileDesc cur = next_live(kt_lo - 1);
-    int bc0 = BIAS_NONE, bc1 = BIAS_NONE;   // bias classes of the current tile's halves
+    int bcode = 0;   // bias code of the current tile (load_bias)
     if (cur.kt <= kt_hi) {
         issue_tile(cur, 0);
-        bc0 = load_bias(cur, 0);
-        bc1 = load_bias(cur, 1);
+        bcode = load_bias(cur);
     }
     wait_all_and_barrier();
     int buf = 0;
@@ -621,13 +718,11 @@ void attn_fwd_kernel(FwdParams p)
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
             }
-            // ---- + bias * sqrt(D); the bias registers then take the next tile's
-            if (bc0 != BIAS_NONE) bias_add(bc0, j0, 0, acc[0]);
-            if (bc1 != BIAS_NONE) bias_add(bc1, j0 + 32, 1, acc[1]);
+            // ---- + bias * sqrt(D); the bias registers / strip then take the next tile's
+            bias_add_tile(bcode, j0, acc);
         }
         asm volatile("" ::: "memory");
-        const int nb0 = load_bias(nxt, 0);   // bias classes of the next tile's halves
-        const int nb1 = load_bias(nxt, 1);
+        const int ncode = load_bias(nxt);   // bias code of the next tile
         asm volatile("" ::: "memory");
 
         if (compute) {
@@ -720,9 +815,8 @@ void attn_fwd_kernel(FwdParams p)
 
         // this wave's part of the next tile's DMA has landed (the bias loads
         // issued after it may still be in flight); then every wave's has
-        wait_dma_and_barrier(bias_loads(nb0) + bias_loads(nb1));
-        bc0 = nb0;
-        bc1 = nb1;
+        wait_dma_and_barrier(bias_loads(ncode));
+        bcode = ncode;
         buf ^= 1;
         cur = nxt;
     }
