@@ -250,6 +250,19 @@ def test_full_size_sampled_rows_and_counts(name):
     assert np.array_equal(cnt, ref)
 
 
+def test_key_tiles_beyond_one_schedule_round():
+    """More than 512 key tiles: the workgroup's tile schedule is built in
+    several rounds; rows near the end read tiles of both."""
+    S = 33000
+    x = W.custom(B=1, S=S, Hq=8, Hkv=1, D=64, E=48, seed=127)
+    rows = W.sample_rows(1, S, 20, 127, must=((0, 0), (0, 32767), (0, 32768), (0, 32831), (0, S - 1)))
+    check_rows(x, rows, "two_schedule_rounds")
+    y = count_probe_inputs(x)
+    out, lse = run_hip(y)
+    cnt = counts_from_lse(lse)
+    assert np.array_equal(cnt[0, :, 0], np.arange(1, S + 1))
+
+
 @pytest.mark.parametrize("name", ["local", "packed", "causal_gqa"])
 def test_full_size_count_probe(name):
     """lse = ln(n_allowed) for every row and head at full size: the hot path's mask is exact."""

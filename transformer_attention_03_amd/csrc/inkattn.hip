@@ -273,7 +273,6 @@ __device__ __forceinline__ float half_sum(float x)
 struct TileDesc {
     int kt;        // tile index (> kt_hi: none)
     int my_cls;    // this wave's class
-    int masked;    // some wave of the workgroup masks this tile
 };
 
 // LDS layout of one staged K tile.  Each 16-byte DMA instruction writes
@@ -337,7 +336,11 @@ void attn_fwd_kernel(FwdParams p)
     // fp32 bias strips staged by DMA: per wave 32 rows x 64 distances (8 KB)
     constexpr int BSTRIP = BM * BN * 4;
     constexpr int B_OFF = CA_OFF + 2 * BN * 4;
-    constexpr int LDS_BYTES = B_OFF + (PROF_BF16 ? 0 : NW * BSTRIP);
+    // tile schedule: one entry per live key tile of a round of NSCHED tiles,
+    // plus a count per wave
+    constexpr int NSCHED = 64 * NW;
+    constexpr int SCHED_OFF = B_OFF + (PROF_BF16 ? 0 : NW * BSTRIP);
+    constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     // vector-memory instructions of one tile's K / V / start-column DMA (per wave)
     constexpr int N_KV_DMA = NGRP / NW + NVG / NW + 1;
 
@@ -410,29 +413,62 @@ void attn_fwd_kernel(FwdParams p)
     const int kt_lo = jhi >= 0 ? jlo / BN : 0;
     const int kt_hi = jhi >= 0 ? jhi / BN : -1;
 
-    // Next tile after `kt` that some wave of the workgroup needs.
-    auto next_live = [&](int kt) -> TileDesc {
-        TileDesc d;
-        for (++kt; kt <= kt_hi; ++kt) {
+    // ---- tile schedule.  A round classifies key tiles base .. base + NSCHED - 1
+    // (one per thread) against every query block of the workgroup and lists
+    // the live ones in LDS in order: entry = (kt - base) | the class of query
+    // block qb_first + x in bits 16 + 2 x .. 17 + 2 x.  Rounds are built by the
+    // whole workgroup between barriers.
+    int* sched = (int*)(smem + SCHED_OFF);
+    auto build_round = [&](int base) -> int {
+        const int kt = base + tid;
+        unsigned code = 0;
+        bool live = false;
+        if (kt <= kt_hi) {
             const int j0 = kt * BN;
             const int kcount = min(BN, p.Sk - j0);
             const TileSummary ks = p.ksum[(size_t)b * p.nKT + kt];
-            int any = 0, masked = 0, mine = TILE_SKIP;
             for (int x = qb_first; x <= qb_last; ++x) {
-                const TileSummary s = p.qsum[(size_t)b * p.nQB + x];
+                const TileSummary qs = p.qsum[(size_t)b * p.nQB + x];
                 const int xc = min(BM, p.Sq - x * BM);
                 const int xlo = p.qoff + x * BM;
-                const int c = classify_tile(s, xlo, xlo + xc - 1, xc, ks, j0, j0 + kcount - 1, kcount, p.window);
-                any |= c != TILE_SKIP;
-                masked |= c == TILE_MASKED;
-                if (x == qb) mine = c;
-            }
-            if (any) {
-                d.kt = kt; d.my_cls = mine; d.masked = masked;
-                return d;
+                const int c = classify_tile(qs, xlo, xlo + xc - 1, xc, ks, j0, j0 + kcount - 1, kcount, p.window);
+                code |= (unsigned)c << (16 + 2 * (x - qb_first));
+                live |= c != TILE_SKIP;
             }
         }
-        d.kt = kt_hi + 1; d.my_cls = TILE_SKIP; d.masked = 0;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(live);
+        const int before = __popcll(bal & ((1ull << lane) - 1ull));
+        wait_all_and_barrier();                 // the previous round's entries are read
+        if (lane == 0) sched[NSCHED + wave] = __popcll(bal);
+        wait_all_and_barrier();
+        int off = 0, total = 0;
+        for (int w = 0; w < NW; ++w) {
+            const int cw = sched[NSCHED + w];
+            off += w < wave ? cw : 0;
+            total += cw;
+        }
+        if (live) sched[off + before] = (int)(code | (unsigned)(kt - base));
+        wait_all_and_barrier();
+        return __builtin_amdgcn_readfirstlane(total);
+    };
+    int round_base = kt_lo, round_n = 0, round_i = 0;
+    // Next live tile (some wave of the workgroup needs it), in order; uniform.
+    auto next_live = [&]() -> TileDesc {
+        while (round_i >= round_n && round_base <= kt_hi) {
+            round_n = build_round(round_base);
+            round_base += NSCHED;
+            round_i = 0;
+        }
+        TileDesc d;
+        if (round_i < round_n) {
+            const unsigned w = (unsigned)__builtin_amdgcn_readfirstlane(sched[round_i]);
+            d.kt = round_base - NSCHED + (int)(w & 0xFFFFu);
+            d.my_cls = (int)((w >> (16 + 2 * (qb - qb_first))) & 3u);
+            ++round_i;
+        } else {
+            d.kt = kt_hi + 1;
+            d.my_cls = TILE_SKIP;
+        }
         return d;
     };
 
@@ -679,7 +715,7 @@ void attn_fwd_kernel(FwdParams p)
     // the bias loads of tile t + 1 go out, so that they stay in flight across
     // the end-of-tile barrier, which waits for the DMA alone; one softmax step
     // covers the 64 keys and O^T += V^T P^T follows.
-    TileDesc cur = next_live(kt_lo - 1);
+    TileDesc cur = next_live();
     int bcode = 0;   // bias code of the current tile (load_bias)
     if (cur.kt <= kt_hi) {
         issue_tile(cur, 0);
@@ -688,7 +724,7 @@ void attn_fwd_kernel(FwdParams p)
     wait_all_and_barrier();
     int buf = 0;
     while (cur.kt <= kt_hi) {
-        const TileDesc nxt = next_live(cur.kt);
+        const TileDesc nxt = next_live();
         const int j0 = cur.kt * BN;
         const bool compute = cur.my_cls != TILE_SKIP;
 
