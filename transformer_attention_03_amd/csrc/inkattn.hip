@@ -217,6 +217,16 @@ __device__ __forceinline__ unsigned opaque(unsigned x)
     return x;
 }
 
+// An empty use of a value in registers: its computation must happen before
+// this point (the device pass only; the host pass never generates kernel code).
+template <typename T>
+__device__ __forceinline__ void pin(const T& x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" ::"v"(x));
+#endif
+}
+
 // Wait for every outstanding memory operation of the wave, then meet the
 // workgroup.  The wait is the builtin so that the compiler's own wait counting
 // knows of it; the barrier is an asm statement with a memory clobber so that
@@ -332,7 +342,10 @@ void attn_fwd_kernel(FwdParams p)
     constexpr int VBYTES = D * 128;          // one V^T tile: D rows of 64 fp16
     constexpr int NVG = D / 8;               // 1 KB DMA groups per V^T tile (8 rows each)
     static_assert(NVG % NW == 0 && NW % 2 == 0, "V^T DMA groups must divide among an even number of waves");
-    constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 2 * VBYTES;
+    // K and the start columns double-buffered; V triple-buffered (the PV
+    // product of a tile runs during the next tile, while the tile after that
+    // is being fetched)
+    constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 3 * VBYTES;
     // fp32 bias strips staged by DMA: per wave 32 rows x 64 distances (8 KB)
     constexpr int BSTRIP = BM * BN * 4;
     constexpr int B_OFF = CA_OFF + 2 * BN * 4;
@@ -491,7 +504,7 @@ void attn_fwd_kernel(FwdParams p)
     // key start columns of this batch row, padded to whole tiles with INT_MIN
     const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.kanchor + (size_t)b * p.nKT * BN), 0, (unsigned)p.nKT * BN * 4u, 0x00020000);
-    auto issue_tile = [&](const TileDesc& d, int bufsel) {
+    auto issue_tile = [&](const TileDesc& d, int bufsel, int vsel) {
         const int j0 = d.kt * BN;
 #pragma unroll
         for (int u = 0; u < GPW; ++u) {
@@ -508,7 +521,7 @@ void attn_fwd_kernel(FwdParams p)
             const int a = wave + NW * u;
             const int soff = d.kt * VBYTES + a * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                vrsrc, (lds_void*)(smem + V_OFF + bufsel * VBYTES + a * 1024), 16, vvoff, soff, 0, 0);
+                vrsrc, (lds_void*)(smem + V_OFF + vsel * VBYTES + a * 1024), 16, vvoff, soff, 0, 0);
         }
         // the tile's 64 key start columns, one dword per lane; every wave
         // writes the same values, so that each wave's sequence of memory
@@ -711,150 +724,186 @@ void attn_fwd_kernel(FwdParams p)
 
     // Software pipeline, per 64-key tile t: the DMA of the next live tile is
     // issued first; S^T = K Q^T of both 32-key halves runs as two interleaved
-    // MFMA chains; then tile t's bias (loaded during tile t - 1) is added and
-    // the bias loads of tile t + 1 go out, so that they stay in flight across
-    // the end-of-tile barrier, which waits for the DMA alone; one softmax step
-    // covers the 64 keys and O^T += V^T P^T follows.
+    // MFMA chains; tile t's bias (loaded during tile t - 1) is added and the
+    // bias loads of tile t + 1 go out, staying in flight across the
+    // end-of-tile barrier, which waits for the DMA alone.  Then the PV product
+    // of tile t - 1 runs on the matrix cores while the softmax of tile t runs
+    // on the vector units: one softmax step covers the 64 keys.
     TileDesc cur = next_live();
     int bcode = 0;   // bias code of the current tile (load_bias)
+    {
+        // V buffer 2 stands for the tile before the first: zeros
+        f32x4* z = (f32x4*)(smem + V_OFF + 2 * VBYTES);
+        for (int t = tid; t < VBYTES / 16; t += 64 * NW) z[t] = f32x4{};
+    }
     if (cur.kt <= kt_hi) {
-        issue_tile(cur, 0);
+        issue_tile(cur, 0, 0);
         bcode = load_bias(cur);
     }
     wait_all_and_barrier();
-    int buf = 0;
+    int kbuf = 0, vbuf = 0, vprev = 2;
+    f16x8 pbp[4];   // P^T of the previous tile (zero when this wave did not compute it)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pbp[c] = f16x8{};
+    constexpr int KHALF = (32 / L::RPI) * L::KGP;   // +32 keys in the K buffer
     while (cur.kt <= kt_hi) {
         const TileDesc nxt = next_live();
         const int j0 = cur.kt * BN;
-        const bool compute = cur.my_cls != TILE_SKIP;
+        const int vnext = vbuf == 2 ? 0 : vbuf + 1;
 
         // (after the last tile the current one is fetched again into the free
-        // buffer, which nothing reads, so that every iteration issues the same
+        // buffers, which nothing reads, so that every iteration issues the same
         // memory instructions)
         asm volatile("" ::: "memory");
-        issue_tile(nxt.kt <= kt_hi ? nxt : cur, buf ^ 1);
+        issue_tile(nxt.kt <= kt_hi ? nxt : cur, kbuf ^ 1, vnext);
         asm volatile("" ::: "memory");
-        const char* kb = smem + K_OFF + buf * KBYTES;
-        const char* vb = smem + V_OFF + buf * VBYTES;
+        const char* kb = smem + K_OFF + kbuf * KBYTES;
+        const char* vbp = smem + V_OFF + vprev * VBYTES;
+
+        // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains
         f32x16 acc[2];
-        if (compute) {
-            constexpr int KHALF = (32 / L::RPI) * L::KGP;   // +32 keys in the K buffer
-            // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains
-            {
-                const bf16x8 a0 = *(const bf16x8*)(kb + kbase_even);
-                const bf16x8 a1 = *(const bf16x8*)(kb + kbase_even + KHALF);
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
-            }
-#pragma unroll
-            for (int kk = 1; kk < NKK; ++kk) {
-                const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk;
-                const bf16x8 a0 = *(const bf16x8*)(kb + ko);
-                const bf16x8 a1 = *(const bf16x8*)(kb + ko + KHALF);
-                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
-            }
-            // ---- + bias * sqrt(D); the bias registers / strip then take the next tile's
-            bias_add_tile(bcode, j0, acc);
+        {
+            const bf16x8 a0 = *(const bf16x8*)(kb + kbase_even);
+            const bf16x8 a1 = *(const bf16x8*)(kb + kbase_even + KHALF);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
         }
+#pragma unroll
+        for (int kk = 1; kk < NKK; ++kk) {
+            const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk;
+            const bf16x8 a0 = *(const bf16x8*)(kb + ko);
+            const bf16x8 a1 = *(const bf16x8*)(kb + ko + KHALF);
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
+        }
+        // ---- + bias * sqrt(D) (nothing on tiles this wave skips); the bias
+        // registers / strip then take the next tile's
+        bias_add_tile(bcode, j0, acc);
         asm volatile("" ::: "memory");
         const int ncode = load_bias(nxt);   // bias code of the next tile
         asm volatile("" ::: "memory");
 
-        if (compute) {
-            // ---- mask.  Element (jj, e) of half s is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
-            if (cur.my_cls == TILE_MASKED) {
-                const int* ca = (const int*)(smem + CA_OFF + buf * BN * 4);
+        // ---- mask (every key of a tile this wave skips is masked: no allowed
+        // pair).  Element (jj, e) of half s is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
+        if (cur.my_cls != TILE_FULL) {
+            const int* ca = (const int*)(smem + CA_OFF + kbuf * BN * 4);
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int kl = 32 * s2 + 8 * jj + 4 * hh;
-                        const i32x4 c4 = *(const i32x4*)(ca + kl);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int kl = 32 * s2 + 8 * jj + 4 * hh;
+                    const i32x4 c4 = *(const i32x4*)(ca + kl);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (!key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
-                                acc[s2][4 * jj + e] = -INFINITY;
-                    }
-            }
-
-            // ---- online softmax over the 64 keys (sink-initialised, lazily rescaled), log2 units
-            float mx = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                mx = fmaxf(mx, acc[0][t]);
-                mx = fmaxf(mx, acc[1][t]);
-            }
-            mx = half_max(mx * p.c_log2);
-            const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
-            const float m_new = move ? mx : m;
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            if (__builtin_amdgcn_ballot_w64(move) != 0) {
-                const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
-                l *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-            }
-            m = m_new;
-
-            // ---- P^T and O^T += V^T P^T, one 16-key step c at a time: the
-            // weights of step c + 1 are computed while step c's MFMAs run.
-            // pb[c] holds keys 16 c + ... in the order of V^T's staged rows.
-            f16x8 pb[4];
-            float ls0 = 0.0f, ls1 = 0.0f;
-            auto make_p = [&](int c) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    pb[c][t] = (_Float16)__builtin_amdgcn_exp2f(
-                        __builtin_fmaf(acc[c >> 1][8 * (c & 1) + t], p.c_log2, -m_use));
-                // the denominator sums the fp16-rounded weights the PV product uses
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    const half2_t w2 = half2_t{pb[c][2 * q2], pb[c][2 * q2 + 1]};
-                    if (q2 & 1) ls1 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
-                    else ls0 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
+                    for (int e = 0; e < 4; ++e)
+                        if (!key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
+                            acc[s2][4 * jj + e] = -INFINITY;
                 }
-            };
-            // V^T operands of step c + 1 are read while step c's MFMAs run
-            f16x8 avn[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vb + voff[0] + db * 32 * 128);
-            make_p(0);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                f16x8 av[NDB];
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) av[db] = avn[db];
-                if (c < 3) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        avn[db] = *(const f16x8*)(vb + voff[c + 1] + db * 32 * 128);
-                    make_p(c + 1);
-                }
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pb[c], oacc[db], 0, 0, 0);
-                if (c < 3) {
-                    // the next step's reads first, then one MFMA per share of its VALU work
-                    __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-                    }
-                }
-            }
-            l += ls0 + ls1;
         }
+
+        // ---- step 0 of the previous tile's O^T += V^T P^T, with this tile's
+        // row max (log2 units) on the vector units meanwhile
+        {
+            f16x8 av[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) av[db] = *(const f16x8*)(vbp + voff[0] + db * 32 * 128);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pbp[0], oacc[db], 0, 0, 0);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            mx = fmaxf(mx, acc[0][t]);
+            mx = fmaxf(mx, acc[1][t]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+        }
+        mx = half_max(mx * p.c_log2);
+        const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
+        const float m_new = move ? mx : m;
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            // into the new frame: the output so far (with step 0 of the previous
+            // tile) and the previous tile's weights still to be multiplied
+            const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+#pragma unroll
+            for (int c = 1; c < 4; ++c)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) pbp[c][t] = (_Float16)((float)pbp[c][t] * alpha);
+        }
+        m = m_new;
+
+        // ---- steps 1..3 of the previous tile's product, with this tile's
+        // weights P^T on the vector units meanwhile.  pb[c] holds keys 16 c + ...
+        // in the order of V^T's staged rows.
+        f16x8 pb[4];
+        float ls0 = 0.0f, ls1 = 0.0f;
+        auto make_p = [&](int c) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                pb[c][t] = (_Float16)__builtin_amdgcn_exp2f(
+                    __builtin_fmaf(acc[c >> 1][8 * (c & 1) + t], p.c_log2, -m_use));
+            // the denominator sums the fp16-rounded weights the PV product uses
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                const half2_t w2 = half2_t{pb[c][2 * q2], pb[c][2 * q2 + 1]};
+                if (q2 & 1) ls1 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls1, false);
+                else ls0 = __builtin_amdgcn_fdot2(w2, half2_t{(_Float16)1.0f, (_Float16)1.0f}, ls0, false);
+            }
+        };
+#pragma unroll
+        for (int c = 1; c < 4; ++c) {
+            f16x8 av[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) av[db] = *(const f16x8*)(vbp + voff[c] + db * 32 * 128);
+            if (c == 1) make_p(0);
+            make_p(c);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pbp[c], oacc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if (c == 1) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);   // VALU
+                else __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+        }
+        // (the weights are pinned here, so that the compiler does not sink
+        // their computation below the MFMAs it is meant to overlap)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pin(pb[c]);
+        l += ls0 + ls1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pbp[c] = pb[c];
 
         // this wave's part of the next tile's DMA has landed (the bias loads
         // issued after it may still be in flight); then every wave's has
         wait_dma_and_barrier(bias_loads(ncode));
         bcode = ncode;
-        buf ^= 1;
+        kbuf ^= 1;
+        vprev = vbuf;
+        vbuf = vnext;
         cur = nxt;
+    }
+    // ---- the last tile's O^T += V^T P^T
+    {
+        const char* vbp = smem + V_OFF + vprev * VBYTES;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    *(const f16x8*)(vbp + voff[c] + db * 32 * 128), pbp[c], oacc[db], 0, 0, 0);
     }
 
     // ---- epilogue
