@@ -85,6 +85,41 @@ def algorithmic_work(x):
     return cnt, pairs, flops, nbytes
 
 
+def flex_allowed_counts(x) -> np.ndarray:
+    """Allowed keys per query row of a generic flex workload (closed form): the row
+    sees the keys from the start of its block (after the last EOS before it, or a
+    fixed-block start) up to itself, within the window."""
+    w = x["workload"]
+    S = w.S
+    cnt = np.zeros((w.B, S), dtype=np.int64)
+    for b in range(w.B):
+        ends = set(x["doc_ends"][b]) if x["tokens"] is not None else set()
+        start = 0
+        for i in range(S):
+            st = start
+            if x["fixed_block_size"]:
+                st = max(st, (i // x["fixed_block_size"]) * x["fixed_block_size"])
+            if x["sliding_window"]:
+                st = max(st, i - x["sliding_window"] + 1)
+            cnt[b, i] = i - st + 1
+            if i in ends:
+                start = i + 1
+    return cnt
+
+
+def flex_algorithmic_work(x):
+    w = x["workload"]
+    cnt = flex_allowed_counts(x)
+    pairs = int(cnt.sum()) * w.Hq
+    flops = 4.0 * w.D * pairs
+    nbytes = (w.B * w.S * w.Hq * w.D * 2            # q
+              + 2 * w.B * w.S * w.Hkv * w.D * 2     # k, v
+              + w.B * w.S * w.Hq * w.D * 2          # out (bf16)
+              + w.B * w.S * w.Hq * 4                # lse
+              + w.B * w.S * 4 + w.Hq * 4)           # tokens, sink weights
+    return cnt, pairs, flops, nbytes
+
+
 def traffic_from_profiles(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
     path = os.path.join(ROOT, "profiles", f"traffic_attn_fwd_kernel_{workload}.json")
@@ -156,8 +191,10 @@ def main():
     from transformer_attention_03_amd import binding
     from transformer_attention_03_amd import workloads as W
 
+    if args.workload in W.FLEX_WORKLOADS:
+        return bench_flex(args)
     if args.workload not in W.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(W.WORKLOADS)}")
+        sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(W.WORKLOADS) + sorted(W.FLEX_WORKLOADS)}")
     w = W.WORKLOADS[args.workload]
     x = W.generate(w)
     cnt, pairs, flops, nbytes = algorithmic_work(x)
@@ -238,6 +275,111 @@ def main():
                                  "frac": gbs / HBM_PEAK_GBS})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def flex_cpu_baseline(x, target_s: float, seed: int = 11):
+    """The generic flex oracle as it stands, on a bounded random sample of rows."""
+    import torch
+    import oracle
+    from transformer_attention_03_amd import workloads as W
+    w = x["workload"]
+    total = w.B * w.S
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        oracle.flex_fwd(x["q"], x["k"], x["v"], x["sink_weights"], x["tokens"], x["eos_id"],
+                        x["fixed_block_size"], x["sliding_window"], x["scale"], rows=rows)
+        return time.perf_counter() - t0
+
+    n = min(64, total)
+    while True:
+        t = timed(W.sample_rows(w.B, w.S, n, seed))
+        if t >= target_s / 8 or n >= total:
+            break
+        n = min(total, n * 4)
+    if n < total and t < 0.75 * target_s:
+        n = int(min(total, max(n, n * target_s / max(t, 1e-9))))
+    rows = torch.arange(total) if n >= total else W.sample_rows(w.B, w.S, n, seed + 1)
+    t = timed(rows)
+    cnt = flex_allowed_counts(x).reshape(-1)
+    pairs = int(cnt[rows.numpy()].sum()) * w.Hq
+    return {"value": 4.0 * w.D * pairs / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{rows.numel()} {'(all)' if n >= total else 'random'} query rows of {total} "
+                      f"(all {w.Hq} heads), {pairs} unmasked pairs, {t:.1f} s wall, fp64"}
+
+
+def bench_flex(args):
+    """The generic flex-attention forward (no relative term): one step = one
+    flex_attn_fwd call (positions, pre-pass, value copy and attention kernel)."""
+    import torch
+    from transformer_attention_03_amd import binding
+    from transformer_attention_03_amd import workloads as W
+
+    w = W.FLEX_WORKLOADS[args.workload]
+    x = W.generate_flex(w)
+    cnt, pairs, flops, nbytes = flex_algorithmic_work(x)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = x["q"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    sw = None if x["sink_weights"] is None else x["sink_weights"].to(dev)
+    tok = None if x["tokens"] is None else x["tokens"].to(dev)
+    out = torch.empty((w.B, w.Hq, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, binding.flex_attn_workspace_size(w.B, w.S, w.S, w.Hkv, w.D)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.flex_attn_fwd(q, k, v, sw, tok, x["eos_id"], x["fixed_block_size"], x["sliding_window"],
+                              x["scale"], out=out, lse=lse, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    if not torch.isfinite(out.float()).all():
+        sys.exit("non-finite output")
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fwd attention TFLOP/s (unmasked pairs) + % MFMA peak, 1 GPU; tokens/s",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: generic flex forward, B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"D={w.D} mask={w.mask} docs U{{{w.doc_min}..{w.doc_max}}} per-head sinks, "
+                               f"bf16 output",
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
+                   "qk_mfma": "bf16", "pv_mfma": "fp16", "accumulate": "fp32"},
+        "tokens_per_s": w.B * w.S / (ms_step * 1e-3),
+        "mfma_frac_step": flops / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+        "unmasked_pairs": pairs,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": traffic_from_profiles(w.name),
+                     "kernel": "flex_attn_fwd call (positions, pre-pass, value copy, attn_fwd_kernel)",
+                     "kernel_ms": call_ms, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = flex_cpu_baseline(x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -182,6 +182,47 @@ int attn_debug_tiles(const uint8_t* valid, const uint8_t* key_valid,
                      uint8_t* tile_class, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * flex_attn_workspace_size / flex_attn_fwd -- the generic flex-attention
+ * forward without the relative term: FlexAttention.forward on the page
+ * "nemo_automodel.components.attention.flex_attention" (section API: forward's
+ * q / k / v layouts, scale, sink_weights, sliding_window and enable_gqa;
+ * attn_mask_type "causal" / "block_causal" and fixed_block_size of the class;
+ * the block-causal and fixed-block mask mods).  For query i and key j of batch
+ * row b, query head h, K/V head g = h / (Hq/Hkv):
+ *
+ *   key j is allowed  <=>  j <= i
+ *                          and (tokens == NULL or i and j lie in the same
+ *                               EOS-delimited block: a block ends with a token
+ *                               equal to eos_id, which belongs to it)
+ *                          and (fixed_block_size <= 0 or
+ *                               i / fixed_block_size == j / fixed_block_size)
+ *                          and (sliding_window <= 0 or i - j < sliding_window)
+ *   z_j = scale * <q[b,h,i,:], k[b,g,j,:]>, where scale is the given one
+ *         (> 0) only when sink_weights is NULL, head_dim^-0.5 otherwise
+ *   s   = sink_weights[h] (a per-head logit in the denominator with a zero
+ *         value), or no sink when sink_weights is NULL
+ *   out[b,h,i,:] = sum_j e^{z_j} v[b,g,j,:] / (e^s + sum_j e^{z_j})   rounded to bf16
+ *   lse[b,h,i]   = ln(e^s + sum_j e^{z_j})   (natural log; -inf for an empty row
+ *                  without sink)
+ *
+ *   q    [B, Hq, Sq, D]  bf16, 16-byte aligned (head-major, as on the page)
+ *   k, v [B, Hkv, Sk, D] bf16, 16-byte aligned
+ *   sink_weights [Hq] fp32 or NULL
+ *   tokens [B, Sq] int32 or NULL (NULL: "causal"; else "block_causal" by eos_id)
+ *   out  [B, Hq, Sq, D]  bf16 (the dtype of q), 16-byte aligned, written
+ *   lse  [B, Hq, Sq]     fp32, written when not NULL
+ *   Block masks (tokens or fixed_block_size > 0) need Sq == Sk.  Queries are
+ *   aligned with the first keys (query i is key column i).  The workspace
+ *   holds the per-token positions and validity this entry derives, then the
+ *   same pre-pass and value copy as attn_fwd.  Errors as for attn_fwd.
+ */
+size_t flex_attn_workspace_size(int B, int Sq, int Sk, int Hkv, int D);
+int flex_attn_fwd(const void* q, const void* k, const void* v, const float* sink_weights,
+                  const int32_t* tokens, int32_t eos_id, int64_t fixed_block_size, int64_t sliding_window,
+                  float scale, int B, int Sq, int Sk, int Hq, int Hkv, int D, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attn_status_string(int status);
 

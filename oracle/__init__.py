@@ -62,6 +62,11 @@ def _load():
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 ctypes.c_int, ctypes.c_int,
                 P, ctypes.c_int64, P, P, P, ctypes.c_int]
+            lib.flex_oracle_fwd.restype = ctypes.c_int
+            lib.flex_oracle_fwd.argtypes = [
+                P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                P, ctypes.c_int64, P, P, P, ctypes.c_int]
             lib.attn_oracle_max_threads.restype = ctypes.c_int
             lib.attn_oracle_mask.restype = ctypes.c_int
             lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
@@ -189,6 +194,47 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
         raise RuntimeError(f"attn_oracle_fwd failed ({rc})")
     if rows is None:
         return out.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq), cnt.reshape(B, Sq)
+    return out, lse, cnt
+
+
+def flex_fwd(q, k, v, sink_weights=None, tokens=None, eos_id: int = 0, fixed_block_size=None,
+             sliding_window: int = 0, scale=None, rows=None, n_threads: int = 0):
+    """fp64 generic flex-attention forward (no relative term), head-major layouts.
+
+    ``q [B,Hq,Sq,D]``, ``k``/``v [B,Hkv,Sk,D]`` bf16; ``sink_weights [Hq]`` or None;
+    ``tokens [B,Sq]`` or None.  Returns ``(out [B,Hq,Sq,D], lse [B,Hq,Sq], n_allowed [B,Sq])``,
+    or with ``rows`` (flattened ``b*Sq + i``) the compact ``out [n,Hq,D]``, ``lse [n,Hq]``,
+    ``n_allowed [n]``.
+    """
+    B, Hq, Sq, D = (int(x) for x in q.shape)
+    Hkv, Sk = int(k.shape[1]), int(k.shape[2])
+    qn = _as_np(q, np.uint16)
+    kn = _as_np(k, np.uint16)
+    vn = _as_np(v, np.uint16)
+    sn = None if sink_weights is None else _as_np(sink_weights, np.float32)
+    tn = None if tokens is None else _as_np(tokens, np.int32)
+    for name, a, shape in (("q", qn, (B, Hq, Sq, D)), ("k", kn, (B, Hkv, Sk, D)), ("v", vn, (B, Hkv, Sk, D)),
+                           ("sink_weights", sn, (Hq,)), ("tokens", tn, (B, Sq))):
+        if a is not None and tuple(a.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(a.shape)} != {shape}")
+    if rows is None:
+        rows_n, n = None, B * Sq
+    else:
+        rows_n = _as_np(rows, np.int64).reshape(-1)
+        n = int(rows_n.shape[0])
+    out = np.empty((n, Hq, D), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    cnt = np.empty((n,), dtype=np.int32)
+    rc = _load().flex_oracle_fwd(
+        _ptr(qn), _ptr(kn), _ptr(vn), None if sn is None else _ptr(sn), None if tn is None else _ptr(tn),
+        int(eos_id), int(fixed_block_size or 0), int(sliding_window or 0),
+        float(scale) if scale is not None else 0.0, B, Sq, Sk, Hq, Hkv, D,
+        None if rows_n is None else _ptr(rows_n), n, _ptr(out), _ptr(lse), _ptr(cnt), int(n_threads))
+    if rc != 0:
+        raise RuntimeError(f"flex_oracle_fwd failed ({rc})")
+    if rows is None:
+        return (out.reshape(B, Sq, Hq, D).transpose(0, 2, 1, 3).copy(), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy(),
+                cnt.reshape(B, Sq))
     return out, lse, cnt
 
 

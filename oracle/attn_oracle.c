@@ -191,6 +191,116 @@ int attn_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return failed ? -1 : 0;
 }
 
+/*
+ * Generic flex-attention forward without the relative term (page
+ * "nemo_automodel.components.attention.flex_attention": FlexAttention and its
+ * forward).  Layouts are head-major as on that page: q [B,Hq,Sq,D], k / v
+ * [B,Hkv,Sk,D] (bf16 bit patterns), sink_weights [Hq] (or NULL), tokens
+ * [B,Sq] (or NULL).  Readings (stated in the repository's design notes):
+ *  - "causal": key j visible from query i iff j <= i;
+ *  - "block_causal": additionally i and j in the same block, where a block
+ *    ends with (and includes) a token equal to eos_id: block(t) = number of
+ *    eos tokens strictly before t;
+ *  - fixed_block_size F > 0: additionally i / F == j / F;
+ *  - sliding_window W > 0: additionally i - j < W (W tokens including i);
+ *  - the given scale (> 0) applies only when there are no sink weights;
+ *    otherwise the scale is head_dim^-0.5;
+ *  - sink_weights[h]: one more logit in the softmax denominator, zero value.
+ * Outputs for the listed rows (flattened b*Sq + i, all when rows == NULL):
+ * out[n_rows, Hq, D], lse[n_rows, Hq] (-inf for an empty row without sink),
+ * n_allowed[n_rows].
+ */
+static int64_t eos_block(const int32_t* tokens, int32_t eos_id, int Sq, int b, int t)
+{
+    int64_t n = 0;
+    for (int u = 0; u < t; ++u)
+        if (tokens[(size_t)b * Sq + u] == eos_id) ++n;
+    return n;
+}
+
+int flex_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const float* sink_weights, const int32_t* tokens, int32_t eos_id,
+                    int64_t fixed_block_size, int64_t window, double scale_arg,
+                    int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                    const int64_t* rows, int64_t n_rows,
+                    double* out, double* lse, int32_t* n_allowed, int n_threads)
+{
+    if (!q || !k || !v || !out || !lse || !n_allowed) return -1;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return -1;
+    if ((tokens || fixed_block_size > 0) && Sq != Sk) return -1;
+    if (!rows && n_rows != (int64_t)B * Sq) return -1;
+    const int G = Hq / Hkv;
+    const double scale = (!sink_weights && scale_arg > 0.0) ? scale_arg : 1.0 / sqrt((double)D);
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        uint8_t* ok = (uint8_t*)malloc((size_t)(Sk > 0 ? Sk : 1));
+        if (!z || !ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_rows; ++t) {
+            if (!z || !ok) continue;
+            int64_t row = rows ? rows[t] : t;
+            int b = (int)(row / Sq), i = (int)(row % Sq);
+            int64_t blk_i = tokens ? eos_block(tokens, eos_id, Sq, b, i) : 0;
+            int count = 0;
+            for (int j = 0; j < Sk; ++j) {
+                int visible = j <= i;
+                if (visible && tokens) visible = eos_block(tokens, eos_id, Sq, b, j) == blk_i;
+                if (visible && fixed_block_size > 0) visible = (i / fixed_block_size) == (j / fixed_block_size);
+                if (visible && window > 0) visible = (int64_t)i - j < window;
+                ok[j] = (uint8_t)visible;
+                count += visible;
+            }
+            n_allowed[t] = count;
+            for (int h = 0; h < Hq; ++h) {
+                int g = h / G;
+                double sigma = sink_weights ? (double)sink_weights[h] : -INFINITY;
+                double* o = out + ((size_t)t * Hq + h) * D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                if (count == 0) {
+                    lse[(size_t)t * Hq + h] = sigma;
+                    continue;
+                }
+                const uint16_t* qrow = q + (((size_t)b * Hq + h) * Sq + i) * D;
+                double M = sigma;
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    const uint16_t* krow = k + (((size_t)b * Hkv + g) * Sk + j) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+                    z[j] = scale * dot;
+                    if (z[j] > M) M = z[j];
+                }
+                double L = sink_weights ? exp(sigma - M) : 0.0;
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    double p = exp(z[j] - M);
+                    L += p;
+                    const uint16_t* vrow = v + (((size_t)b * Hkv + g) * Sk + j) * D;
+                    for (int d = 0; d < D; ++d) o[d] += p * bf16_to_double(vrow[d]);
+                }
+                for (int d = 0; d < D; ++d) o[d] /= L;
+                lse[(size_t)t * Hq + h] = M + log(L);
+            }
+        }
+        free(z);
+        free(ok);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Threads the OpenMP runtime will use for a parallel region (reported by callers). */
 int attn_oracle_max_threads(void)
 {

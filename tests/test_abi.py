@@ -24,7 +24,7 @@ P = ctypes.c_void_p
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:flex_)?attn_[a-z_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -103,3 +103,33 @@ def test_product_path_does_not_reach_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "attn_oracle" not in text, f
+
+
+def flex_call(**over):
+    a = dict(q=A, k=A, v=A, sink=None, tokens=None, eos=0, fixed=0, window=0, scale=0.0,
+             B=1, Sq=64, Sk=64, Hq=4, Hkv=2, D=128, out=A, lse=None, ws=A, wsb=1 << 20, stream=None)
+    a.update(over)
+    lib = binding.load()
+    return lib.flex_attn_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["sink"]), P(a["tokens"]), a["eos"],
+                             a["fixed"], a["window"], a["scale"], a["B"], a["Sq"], a["Sk"], a["Hq"],
+                             a["Hkv"], a["D"], P(a["out"]), P(a["lse"]), P(a["ws"]), a["wsb"],
+                             P(a["stream"]))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=3, Hkv=2), 2), (dict(D=96), 3), (dict(q=None), 1), (dict(out=None), 1), (dict(k=None), 1),
+    (dict(q=A + 8), 4), (dict(out=A + 4), 4), (dict(sink=A + 2), 4), (dict(tokens=A, Sk=65), 2),
+    (dict(fixed=16, Sk=65), 2), (dict(ws=None), 5), (dict(wsb=100), 5), (dict(B=-1), 2),
+])
+def test_flex_host_validation(over, status):
+    assert flex_call(**over) == status
+    assert binding.attn_last_error() != ""
+
+
+def test_flex_workspace_size():
+    # the attention workspace, then positions (4 B per query) and validity (1 B per token), each rounded to 256 B
+    assert binding.flex_attn_workspace_size(1, 64, 64, 2, 128) == (binding.attn_fwd_workspace_size(1, 64, 64, 2, 128)
+                                                                   + 256 + 256)
+    assert binding.flex_attn_workspace_size(2, 100, 300, 1, 64) == (binding.attn_fwd_workspace_size(2, 100, 300, 1, 64)
+                                                                     + 1024 + 768)
+    assert binding.flex_attn_workspace_size(0, 64, 64, 2, 128) == 0

@@ -24,7 +24,7 @@ STATUS = {0: "INKATTN_OK", 1: "INKATTN_ERR_NULL", 2: "INKATTN_ERR_SHAPE", 3: "IN
 
 # Every symbol include/inkattn.h declares.
 EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
-           "attn_debug_counts", "attn_debug_tiles",
+           "attn_debug_counts", "attn_debug_tiles", "flex_attn_workspace_size", "flex_attn_fwd",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
 _lock = threading.Lock()
@@ -61,6 +61,11 @@ def load() -> ctypes.CDLL:
             lib.attn_debug_counts.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P]
             lib.attn_debug_tiles.restype = I
             lib.attn_debug_tiles.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P, SZ, P]
+            lib.flex_attn_workspace_size.restype = SZ
+            lib.flex_attn_workspace_size.argtypes = [I, I, I, I, I]
+            lib.flex_attn_fwd.restype = I
+            lib.flex_attn_fwd.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, ctypes.c_float,
+                                          I, I, I, I, I, I, P, P, P, SZ, P]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [I]
             lib.attn_last_error.restype = ctypes.c_char_p
@@ -315,3 +320,51 @@ class LearnedRelativeAttention:
                         self.window, query_offset, stream=stream)
 
     __call__ = forward
+
+
+def flex_attn_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
+    return int(load().flex_attn_workspace_size(B, Sq, Sk, Hkv, D))
+
+
+def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  sink_weights: Optional[torch.Tensor] = None, tokens: Optional[torch.Tensor] = None,
+                  eos_id: int = 0, fixed_block_size: Optional[int] = None, sliding_window: int = 0,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Generic flex-attention forward (no relative term).  Returns ``(out [B,Hq,Sq,D] bf16,
+    lse [B,Hq,Sq] fp32)``.
+
+    q [B,Hq,Sq,D] bf16; k, v [B,Hkv,Sk,D] bf16; sink_weights [Hq] fp32 or None;
+    tokens [B,Sq] int32/int64 or None (None: causal; else block-causal, blocks ending at
+    ``eos_id``); ``fixed_block_size`` None/<=0: none; ``sliding_window`` <= 0: none;
+    ``scale`` applies only without sink weights (None: head_dim^-0.5).
+    """
+    dev = q.device
+    q = _dev(q, "q", (torch.bfloat16,), None)
+    k = _dev(k, "k", (torch.bfloat16,), dev)
+    v = _dev(v, "v", (torch.bfloat16,), dev)
+    sink_weights = _dev(sink_weights, "sink_weights", (torch.float32,), dev)
+    tokens = _pos_tensor(tokens, "tokens", dev)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k and v must be 4-d")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    for name, t, shape in (("k", k, (B, Hkv, Sk, D)), ("v", v, (B, Hkv, Sk, D)),
+                           ("sink_weights", sink_weights, (Hq,)), ("tokens", tokens, (B, Sq))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
+    out = (torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=dev) if out is None
+           else _dev(out, "out", (torch.bfloat16,), dev))
+    lse = (torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if lse is None
+           else _dev(lse, "lse", (torch.float32,), dev))
+    if workspace is None:
+        workspace = torch.empty(max(flex_attn_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
+                                device=dev)
+    rc = load().flex_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink_weights), _ptr(tokens), int(eos_id),
+                              int(fixed_block_size or 0), int(sliding_window or 0),
+                              float(scale) if scale is not None else 0.0, B, Sq, Sk, Hq, Hkv, D,
+                              _ptr(out), _ptr(lse), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    _check(rc, "flex_attn_fwd")
+    return out, lse

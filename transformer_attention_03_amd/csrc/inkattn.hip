@@ -70,6 +70,7 @@ constexpr int WAIT_VM_LGKM = 0x0070;
 constexpr int WAIT_LGKM = 0xC07F;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -194,9 +195,12 @@ struct FwdParams {
     const TileSummary* qsum;       // [B, nQB]
     const TileSummary* ksum;       // [B, nKT]
     const int* kanchor;            // [B, Sk] key start column j - key_positions[j], INT_MIN if not real
-    float* out;
-    float* lse;
-    int B, Sq, Sk, Hq, Hkv, G, E;
+    void* out;                     // fp32, or bf16 when out_bf16
+    float* lse;                    // may be NULL (not written)
+    // element strides (batch row, token, head) of q, k, out, lse and sink
+    long long q_bs, q_ts, q_hs, k_bs, k_ts, k_hs, o_bs, o_ts, o_hs, l_bs, l_ts, l_hs, s_bs, s_ts, s_hs;
+    int out_bf16;
+    int B, Sq, Sk, Hq, Hkv, G, E;  // E == 0: no relative bias (profiles unused)
     int window;      // <= 0: none
     int qoff;        // query_offset
     int hpw;         // query heads per workgroup
@@ -321,6 +325,7 @@ enum : int { BIAS_NONE = 0, BIAS_FAST = 1, BIAS_EDGE = 2 };
 // [0, E) (one contiguous 4-element run per lane and 4 keys), or mixed.
 __device__ __forceinline__ int bias_class(int qlo, int qhi, int js, int E)
 {
+    if (E <= 0) return BIAS_NONE;   // no relative term
     const int rmin = qlo - (js + 31), rmax = qhi - js;
     if (rmin >= E) return BIAS_NONE;
     if (rmin >= 0 && rmax < E) return BIAS_FAST;
@@ -389,12 +394,12 @@ void attn_fwd_kernel(FwdParams p)
     const int a_q = qreal ? (p.positions ? gi - p.positions[qrow] : 0) : 0;
     const int gi_eff = qreal ? gi : -1;
     const unsigned wlim = p.window > 0 ? (unsigned)p.window : 0x80000000u;
-    const float sig = qin ? p.sink[qrow * p.Hq + h] : -INFINITY;
+    const float sig = (qin && p.sink) ? p.sink[b * p.s_bs + i * p.s_ts + h * p.s_hs] : -INFINITY;
 
     // Q^T operand: lane holds q[i, h, 16*kk + 8*hh + 0..7].
     bf16x8 qreg[NKK];
     {
-        const __bf16* qp = p.q + (qrow * p.Hq + h) * D + 8 * hh;
+        const __bf16* qp = p.q + b * p.q_bs + (long long)i * p.q_ts + h * p.q_hs + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = qin ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
     }
@@ -488,10 +493,10 @@ void attn_fwd_kernel(FwdParams p)
     // ---- K / V staging by LDS DMA.  The K resource covers rows 0..Sk-1 of
     // this (batch row, K/V head), rows past Sk read as zero; the V^T resource
     // covers the staged tiles of this (batch row, K/V head).
-    const int krow = p.Hkv * D * 2;                     // bytes between consecutive keys
+    const int krow = (int)p.k_ts * 2;                   // bytes between consecutive keys
     const unsigned nrec = p.Sk > 0 ? (unsigned)((size_t)(p.Sk - 1) * krow + D * 2) : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.k + ((size_t)b * p.Sk * p.Hkv + g) * D), 0, nrec, 0x00020000);
+        (void*)(p.k + b * p.k_bs + g * p.k_hs), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.v16 + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(D * BN)), 0,
         (unsigned)p.nKT * (unsigned)VBYTES, 0x00020000);
@@ -910,7 +915,7 @@ void attn_fwd_kernel(FwdParams p)
     const float l_tot = half_sum(l);
     if (!qin) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* op = p.out + (qrow * p.Hq + h) * D;
+    const long long oo = b * p.o_bs + (long long)i * p.o_ts + h * p.o_hs;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -918,15 +923,23 @@ void attn_fwd_kernel(FwdParams p)
             f32x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * jj + e] * inv;
-            *(f32x4*)(op + 32 * db + 8 * jj + 4 * hh) = w;
+            const int d0 = 32 * db + 8 * jj + 4 * hh;
+            if (p.out_bf16) {
+                bf16x4 wb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wb[e] = (__bf16)w[e];   // round to nearest even
+                *(bf16x4*)((__bf16*)p.out + oo + d0) = wb;
+            } else {
+                *(f32x4*)((float*)p.out + oo + d0) = w;
+            }
         }
     }
-    if (hh == 0) {
+    if (hh == 0 && p.lse) {
         float lse;
         if (!qreal) lse = sig;
         else if (l_tot > 0.0f) lse = (m + log2f(l_tot)) * LN2;
         else lse = -INFINITY;
-        p.lse[qrow * p.Hq + h] = lse;
+        p.lse[b * p.l_bs + (long long)i * p.l_ts + h * p.l_hs] = lse;
     }
 }
 
@@ -941,7 +954,9 @@ void attn_fwd_kernel(FwdParams p)
 template <int D>
 __global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restrict__ v,
                                                            const uint8_t* __restrict__ key_valid,
-                                                           int Sk, int Hkv, int nKT, _Float16* __restrict__ vt)
+                                                           int Sk, int Hkv, int nKT, long long v_bs,
+                                                           long long v_ts, long long v_hs,
+                                                           _Float16* __restrict__ vt)
 {
     constexpr int CH = D / 8;                 // 16-byte chunks per key row
     constexpr int PITCH = BN + 8;             // fp16 per transposed LDS row
@@ -955,7 +970,7 @@ __global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restr
         const int j = kt * BN + key;
         f16x8 y = f16x8{};
         if (j < Sk && key_valid[(size_t)b * Sk + j]) {
-            const bf16x8 x = *(const bf16x8*)(v + (((size_t)b * Sk + j) * Hkv + g) * D + 8 * dc);
+            const bf16x8 x = *(const bf16x8*)(v + b * v_bs + j * v_ts + g * v_hs + 8 * dc);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
         }
@@ -1153,7 +1168,7 @@ int check_fwd_args(const void* q, const void* k, const void* v, const void* prof
     return INKATTN_OK;
 }
 
-// Workgroup shape: 4 waves; heads per workgroup hpw divides G; hpw * tpw = 4.
+// Workgroup shape: NWAVES waves; heads per workgroup hpw divides G; hpw * tpw = NWAVES.
 struct Shape {
     int nw, hpw, tpw;
 };
@@ -1174,6 +1189,114 @@ void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
     hipLaunchKernelGGL((attn_fwd_kernel<D, PB, NWAVES>), grid, dim3(64 * NWAVES), 0, st, p);
 }
 
+// Positions for the generic flex forward, one workgroup per batch row: a
+// token's position counts from the start of its block, where blocks end after
+// every token equal to eos (when tokens is given) and, with fixed > 0, also
+// start at every multiple of fixed.  Also writes nones bytes of 1 (token
+// validity: every token is real).
+__global__ __launch_bounds__(256) void flex_positions_kernel(const int32_t* __restrict__ tokens, int eos, int fixed,
+                                                             int S, int32_t* __restrict__ pos,
+                                                             uint8_t* __restrict__ ones, size_t nones)
+{
+    __shared__ int carry[256];
+    const int b = blockIdx.x, t = threadIdx.x;
+    for (size_t u = (size_t)b * 256 + t; u < nones; u += (size_t)gridDim.x * 256) ones[u] = 1;
+    if (!pos) return;
+    const int32_t* tk = tokens ? tokens + (size_t)b * S : nullptr;
+    int32_t* ps = pos + (size_t)b * S;
+    const int len = (S + 255) / 256;
+    const int lo = min(S, t * len), hi = min(S, lo + len);
+    // start column after the last eos of this thread's segment (-1: none)
+    int last = -1;
+    if (tk)
+        for (int u = lo; u < hi; ++u)
+            if (tk[u] == eos) last = u + 1;
+    carry[t] = last;
+    __syncthreads();
+    // exclusive running max over the segments before this one
+    int start = 0;
+    for (int w = 0; w < t; ++w) start = max(start, carry[w]);
+    for (int u = lo; u < hi; ++u) {
+        const int st = fixed > 0 ? max(start, (u / fixed) * fixed) : start;
+        ps[u] = u - st;
+        if (tk && tk[u] == eos) start = u + 1;
+    }
+}
+
+// Launches the fp16 value staging for v with element strides (batch row,
+// key, head).
+int launch_stage(const __bf16* v, const uint8_t* key_valid, int B, int Sk, int Hkv, int D, long long v_bs,
+                 long long v_ts, long long v_hs, _Float16* v16, hipStream_t st)
+{
+    const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
+    if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
+    if (D == 128)
+        hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, st, v, key_valid, Sk, Hkv,
+                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
+    else
+        hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, st, v, key_valid, Sk, Hkv,
+                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
+    return check_launch("stage_values_kernel");
+}
+
+struct Strides {
+    long long bs, ts, hs;   // elements between batch rows, tokens, heads
+};
+
+// Launches the attention kernel over a planned and staged workspace.
+int run_forward(const void* q, const void* k, void* workspace, const void* profiles, int profiles_dtype,
+                const float* sink, const uint8_t* valid, const MaskArgs& ma, const int32_t* positions, int window,
+                int query_offset, int B, int Sq, int Sk, int Hq, int Hkv, int D, int E, void* out, int out_bf16,
+                float* lse, Strides qs, Strides ks, Strides os, Strides ls, Strides ss, float c_log2,
+                hipStream_t st)
+{
+    const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
+    const Shape sh = choose_shape(Hq / Hkv);
+
+    FwdParams p;
+    p.q = (const __bf16*)q;
+    p.k = (const __bf16*)k;
+    p.v16 = (const _Float16*)((const char*)workspace + summaries_bytes(B, Sq, Sk));
+    p.profiles = profiles;
+    p.sink = sink;
+    p.valid = valid;
+    p.key_valid = ma.key_valid;
+    p.positions = positions;
+    p.key_positions = ma.key_positions;
+    p.qsum = (const TileSummary*)workspace;
+    p.ksum = p.qsum + (size_t)B * nQB;
+    p.kanchor = (const int*)((const char*)workspace + tile_summary_bytes(B, Sq, Sk));
+    p.out = out;
+    p.lse = lse;
+    p.q_bs = qs.bs; p.q_ts = qs.ts; p.q_hs = qs.hs;
+    p.k_bs = ks.bs; p.k_ts = ks.ts; p.k_hs = ks.hs;
+    p.o_bs = os.bs; p.o_ts = os.ts; p.o_hs = os.hs;
+    p.l_bs = ls.bs; p.l_ts = ls.ts; p.l_hs = ls.hs;
+    p.s_bs = ss.bs; p.s_ts = ss.ts; p.s_hs = ss.hs;
+    p.out_bf16 = out_bf16;
+    p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.E = E;
+    p.window = window;
+    p.qoff = query_offset;
+    p.hpw = sh.hpw;
+    p.tpw = sh.tpw;
+    p.nchunk = p.G / p.hpw;
+    p.nQB = nQB; p.nQG = ceil_div(nQB, sh.tpw); p.nKT = nKT;
+    p.c_log2 = c_log2;
+
+    const size_t nblocks = (size_t)p.nQG * B * Hkv * p.nchunk;
+    if (nblocks >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
+    const dim3 grid((unsigned)nblocks);
+    const bool pb = profiles_dtype == INKATTN_BF16;
+    if (D == 128) {
+        if (pb) launch_fwd<128, true>(sh, grid, st, p);
+        else launch_fwd<128, false>(sh, grid, st, p);
+    } else {
+        if (pb) launch_fwd<64, true>(sh, grid, st, p);
+        else launch_fwd<64, false>(sh, grid, st, p);
+    }
+    return check_launch("attn_fwd_kernel");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1186,6 +1309,68 @@ size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D)
 
 int attn_query_block(void) { return BM; }
 int attn_key_tile(void) { return BN; }
+
+size_t flex_attn_workspace_size(int B, int Sq, int Sk, int Hkv, int D)
+{
+    if (B <= 0 || Sq < 0 || Sk < 0 || Hkv < 0 || D < 0) return 0;
+    return attn_fwd_workspace_size(B, Sq, Sk, Hkv, D) + round256((size_t)B * Sq * 4) +
+           round256((size_t)B * std::max(Sq, Sk));
+}
+
+int flex_attn_fwd(const void* q, const void* k, const void* v, const float* sink_weights,
+                  const int32_t* tokens, int32_t eos_id, int64_t fixed_block_size, int64_t sliding_window,
+                  float scale, int B, int Sq, int Sk, int Hq, int Hkv, int D, void* out, float* lse,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_last_error[0] = '\0';
+    if (B < 0 || Sq < 0 || Sk < 0) return fail(INKATTN_ERR_SHAPE, "negative size");
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(INKATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
+    if (Sq >= (1 << 30) || Sk >= (1 << 30)) return fail(INKATTN_ERR_SHAPE, "sequence lengths must stay below 2^30");
+    if ((size_t)B * Hq * Sq * D >= (size_t(1) << 40) || (size_t)Sk * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "tensor too large");
+    const bool blocks = tokens != nullptr || fixed_block_size > 0;
+    if (blocks && Sq != Sk) return fail(INKATTN_ERR_SHAPE, "block masks need Sq == Sk (got %d, %d)", Sq, Sk);
+    if (fixed_block_size >= (int64_t(1) << 31)) fixed_block_size = 0;
+    if (sliding_window >= (int64_t(1) << 31) || sliding_window < 0) sliding_window = 0;
+    if ((size_t)B * Sq == 0) return INKATTN_OK;
+    if (!q || !out) return fail(INKATTN_ERR_NULL, "q or out is NULL");
+    if (Sk > 0 && (!k || !v)) return fail(INKATTN_ERR_NULL, "k or v is NULL");
+    if (!aligned(q, 16) || (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16))) || !aligned(out, 16))
+        return fail(INKATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+    if ((sink_weights && !aligned(sink_weights, 4)) || (lse && !aligned(lse, 4)) || (tokens && !aligned(tokens, 4)))
+        return fail(INKATTN_ERR_ALIGN, "sink_weights / lse / tokens misaligned");
+    if (int rc = check_workspace(workspace, workspace_bytes, flex_attn_workspace_size(B, Sq, Sk, Hkv, D))) return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    const size_t attn_ws = attn_fwd_workspace_size(B, Sq, Sk, Hkv, D);
+    int32_t* pos = blocks ? (int32_t*)(ws + attn_ws) : nullptr;
+    uint8_t* ones = (uint8_t*)(ws + attn_ws + round256((size_t)B * Sq * 4));
+    const size_t nones = (size_t)B * std::max(Sq, Sk);
+    hipLaunchKernelGGL(flex_positions_kernel, dim3((unsigned)B), dim3(256), 0, st, tokens, (int)eos_id,
+                       (int)fixed_block_size, Sq, pos, ones, nones);
+    if (int rc = check_launch("flex_positions_kernel")) return rc;
+
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(ones, ones, pos, pos, 0, B, Sq, Sk, &ma)) return rc;
+    if (int rc = launch_summaries(ones, pos, ma.key_valid, ma.key_positions, 0, B, Sq, Sk, workspace, st)) return rc;
+    if (Sk > 0) {
+        const long long v_hs = (long long)Sk * D;
+        if (int rc = launch_stage((const __bf16*)v, ones, B, Sk, Hkv, D, Hkv * v_hs, D, v_hs,
+                                  (_Float16*)(ws + summaries_bytes(B, Sq, Sk)), st))
+            return rc;
+    }
+    // scale: applied only without sink weights (the default head_dim^-0.5 otherwise)
+    const double sc = (!sink_weights && scale > 0.0f) ? (double)scale : 1.0 / std::sqrt((double)D);
+    const long long q_hs = (long long)Sq * D, k_hs = (long long)Sk * D;
+    return run_forward(q, k, workspace, nullptr, INKATTN_F32, sink_weights, ones, ma, pos, (int)sliding_window, 0, B,
+                       Sq, Sk, Hq, Hkv, D, 0, out, 1, lse, Strides{Hq * q_hs, D, q_hs},
+                       Strides{Hkv * k_hs, D, k_hs}, Strides{Hq * q_hs, D, q_hs},
+                       Strides{(long long)Hq * Sq, 1, Sq}, Strides{0, 0, 1},
+                       (float)(sc * 1.4426950408889634), st);
+}
 
 const char* attn_status_string(int status)
 {
@@ -1233,16 +1418,8 @@ int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_va
     if (int rc = check_workspace(workspace, workspace_bytes,
                                  summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
         return rc;
-    const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
-    if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
-    _Float16* v16 = (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk));
-    if (D == 128)
-        hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream,
-                           (const __bf16*)v, ma.key_valid, Sk, Hkv, ceil_div(Sk, BN), v16);
-    else
-        hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, (hipStream_t)stream,
-                           (const __bf16*)v, ma.key_valid, Sk, Hkv, ceil_div(Sk, BN), v16);
-    return check_launch("stage_values_kernel");
+    return launch_stage((const __bf16*)v, ma.key_valid, B, Sk, Hkv, D, (long long)Sk * Hkv * D, (long long)Hkv * D, D,
+                        (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk)), (hipStream_t)stream);
 }
 
 int attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -1268,47 +1445,12 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
                                  summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
         return rc;
 
-    hipStream_t st = (hipStream_t)stream;
-    const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
-    const Shape sh = choose_shape(Hq / Hkv);
-
-    FwdParams p;
-    p.q = (const __bf16*)q;
-    p.k = (const __bf16*)k;
-    (void)v;   // read through the fp16 copy attn_stage_values wrote
-    p.v16 = (const _Float16*)((const char*)workspace + summaries_bytes(B, Sq, Sk));
-    p.profiles = profiles;
-    p.sink = sink;
-    p.valid = valid;
-    p.key_valid = ma.key_valid;
-    p.positions = positions;
-    p.key_positions = ma.key_positions;
-    p.qsum = (const TileSummary*)workspace;
-    p.ksum = p.qsum + (size_t)B * nQB;
-    p.kanchor = (const int*)((const char*)workspace + tile_summary_bytes(B, Sq, Sk));
-    p.out = out;
-    p.lse = lse;
-    p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.E = E;
-    p.window = (int)window;
-    p.qoff = (int)query_offset;
-    p.hpw = sh.hpw;
-    p.tpw = sh.tpw;
-    p.nchunk = p.G / p.hpw;
-    p.nQB = nQB; p.nQG = ceil_div(nQB, sh.tpw); p.nKT = nKT;
-    p.c_log2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
-
-    const size_t nblocks = (size_t)p.nQG * B * Hkv * p.nchunk;
-    if (nblocks >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
-    const dim3 grid((unsigned)nblocks);
-    const bool pb = profiles_dtype == INKATTN_BF16;
-    if (D == 128) {
-        if (pb) launch_fwd<128, true>(sh, grid, st, p);
-        else launch_fwd<128, false>(sh, grid, st, p);
-    } else {
-        if (pb) launch_fwd<64, true>(sh, grid, st, p);
-        else launch_fwd<64, false>(sh, grid, st, p);
-    }
-    return check_launch("attn_fwd_kernel");
+    const long long sq_h = (long long)Hq * D, sk_h = (long long)Hkv * D;
+    return run_forward(q, k, workspace, profiles, profiles_dtype, sink, valid, ma, positions, (int)window,
+                       (int)query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, 0, lse,
+                       Strides{Sq * sq_h, sq_h, D}, Strides{Sk * sk_h, sk_h, D}, Strides{Sq * sq_h, sq_h, D},
+                       Strides{(long long)Sq * Hq, Hq, 1}, Strides{(long long)Sq * Hq, Hq, 1},
+                       (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634), (hipStream_t)stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v,

@@ -166,3 +166,78 @@ def sample_rows(B: int, S: int, n: int, seed: int, must: tuple = ()) -> torch.Te
     extra = torch.tensor([b * S + i for (b, i) in must], dtype=torch.int64)
     rows = torch.unique(torch.cat([picks, extra]))
     return rows[(rows >= 0) & (rows < B * S)]
+
+
+# ----------------------------------------------------------------------------
+# Generic flex-attention inputs (page "nemo_automodel.components.attention.
+# flex_attention", FlexAttention.forward): head-major q [B,Hq,S,D], k / v
+# [B,Hkv,S,D] bf16, per-head sink weights [Hq] fp32, and token ids [B,S] int32
+# whose EOS tokens end the documents of "block_causal".
+# ----------------------------------------------------------------------------
+EOS_ID = 2
+
+
+@dataclasses.dataclass(frozen=True)
+class FlexWorkload:
+    """Shape and value recipe of one synthetic generic flex-attention workload."""
+
+    name: str
+    B: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    mask: str                       # "causal" or "block_causal"
+    doc_min: int = 0                # block_causal: document lengths U{doc_min..doc_max}
+    doc_max: int = 0
+    fixed_block_size: Optional[int] = None
+    sliding_window: int = 0
+    sinks: bool = True
+    sink_std: float = 1.0
+    scale: Optional[float] = None
+    Sk: Optional[int] = None        # key length (default S; only for "causal" without fixed blocks)
+    seed: int = 0
+
+
+FLEX_WORKLOADS = {
+    # the S = 8192 GQA shape of the local / full-causal workloads, as a generic
+    # block-causal layer: EOS-delimited documents, per-head sinks, bf16 output
+    "flex_block_causal": FlexWorkload("flex_block_causal", B=1, S=8192, Hq=32, Hkv=8, D=128,
+                                      mask="block_causal", doc_min=256, doc_max=4096, seed=1101),
+}
+
+
+def generate_flex(w: FlexWorkload, seed: Optional[int] = None) -> dict:
+    """Host tensors for a generic flex workload; deterministic in (w, seed)."""
+    gen = torch.Generator().manual_seed(w.seed if seed is None else seed)
+    B, S = w.B, w.S
+    Sk = S if w.Sk is None else w.Sk
+    tokens = None
+    doc_ends = []
+    if w.mask == "block_causal":
+        # token ids in [3, 1000); an EOS closes each document (the last one may run to the end)
+        tokens = torch.randint(3, 1000, (B, S), generator=gen, dtype=torch.int32)
+        for b in range(B):
+            ends = []
+            c = 0
+            while True:
+                length = int(torch.randint(w.doc_min, w.doc_max + 1, (1,), generator=gen))
+                if c + length > S:
+                    break
+                tokens[b, c + length - 1] = EOS_ID
+                ends.append(c + length - 1)
+                c += length
+            doc_ends.append(ends)
+    q = _randn((B, w.Hq, S, w.D), 1.0, gen, torch.bfloat16)
+    k = _randn((B, w.Hkv, Sk, w.D), 1.0, gen, torch.bfloat16)
+    v = _randn((B, w.Hkv, Sk, w.D), 1.0, gen, torch.bfloat16)
+    sink_weights = _randn((w.Hq,), w.sink_std, gen, torch.float32) if w.sinks else None
+    return dict(q=q, k=k, v=v, sink_weights=sink_weights, tokens=tokens, eos_id=EOS_ID,
+                fixed_block_size=w.fixed_block_size, sliding_window=w.sliding_window, scale=w.scale,
+                doc_ends=doc_ends, workload=w)
+
+
+def flex_custom(B: int, S: int, Hq: int, Hkv: int, D: int, mask: str = "causal", seed: int = 0,
+                **kw) -> dict:
+    """Inputs for an ad-hoc generic flex shape with the same value recipe."""
+    return generate_flex(FlexWorkload("custom", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, mask=mask, seed=seed, **kw))
