@@ -948,25 +948,30 @@ void attn_fwd_kernel(FwdParams p)
 // that are not real, so that a masked key's weight 0 never meets a value that
 // fp16 cannot hold.  One thread per 8 elements.
 // ---------------------------------------------------------------------------
-// One workgroup per (batch row, K/V head, 64-key tile): v (bf16) -> V^T
-// (fp16, saturated to +-65504, 0 at keys that are not real or lie past Sk),
-// the keys of each row in vt_slot order.
+// One workgroup of D threads per (batch row, K/V head, 64-key tile): v (bf16)
+// -> V^T (fp16, saturated to +-65504, 0 at keys that are not real or lie past
+// Sk), the keys of each row in vt_slot order.  Thread (slot group sg, dim
+// chunk dc) loads the 8 keys of output slots 8 sg .. 8 sg + 7 at dims
+// 8 dc .. 8 dc + 7, transposes the 8 x 8 block in registers and writes 8 rows
+// of 16 bytes.
 template <int D>
-__global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restrict__ v,
-                                                           const uint8_t* __restrict__ key_valid,
-                                                           int Sk, int Hkv, int nKT, long long v_bs,
-                                                           long long v_ts, long long v_hs,
-                                                           _Float16* __restrict__ vt)
+__global__ __launch_bounds__(D) void stage_values_kernel(const __bf16* __restrict__ v,
+                                                         const uint8_t* __restrict__ key_valid,
+                                                         int Sk, int Hkv, int nKT, long long v_bs,
+                                                         long long v_ts, long long v_hs,
+                                                         _Float16* __restrict__ vt)
 {
     constexpr int CH = D / 8;                 // 16-byte chunks per key row
-    constexpr int PITCH = BN + 8;             // fp16 per transposed LDS row
-    __shared__ __attribute__((aligned(16))) _Float16 tile[D * PITCH];
     const int t = blockIdx.x;                 // ((b * Hkv + g) * nKT + kt)
     const int kt = t % nKT;
     const int g = (t / nKT) % Hkv;
     const int b = t / (nKT * Hkv);
-    for (int c = threadIdx.x; c < BN * CH; c += blockDim.x) {
-        const int key = c / CH, dc = c % CH;
+    const int sg = threadIdx.x / CH, dc = threadIdx.x % CH;
+    f16x8 rows[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        // slot 8 sg + tt holds key 16 (sg / 2) + 8 (tt / 4) + 4 (sg % 2) + ((tt % 4) ^ 3)
+        const int key = 16 * (sg >> 1) + 8 * (tt >> 2) + 4 * (sg & 1) + ((tt & 3) ^ 3);
         const int j = kt * BN + key;
         f16x8 y = f16x8{};
         if (j < Sk && key_valid[(size_t)b * Sk + j]) {
@@ -974,15 +979,15 @@ __global__ __launch_bounds__(256) void stage_values_kernel(const __bf16* __restr
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
         }
-        const int slot = vt_slot(key);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tile[(8 * dc + e) * PITCH + slot] = y[e];
+        rows[tt] = y;
     }
-    __syncthreads();
     _Float16* dst = vt + (size_t)t * D * BN;
-    for (int c = threadIdx.x; c < D * (BN / 8); c += blockDim.x) {
-        const int d = c / (BN / 8), sc = c % (BN / 8);
-        *(f16x8*)(dst + d * BN + 8 * sc) = *(const f16x8*)(tile + d * PITCH + 8 * sc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        f16x8 o;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) o[tt] = rows[tt][e];
+        *(f16x8*)(dst + (8 * dc + e) * BN + 8 * sg) = o;
     }
 }
 
@@ -1194,32 +1199,49 @@ void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
 // every token equal to eos (when tokens is given) and, with fixed > 0, also
 // start at every multiple of fixed.  Also writes nones bytes of 1 (token
 // validity: every token is real).
-__global__ __launch_bounds__(256) void flex_positions_kernel(const int32_t* __restrict__ tokens, int eos, int fixed,
-                                                             int S, int32_t* __restrict__ pos,
-                                                             uint8_t* __restrict__ ones, size_t nones)
+__global__ __launch_bounds__(1024) void flex_positions_kernel(const int32_t* __restrict__ tokens, int eos,
+                                                              int fixed, int S, int32_t* __restrict__ pos,
+                                                              uint8_t* __restrict__ ones, size_t nones)
 {
-    __shared__ int carry[256];
+    constexpr int PER = 8;                       // tokens per thread and pass
+    __shared__ int scan[1024];
     const int b = blockIdx.x, t = threadIdx.x;
-    for (size_t u = (size_t)b * 256 + t; u < nones; u += (size_t)gridDim.x * 256) ones[u] = 1;
+    for (size_t u = (size_t)b * 1024 + t; u < nones; u += (size_t)gridDim.x * 1024) ones[u] = 1;
     if (!pos) return;
     const int32_t* tk = tokens ? tokens + (size_t)b * S : nullptr;
     int32_t* ps = pos + (size_t)b * S;
-    const int len = (S + 255) / 256;
-    const int lo = min(S, t * len), hi = min(S, lo + len);
-    // start column after the last eos of this thread's segment (-1: none)
-    int last = -1;
-    if (tk)
-        for (int u = lo; u < hi; ++u)
-            if (tk[u] == eos) last = u + 1;
-    carry[t] = last;
-    __syncthreads();
-    // exclusive running max over the segments before this one
-    int start = 0;
-    for (int w = 0; w < t; ++w) start = max(start, carry[w]);
-    for (int u = lo; u < hi; ++u) {
-        const int st = fixed > 0 ? max(start, (u / fixed) * fixed) : start;
-        ps[u] = u - st;
-        if (tk && tk[u] == eos) start = u + 1;
+    int carry = 0;                               // start column after the last eos of earlier passes
+    for (int base = 0; base < S; base += 1024 * PER) {
+        const int lo = base + t * PER;
+        int is_eos[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) is_eos[e] = (tk && lo + e < S) ? (tk[lo + e] == eos) : 0;
+        int last = 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (is_eos[e]) last = lo + e + 1;
+        // running max over the threads' segments (Hillis-Steele), exclusive
+        scan[t] = last;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {
+            const int other = t >= d ? scan[t - d] : 0;
+            __syncthreads();
+            scan[t] = max(scan[t], other);
+            __syncthreads();
+        }
+        int start = max(carry, t > 0 ? scan[t - 1] : 0);
+        const int pass_max = scan[1023];
+        __syncthreads();                         // scan[] is rewritten by the next pass
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int u = lo + e;
+            if (u < S) {
+                const int st = fixed > 0 ? max(start, (u / fixed) * fixed) : start;
+                ps[u] = u - st;
+            }
+            if (is_eos[e]) start = u + 1;
+        }
+        carry = max(carry, pass_max);
     }
 }
 
@@ -1231,10 +1253,10 @@ int launch_stage(const __bf16* v, const uint8_t* key_valid, int B, int Sk, int H
     const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
     if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
     if (D == 128)
-        hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, st, v, key_valid, Sk, Hkv,
+        hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(128), 0, st, v, key_valid, Sk, Hkv,
                            ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
     else
-        hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, st, v, key_valid, Sk, Hkv,
+        hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(64), 0, st, v, key_valid, Sk, Hkv,
                            ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
     return check_launch("stage_values_kernel");
 }
@@ -1349,7 +1371,7 @@ int flex_attn_fwd(const void* q, const void* k, const void* v, const float* sink
     int32_t* pos = blocks ? (int32_t*)(ws + attn_ws) : nullptr;
     uint8_t* ones = (uint8_t*)(ws + attn_ws + round256((size_t)B * Sq * 4));
     const size_t nones = (size_t)B * std::max(Sq, Sk);
-    hipLaunchKernelGGL(flex_positions_kernel, dim3((unsigned)B), dim3(256), 0, st, tokens, (int)eos_id,
+    hipLaunchKernelGGL(flex_positions_kernel, dim3((unsigned)B), dim3(1024), 0, st, tokens, (int)eos_id,
                        (int)fixed_block_size, Sq, pos, ones, nones);
     if (int rc = check_launch("flex_positions_kernel")) return rc;
 
