@@ -67,6 +67,11 @@ def _load():
                 P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 P, ctypes.c_int64, P, P, P, ctypes.c_int]
+            lib.attn_oracle_bwd.restype = ctypes.c_int
+            lib.attn_oracle_bwd.argtypes = [
+                P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                P, P, P, P, P, P, P]
             lib.attn_oracle_max_threads.restype = ctypes.c_int
             lib.attn_oracle_mask.restype = ctypes.c_int
             lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
@@ -195,6 +200,42 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
     if rows is None:
         return out.reshape(B, Sq, Hq, D), lse.reshape(B, Sq, Hq), cnt.reshape(B, Sq)
     return out, lse, cnt
+
+
+def attn_bwd(q, k, v, profiles, sink, valid, dout, dlse=None, key_valid=None, positions=None,
+             key_positions=None, window: Optional[int] = None, query_offset: int = 0,
+             profiles_bf16: Optional[bool] = None):
+    """fp64 gradients of the forward for upstream gradients ``dout [B,Sq,Hq,D]`` and ``dlse
+    [B,Sq,Hq]`` (None: zero).  Returns ``(dq, dk, dv, dprofiles, dsink)`` as fp64 numpy arrays."""
+    import torch
+
+    B, Sq, Hq, D = (int(x) for x in q.shape)
+    Sk, Hkv = int(k.shape[1]), int(k.shape[2])
+    E = int(profiles.shape[-1])
+    if profiles_bf16 is None:
+        profiles_bf16 = isinstance(profiles, torch.Tensor) and profiles.dtype == torch.bfloat16
+    qn, kn, vn = _as_np(q, np.uint16), _as_np(k, np.uint16), _as_np(v, np.uint16)
+    pn = _as_np(profiles, np.uint16 if profiles_bf16 else np.float32)
+    sn = _as_np(sink, np.float32)
+    don = np.ascontiguousarray(_as_np(dout, np.float64) if not isinstance(dout, torch.Tensor)
+                               else dout.to(torch.float64).numpy())
+    dln = None
+    if dlse is not None:
+        dln = np.ascontiguousarray(dlse.to(torch.float64).numpy() if isinstance(dlse, torch.Tensor)
+                                   else np.asarray(dlse, dtype=np.float64))
+    valid_n, kvalid_n, pos_n, kpos_n = _mask_inputs(valid, key_valid, positions, key_positions,
+                                                    query_offset, B, Sq, Sk)
+    dq = np.empty((B, Sq, Hq, D)); dk = np.empty((B, Sk, Hkv, D)); dv = np.empty((B, Sk, Hkv, D))
+    dp = np.empty((B, Hq, Sq, E)); ds = np.empty((B, Sq, Hq))
+    w = 0 if window is None else int(window)
+    rc = _load().attn_oracle_bwd(
+        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), int(bool(profiles_bf16)), _ptr(sn),
+        _ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n), w, int(query_offset),
+        B, Sq, Sk, Hq, Hkv, D, E, _ptr(don), None if dln is None else _ptr(dln),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dp), _ptr(ds))
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_bwd failed ({rc})")
+    return dq, dk, dv, dp, ds
 
 
 def flex_fwd(q, k, v, sink_weights=None, tokens=None, eos_id: int = 0, fixed_block_size=None,

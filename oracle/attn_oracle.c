@@ -301,6 +301,121 @@ int flex_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     return failed ? -1 : 0;
 }
 
+/*
+ * Gradients of the forward above.  The page "nemo_automodel.components.models.
+ * inkling2.flex_attention" (module summary and class Inkling2FlexAttention)
+ * makes the per-query sinks differentiable and lets gradients reach the
+ * profiles and flow in through the returned log-sum-exp; q, k and v are the
+ * ordinary attention inputs.  The gradients are the plain derivatives of the
+ * forward's definition (chain rule through the sink-augmented softmax).  For a loss with
+ * dL/dout = dout [B,Sq,Hq,D] and dL/dlse = dlse [B,Sq,Hq] (dlse may be NULL:
+ * zero), per row (b, i, h) with P_j = e^{z_j - lse}, p_s = e^{sigma - lse}:
+ *   Delta  = <dout, out>
+ *   dz_j   = P_j (<dout, v_j> - Delta + dlse)          (allowed j)
+ *   dq     = scale * sum_j dz_j k_j;   dk_j += scale * dz_j q;   dv_j += P_j dout
+ *   dprofiles[b,h,i,r] = dz_j for the allowed j at distance r in [0, E), else 0
+ *   dsink  = p_s (dlse - Delta)
+ * out / lse are recomputed here in fp64.  Outputs: dq [B,Sq,Hq,D],
+ * dk / dv [B,Sk,Hkv,D], dprofiles [B,Hq,Sq,E], dsink [B,Sq,Hq], all fp64.
+ * Single-threaded over rows for dk / dv (they accumulate across rows).
+ */
+int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const void* profiles, int profiles_is_bf16,
+                    const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                    const int32_t* positions, const int32_t* key_positions,
+                    int64_t window, int64_t query_offset,
+                    int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                    const double* dout, const double* dlse,
+                    double* dq, double* dk, double* dv, double* dprofiles, double* dsink)
+{
+    if (!q || !k || !v || !profiles || !sink || !valid || !key_valid || !positions || !key_positions ||
+        !dout || !dq || !dk || !dv || !dprofiles || !dsink)
+        return -1;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || E <= 0 || Hq % Hkv) return -1;
+    const int G = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)D);
+    memset(dq, 0, sizeof(double) * (size_t)B * Sq * Hq * D);
+    memset(dk, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
+    memset(dv, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
+    memset(dprofiles, 0, sizeof(double) * (size_t)B * Hq * Sq * E);
+    double* z = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)D);
+    uint8_t* ok = (uint8_t*)malloc((size_t)(Sk > 0 ? Sk : 1));
+    if (!z || !o || !ok) {
+        free(z); free(o); free(ok);
+        return -1;
+    }
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < Sq; ++i) {
+            int count = 0;
+            for (int j = 0; j < Sk; ++j) {
+                ok[j] = (uint8_t)allowed(valid, key_valid, positions, key_positions, window, query_offset,
+                                         Sq, Sk, b, i, j);
+                count += ok[j];
+            }
+            int64_t p_i = positions[(size_t)b * Sq + i];
+            for (int h = 0; h < Hq; ++h) {
+                int g = h / G;
+                size_t row = ((size_t)b * Sq + i) * Hq + h;
+                double sigma = (double)sink[row];
+                double dl = dlse ? dlse[row] : 0.0;
+                const double* dov = dout + row * D;
+                if (count == 0) {                  /* lse = sigma, out = 0: only the sink moves lse */
+                    dsink[row] = isinf(sigma) && sigma < 0 ? 0.0 : dl;
+                    continue;
+                }
+                const uint16_t* qrow = q + row * D;
+                double M = sigma;
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+                    int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
+                    double bias = 0.0;
+                    if (r >= 0 && r < E)
+                        bias = profile_at(profiles, profiles_is_bf16, (((size_t)b * Hq + h) * Sq + i) * (size_t)E + r);
+                    z[j] = scale * dot + bias;
+                    if (z[j] > M) M = z[j];
+                }
+                double L = exp(sigma - M);
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    double pj = exp(z[j] - M);
+                    L += pj;
+                    const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    for (int d = 0; d < D; ++d) o[d] += pj * bf16_to_double(vrow[d]);
+                }
+                double lse = M + log(L);
+                double delta = 0.0;
+                for (int d = 0; d < D; ++d) delta += dov[d] * (o[d] / L);
+                dsink[row] = exp(sigma - lse) * (dl - delta);
+                for (int j = 0; j < Sk; ++j) {
+                    if (!ok[j]) continue;
+                    double pj = exp(z[j] - lse);
+                    const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d) dp += dov[d] * bf16_to_double(vrow[d]);
+                    double dz = pj * (dp - delta + dl);
+                    double* dkr = dk + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    double* dvr = dv + (((size_t)b * Sk + j) * Hkv + g) * D;
+                    double* dqr = dq + row * D;
+                    for (int d = 0; d < D; ++d) {
+                        dqr[d] += scale * dz * bf16_to_double(krow[d]);
+                        dkr[d] += scale * dz * bf16_to_double(qrow[d]);
+                        dvr[d] += pj * dov[d];
+                    }
+                    int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
+                    if (r >= 0 && r < E) dprofiles[(((size_t)b * Hq + h) * Sq + i) * (size_t)E + r] = dz;
+                }
+            }
+        }
+    free(z); free(o); free(ok);
+    return 0;
+}
+
 /* Threads the OpenMP runtime will use for a parallel region (reported by callers). */
 int attn_oracle_max_threads(void)
 {
