@@ -71,7 +71,7 @@ def _load():
             lib.attn_oracle_bwd.argtypes = [
                 P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                P, P, P, P, P, P, P]
+                P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
             lib.attn_oracle_max_threads.restype = ctypes.c_int
             lib.attn_oracle_mask.restype = ctypes.c_int
             lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
@@ -204,9 +204,12 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
 
 def attn_bwd(q, k, v, profiles, sink, valid, dout, dlse=None, key_valid=None, positions=None,
              key_positions=None, window: Optional[int] = None, query_offset: int = 0,
-             profiles_bf16: Optional[bool] = None):
+             profiles_bf16: Optional[bool] = None, row_lo: int = 0, magnitudes: bool = False):
     """fp64 gradients of the forward for upstream gradients ``dout [B,Sq,Hq,D]`` and ``dlse
-    [B,Sq,Hq]`` (None: zero).  Returns ``(dq, dk, dv, dprofiles, dsink)`` as fp64 numpy arrays."""
+    [B,Sq,Hq]`` (None: zero).  Returns ``(dq, dk, dv, dprofiles, dsink)`` as fp64 numpy arrays.
+
+    ``row_lo`` leaves out the query rows below it (dk / dv then hold only the later rows'
+    contributions); ``magnitudes`` returns the sums of absolute contributions instead."""
     import torch
 
     B, Sq, Hq, D = (int(x) for x in q.shape)
@@ -231,8 +234,8 @@ def attn_bwd(q, k, v, profiles, sink, valid, dout, dlse=None, key_valid=None, po
     rc = _load().attn_oracle_bwd(
         _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), int(bool(profiles_bf16)), _ptr(sn),
         _ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n), w, int(query_offset),
-        B, Sq, Sk, Hq, Hkv, D, E, _ptr(don), None if dln is None else _ptr(dln),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dp), _ptr(ds))
+        B, Sq, Sk, Hq, Hkv, D, E, _ptr(don), None if dln is None else _ptr(dln), int(row_lo),
+        int(bool(magnitudes)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dp), _ptr(ds))
     if rc != 0:
         raise RuntimeError(f"attn_oracle_bwd failed ({rc})")
     return dq, dk, dv, dp, ds

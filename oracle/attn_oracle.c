@@ -318,6 +318,16 @@ int flex_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * out / lse are recomputed here in fp64.  Outputs: dq [B,Sq,Hq,D],
  * dk / dv [B,Sk,Hkv,D], dprofiles [B,Hq,Sq,E], dsink [B,Sq,Hq], all fp64.
  * Single-threaded over rows for dk / dv (they accumulate across rows).
+ *
+ * row_lo > 0 leaves out the query rows i < row_lo (their outputs stay 0):
+ * dq / dprofiles / dsink of the other rows are unchanged, and dk / dv are
+ * exact for the keys no earlier row can see (under the causal order, keys
+ * j >= query_offset + row_lo).
+ *
+ * magnitudes != 0 returns, in the same arrays, each output's sum of absolute
+ * contributions instead (every product and difference above taken in
+ * absolute value: |dout . v| -> sum |dout_d v_d|, Delta -> sum |dout_d out_d|,
+ * dlse -> |dlse|).  Tests scale their rounding tolerance by it.
  */
 int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const void* profiles, int profiles_is_bf16,
@@ -325,7 +335,7 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* positions, const int32_t* key_positions,
                     int64_t window, int64_t query_offset,
                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
-                    const double* dout, const double* dlse,
+                    const double* dout, const double* dlse, int row_lo, int magnitudes,
                     double* dq, double* dk, double* dv, double* dprofiles, double* dsink)
 {
     if (!q || !k || !v || !profiles || !sink || !valid || !key_valid || !positions || !key_positions ||
@@ -345,8 +355,9 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         free(z); free(o); free(ok);
         return -1;
     }
+    memset(dsink, 0, sizeof(double) * (size_t)B * Sq * Hq);
     for (int b = 0; b < B; ++b)
-        for (int i = 0; i < Sq; ++i) {
+        for (int i = row_lo > 0 ? row_lo : 0; i < Sq; ++i) {
             int count = 0;
             for (int j = 0; j < Sk; ++j) {
                 ok[j] = (uint8_t)allowed(valid, key_valid, positions, key_positions, window, query_offset,
@@ -361,7 +372,7 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 double dl = dlse ? dlse[row] : 0.0;
                 const double* dov = dout + row * D;
                 if (count == 0) {                  /* lse = sigma, out = 0: only the sink moves lse */
-                    dsink[row] = isinf(sigma) && sigma < 0 ? 0.0 : dl;
+                    dsink[row] = isinf(sigma) && sigma < 0 ? 0.0 : (magnitudes ? fabs(dl) : dl);
                     continue;
                 }
                 const uint16_t* qrow = q + row * D;
@@ -389,23 +400,31 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 }
                 double lse = M + log(L);
                 double delta = 0.0;
-                for (int d = 0; d < D; ++d) delta += dov[d] * (o[d] / L);
-                dsink[row] = exp(sigma - lse) * (dl - delta);
+                for (int d = 0; d < D; ++d)
+                    delta += magnitudes ? fabs(dov[d] * (o[d] / L)) : dov[d] * (o[d] / L);
+                dsink[row] = magnitudes ? exp(sigma - lse) * (fabs(dl) + delta) : exp(sigma - lse) * (dl - delta);
                 for (int j = 0; j < Sk; ++j) {
                     if (!ok[j]) continue;
                     double pj = exp(z[j] - lse);
                     const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
                     const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
                     double dp = 0.0;
-                    for (int d = 0; d < D; ++d) dp += dov[d] * bf16_to_double(vrow[d]);
-                    double dz = pj * (dp - delta + dl);
+                    for (int d = 0; d < D; ++d)
+                        dp += magnitudes ? fabs(dov[d] * bf16_to_double(vrow[d])) : dov[d] * bf16_to_double(vrow[d]);
+                    double dz = magnitudes ? pj * (dp + delta + fabs(dl)) : pj * (dp - delta + dl);
                     double* dkr = dk + (((size_t)b * Sk + j) * Hkv + g) * D;
                     double* dvr = dv + (((size_t)b * Sk + j) * Hkv + g) * D;
                     double* dqr = dq + row * D;
                     for (int d = 0; d < D; ++d) {
-                        dqr[d] += scale * dz * bf16_to_double(krow[d]);
-                        dkr[d] += scale * dz * bf16_to_double(qrow[d]);
-                        dvr[d] += pj * dov[d];
+                        double kd = bf16_to_double(krow[d]), qd = bf16_to_double(qrow[d]), od = dov[d];
+                        if (magnitudes) {
+                            kd = fabs(kd);
+                            qd = fabs(qd);
+                            od = fabs(od);
+                        }
+                        dqr[d] += scale * dz * kd;
+                        dkr[d] += scale * dz * qd;
+                        dvr[d] += pj * od;
                     }
                     int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
                     if (r >= 0 && r < E) dprofiles[(((size_t)b * Hq + h) * Sq + i) * (size_t)E + r] = dz;

@@ -185,3 +185,33 @@ def test_row_without_keys_feeds_only_the_sink():
     dq, _, _, dp, ds = _bwd(x, dout, dlse)
     assert np.all(dq[1, 10] == 0) and np.all(dp[1, :, 10] == 0)
     np.testing.assert_array_equal(ds[1, 10], dlse.numpy()[1, 10])
+
+
+def test_row_range_keeps_later_rows_and_keys():
+    x = small(45, structure="packed", doc_min=3, doc_max=9)
+    dout, dlse = _upstream(x, 145)
+    full = _bwd(x, dout, dlse)
+    part = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                           positions=x["positions"], row_lo=17)
+    np.testing.assert_array_equal(part[0][:, 17:], full[0][:, 17:])
+    np.testing.assert_array_equal(part[3][:, :, 17:], full[3][:, :, 17:])
+    np.testing.assert_array_equal(part[4][:, 17:], full[4][:, 17:])
+    np.testing.assert_allclose(part[1][:, 17:], full[1][:, 17:], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(part[2][:, 17:], full[2][:, 17:], atol=1e-14, rtol=0)
+    assert np.all(part[0][:, :17] == 0)
+
+
+def test_magnitudes_bound_the_gradients():
+    x = small(46, window=7)
+    dout, dlse = _upstream(x, 146)
+    g = _bwd(x, dout, dlse)
+    m = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                        positions=x["positions"], window=7, magnitudes=True)
+    for a, b in zip(g, m):
+        assert np.all(np.abs(a) <= b * (1 + 1e-12) + 1e-300)
+    # with dout >= 0 every dv contribution is non-negative: the magnitude is the value
+    dpos = dout.abs()
+    gv = _bwd(x, dpos, dlse)[2]
+    mv = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dpos, dlse,
+                         positions=x["positions"], window=7, magnitudes=True)[2]
+    np.testing.assert_allclose(gv, mv, rtol=1e-12, atol=0)
