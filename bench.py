@@ -169,6 +169,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the gradients (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes (calibrates HBM counters)")
     args = ap.parse_args()
@@ -197,6 +199,8 @@ def main():
         sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(W.WORKLOADS) + sorted(W.FLEX_WORKLOADS)}")
     w = W.WORKLOADS[args.workload]
     x = W.generate(w)
+    if args.backward:
+        return bench_backward(args, w, x)
     cnt, pairs, flops, nbytes = algorithmic_work(x)
 
     dev = torch.device("cuda", 0)
@@ -275,6 +279,126 @@ def main():
                                  "frac": gbs / HBM_PEAK_GBS})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def backward_work(x):
+    """Algorithmic work of the gradients: 10 D flops per unmasked pair (q.k, dout.v, P^T dout,
+    dS k and dS^T q, 2 D each); bytes: q, k, v (bf16), the profile entries the forward used,
+    sink, out, lse, dout, dlse (fp32) read once; dq, dk, dv (fp32), the whole profile gradient
+    (dtype of profiles) and dsink written once."""
+    w = x["workload"]
+    cnt, pairs, _, _ = algorithmic_work(x)
+    flops = 10.0 * w.D * pairs
+    pb = 2 if str(w.profiles_dtype).endswith("bfloat16") else 4
+    rows = w.B * w.S * w.Hq
+    nbytes = (2 * rows * w.D + 2 * 2 * w.B * w.S * w.Hkv * w.D + used_profile_entries(x) * w.Hq * pb
+              + rows * 4 * (1 + w.D + 1 + w.D + 1)
+              + 4 * rows * w.D + 2 * 4 * w.B * w.S * w.Hkv * w.D + rows * w.E * pb + 4 * rows)
+    return cnt, pairs, flops, nbytes
+
+
+def backward_cpu_baseline(x, dout, dlse, target_s: float):
+    """The backward oracle as it stands, on the last rows of each sequence (the oracle's row
+    range), grown until the run takes about ``target_s`` seconds."""
+    import oracle
+    w = x["workload"]
+    cnt = allowed_counts(x)
+
+    def timed(n):
+        t0 = time.perf_counter()
+        oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                        positions=x["positions"], window=x["window"], row_lo=w.S - n)
+        return time.perf_counter() - t0
+
+    n = 8
+    t = timed(n)
+    while t < target_s / 8 and n < w.S:
+        n = min(w.S, n * 4)
+        t = timed(n)
+    if n < w.S and t < 0.75 * target_s:
+        n = int(min(w.S, max(n, n * target_s / max(t, 1e-9))))
+        t = timed(n)
+    pairs = int(cnt[:, w.S - n:].sum()) * w.Hq
+    return {"value": 10.0 * w.D * pairs / t / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"last {n} query rows of each of {w.B} sequence(s) (all {w.Hq} heads), {pairs} unmasked "
+                      f"pairs, {t:.1f} s wall, fp64, one thread"}
+
+
+def bench_backward(args, w, x):
+    """Gradients of the forward on workload ``w``: one step = one attn_bwd call (pre-pass, row
+    statistics and transposed copies, the dQ / profile-gradient kernel and the dK / dV kernel),
+    with the forward's out / lse and seeded upstream gradients already resident in HBM."""
+    import torch
+    from transformer_attention_03_amd import binding
+
+    cnt, pairs, flops, nbytes = backward_work(x)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = {k: (x[k].to(dev) if isinstance(x.get(k), torch.Tensor) else None)
+         for k in ("q", "k", "v", "profiles", "sink", "valid", "positions")}
+    gen = torch.Generator().manual_seed(4242)
+    dout_h = torch.randn(w.B, w.S, w.Hq, w.D, generator=gen)
+    dlse_h = torch.randn(w.B, w.S, w.Hq, generator=gen)
+    dout, dlse = dout_h.to(dev), dlse_h.to(dev)
+    out, lse = binding.attn_fwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"],
+                                positions=d["positions"], window=w.window)
+    grads = (torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.S, w.Hkv, w.D), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.S, w.Hkv, w.D), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hq, w.S, w.E), dtype=w.profiles_dtype, device=dev),
+             torch.empty((w.B, w.S, w.Hq), dtype=torch.float32, device=dev))
+    ws = torch.empty(max(16, binding.attn_bwd_workspace_size(w.B, w.S, w.S, w.Hq, w.Hkv, w.D)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.attn_bwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"], out, lse, dout, dlse,
+                         positions=d["positions"], window=w.window, grads=grads, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    if not all(bool(torch.isfinite(g.float()).all()) for g in grads):
+        sys.exit("non-finite gradient")
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    line = {
+        "metric": "bwd attention TFLOP/s (unmasked pairs, 10*D flops per pair) + % MFMA peak, 1 GPU",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} backward: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} E={w.E} "
+                               f"window={w.window} profiles={str(w.profiles_dtype).replace('torch.', '')}",
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
+                   "mfma": "bf16", "accumulate": "fp32"},
+        "unmasked_pairs": pairs,
+        "hbm_gbs_algorithmic": nbytes / (call_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_bwd call (pre-pass, prep, staging, bwd_dq_kernel, bwd_dkdv_kernel)",
+                     "kernel_ms": call_ms, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = backward_cpu_baseline(x, dout_h.double(), dlse_h.double(), args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -113,6 +113,61 @@ int attn_fwd(const void* q, const void* k, const void* v,
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace attn_bwd needs: the pre-pass summaries as for
+ * attn_fwd, then per query 8 bytes and per (query, head) row 8 bytes of row
+ * statistics, a bf16 copy of dout (B*Sq*Hq*D*2), K^T in whole 64-key tiles
+ * (B*Hkv*ceil(Sk/64)*64*D*2) and Q^T and dout^T in whole 32-query tiles
+ * (2 * B*Hq*ceil(Sq/32)*32*D*2); each part rounded up to 256 bytes.  Never
+ * fails; returns 0 for non-positive B.
+ */
+size_t attn_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+
+/*
+ * attn_bwd -- gradients of attn_fwd.  The page
+ * "nemo_automodel.components.models.inkling2.flex_attention" (module summary;
+ * class Inkling2FlexAttention) makes the per-query sinks differentiable and
+ * passes gradients to the captured profiles and through the returned
+ * log-sum-exp.  For a loss L with dout = dL/dout and dlse = dL/dlse, per row
+ * (b, i, h) with P_j = e^{z_j - lse} over the allowed keys j:
+ *
+ *   Delta  = <dout[b,i,h,:], out[b,i,h,:]>
+ *   dz_j   = P_j (<dout[b,i,h,:], v[b,j,g,:]> - Delta + dlse[b,i,h])
+ *   dq[b,i,h,:]  = head_dim^-0.5 sum_j dz_j k[b,j,g,:]
+ *   dk[b,j,g,:] += head_dim^-0.5 dz_j q[b,i,h,:]     (summed over rows and
+ *   dv[b,j,g,:] += P_j dout[b,i,h,:]                   the G heads of g)
+ *   dprofiles[b,h,i,r] = dz_j for the allowed key j at distance r < E, else 0
+ *   dsink[b,i,h] = e^{sink - lse} (dlse - Delta)      (0 where lse = -inf)
+ *
+ * Arguments q ... E as for attn_fwd (same masks, window, offset); the same
+ * tensors the forward saw must be passed.
+ *   out, lse   the forward's outputs for these inputs (fp32, [B,Sq,Hq,D] and
+ *              [B,Sq,Hq]); out 16-byte aligned
+ *   dout       [B, Sq, Hq, D] fp32, 16-byte aligned (rounded to bf16 for the
+ *              matrix products)
+ *   dlse       [B, Sq, Hq] fp32, or NULL (zero)
+ *   dq         [B, Sq, Hq, D] fp32, 16-byte aligned, written
+ *   dk, dv     [B, Sk, Hkv, D] fp32, 16-byte aligned, written
+ *   dprofiles  [B, Hq, Sq, E] in profiles_dtype, written in full (zeros
+ *              included)
+ *   dsink      [B, Sq, Hq] fp32, written
+ *   workspace  at least attn_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D) bytes,
+ *              16-byte aligned; contents on entry are ignored
+ * Inputs at tokens that are not valid (q, k, v, dout rows) never reach an
+ * output other than their own row's out-of-mask zeros.  The products run in
+ * bf16 MFMA with fp32 accumulation: P and dz are rounded to bf16 for dv / dq /
+ * dk, dout for dz and dv.
+ */
+int attn_bwd(const void* q, const void* k, const void* v,
+             const void* profiles, int profiles_dtype,
+             const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+             const int32_t* positions, const int32_t* key_positions,
+             int64_t window, int64_t query_offset,
+             int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+             const float* out, const float* lse, const float* dout, const float* dlse,
+             float* dq, float* dk, float* dv, void* dprofiles, float* dsink,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_plan -- the scheduler pre-pass alone: writes the per-tile mask
  * summaries (document start columns and real-token counts of every 32-token
  * query block and 64-key tile) into `workspace`.  The summaries depend only on

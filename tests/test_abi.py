@@ -133,3 +133,40 @@ def test_flex_workspace_size():
     assert binding.flex_attn_workspace_size(2, 100, 300, 1, 64) == (binding.attn_fwd_workspace_size(2, 100, 300, 1, 64)
                                                                      + 1024 + 768)
     assert binding.flex_attn_workspace_size(0, 64, 64, 2, 128) == 0
+
+
+def bwd_call(**over):
+    a = dict(q=A, k=A, v=A, profiles=A, pdt=0, sink=A, valid=A, key_valid=None, positions=None,
+             key_positions=None, window=0, qoff=0, B=1, Sq=64, Sk=64, Hq=4, Hkv=2, D=128, E=16,
+             out=A, lse=A, dout=A, dlse=None, dq=A, dk=A, dv=A, dprof=A, dsink=A, ws=A, wsb=1 << 20,
+             stream=None)
+    a.update(over)
+    lib = binding.load()
+    return lib.attn_bwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["profiles"]), a["pdt"], P(a["sink"]),
+                        P(a["valid"]), P(a["key_valid"]), P(a["positions"]), P(a["key_positions"]),
+                        a["window"], a["qoff"], a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"], a["E"],
+                        P(a["out"]), P(a["lse"]), P(a["dout"]), P(a["dlse"]), P(a["dq"]), P(a["dk"]),
+                        P(a["dv"]), P(a["dprof"]), P(a["dsink"]), P(a["ws"]), a["wsb"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dprof=None), 1),
+    (dict(dsink=None), 1), (dict(lse=None), 1), (dict(valid=None), 1), (dict(Sk=100), 1),
+    (dict(Hq=6, Hkv=4), 2), (dict(E=0), 2), (dict(Sq=-1), 2), (dict(D=96), 3), (dict(pdt=5), 3),
+    (dict(dout=A + 8), 4), (dict(dk=A + 4), 4), (dict(dprof=A + 2), 4), (dict(dsink=A + 2), 4),
+    (dict(ws=None), 5), (dict(wsb=232447), 5),
+])
+def test_bwd_host_validation(over, status):
+    assert bwd_call(**over) == status
+    assert binding.attn_last_error() != ""
+
+
+def test_bwd_workspace_size():
+    # summaries 256 + 256; per query 8 B; per row 8 B; bf16 dout; K^T in 64-key tiles; Q^T and dO^T
+    # in 32-query tiles; each rounded up to 256 B
+    assert binding.attn_bwd_workspace_size(1, 64, 64, 4, 2, 128) == (512 + 512 + 2048 + 65536 + 32768
+                                                                     + 2 * 65536)
+    assert bwd_call(wsb=232448, ws=None) == 5
+    assert binding.attn_bwd_workspace_size(0, 64, 64, 4, 2, 128) == 0
+    # bf16 profile gradients need only 2-byte alignment: the workspace check is what stops this call
+    assert bwd_call(pdt=1, profiles=A + 2, dprof=A + 2, wsb=8) == 5

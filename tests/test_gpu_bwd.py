@@ -1,0 +1,242 @@
+"""GPU parity of the backward (``attn_bwd``) against the fp64 oracle (``oracle.attn_bwd``).
+
+Tolerance, derived from the arithmetic of the HIP path: the products run in bf16
+MFMA with fp32 accumulation, and dout, P and dz are rounded to bf16 (relative
+error <= 2^-9 each) before they enter a product.  Each gradient entry is a sum
+of terms that carry at most two such roundings, so its error is at most about
+2^-8 times the sum of the absolute values of its terms; fp32 accumulation adds
+at most n 2^-24 of the same sum (n <= 2^15 terms here).  The bar is therefore
+
+    |gpu - oracle| <= 2^-7 * M
+
+with M the oracle's magnitude of that entry (``magnitudes=True``: the sum of
+absolute contributions).  bf16 profile gradients add half a bf16 unit in the
+last place of the value (the output rounding).  Masks are exact: the oracle's
+exact zeros of dprofiles (no key at that distance), of dq at rows that are not
+real and of dk / dv at keys that are not real must be exact zeros.
+
+The backward is given the oracle's out and lse (rounded to fp32), which isolates
+it; one case feeds it the GPU forward's instead.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import announce
+from transformer_attention_03_amd import binding
+from transformer_attention_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+REL = 2.0 ** -7
+NAMES = ("dq", "dk", "dv", "dprofiles", "dsink")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.load()
+    yield
+
+
+def _upstream(x, seed, with_dlse=True, Sq=None):
+    g = torch.Generator().manual_seed(seed)
+    B, S, Hq, D = x["q"].shape
+    dout = torch.randn(B, S, Hq, D, generator=g, dtype=torch.float32)
+    dlse = torch.randn(B, S, Hq, generator=g, dtype=torch.float32) if with_dlse else None
+    return dout, dlse
+
+
+def _okw(x):
+    return dict(key_valid=x.get("key_valid"), positions=x.get("positions"), key_positions=x.get("key_positions"),
+                window=x.get("window"), query_offset=x.get("query_offset", 0))
+
+
+def _dev(t):
+    return None if t is None else t.cuda()
+
+
+def run_gpu_bwd(x, out, lse, dout, dlse):
+    kw = _okw(x)
+    g = binding.attn_bwd(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["profiles"].cuda(), x["sink"].cuda(),
+                         x["valid"].cuda(), out.cuda(), lse.cuda(), dout.cuda(), _dev(dlse),
+                         key_valid=_dev(kw["key_valid"]), positions=_dev(kw["positions"]),
+                         key_positions=_dev(kw["key_positions"]), window=kw["window"],
+                         query_offset=kw["query_offset"])
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in g]
+
+
+def oracle_bwd(x, dout, dlse, row_lo=0, magnitudes=False):
+    return oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout.double(),
+                           None if dlse is None else dlse.double(), row_lo=row_lo, magnitudes=magnitudes,
+                           **_okw(x))
+
+
+def oracle_fwd(x):
+    out, lse, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], **_okw(x))
+    return torch.from_numpy(out).float(), torch.from_numpy(lse).float()
+
+
+def assert_grads_close(got, ref, mag, what, bf16_prof=False, sel=None):
+    for n, a, r, m in zip(NAMES, got, ref, mag):
+        if sel is not None and sel.get(n) is not None:
+            a, r, m = a[sel[n]], r[sel[n]], m[sel[n]]
+        bound = REL * m + 1e-30          # (+ fp32 underflow of weights below 2^-126)
+        if n == "dprofiles" and bf16_prof:
+            bound = bound + np.abs(r) * 2.0 ** -9
+        err = np.abs(a - r)
+        bad = ~(err <= bound)
+        assert not bad.any(), (f"{what} {n}: {int(bad.sum())} entries off, first {np.argwhere(bad)[:3].tolist()}, "
+                               f"max err {np.nanmax(err):.3g}, max err/M {np.nanmax(err / np.maximum(m, 1e-300)):.3g}")
+        zero = (r == 0) & (m == 0)
+        assert np.all(a[zero] == 0), f"{what} {n}: nonzero where no term exists"
+
+
+SMALL = {
+    "single_G4_D128": dict(B=1, S=300, Hq=8, Hkv=2, D=128, E=48, structure="single", seed=301),
+    "packed_window_invalid": dict(B=2, S=260, Hq=8, Hkv=2, D=128, E=40, window=50, structure="packed",
+                                  doc_min=20, doc_max=120, invalid_tail=9, seed=302),
+    "window_G8": dict(B=1, S=200, Hq=16, Hkv=2, D=128, E=64, window=70, structure="single", seed=303),
+    "tailpad_G1_D64": dict(B=2, S=170, Hq=3, Hkv=3, D=64, E=30, structure="tail_pad", max_tail_pad=40, seed=304),
+    "bf16_profiles": dict(B=1, S=230, Hq=8, Hkv=2, D=128, E=100, structure="packed", doc_min=30, doc_max=150,
+                          profiles_dtype=torch.bfloat16, sink_std=2.0, seed=305),
+    "extent_1": dict(B=1, S=140, Hq=4, Hkv=1, D=128, E=1, structure="single", seed=306),
+    "extent_beyond_S": dict(B=1, S=150, Hq=4, Hkv=2, D=64, E=400, structure="packed", doc_min=10, doc_max=90,
+                            seed=307),
+    "G2_D64_window": dict(B=1, S=333, Hq=4, Hkv=2, D=64, E=64, window=100, structure="single", seed=308),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bwd_small_parity(name):
+    c = dict(SMALL[name])
+    x = W.custom(**c)
+    dout, dlse = _upstream(x, c["seed"] + 1000, with_dlse=(name != "extent_1"))
+    announce(f"bwd {name}: q={tuple(x['q'].shape)} E={c['E']}")
+    out, lse = oracle_fwd(x)
+    got = run_gpu_bwd(x, out, lse, dout, dlse)
+    ref = oracle_bwd(x, dout, dlse)
+    mag = oracle_bwd(x, dout, dlse, magnitudes=True)
+    assert_grads_close(got, ref, mag, name, bf16_prof=x["profiles"].dtype == torch.bfloat16)
+
+
+def test_bwd_garbage_at_invalid_tokens_stays_out():
+    """NaN in q / k / v / dout at tokens that are not real reaches no output."""
+    c = dict(SMALL["packed_window_invalid"])
+    x = W.custom(**c)
+    dout, dlse = _upstream(x, 2302)
+    out, lse = oracle_fwd(x)
+    ref = oracle_bwd(x, dout, dlse)
+    mag = oracle_bwd(x, dout, dlse, magnitudes=True)
+    bad = ~x["valid"]
+    y = dict(x)
+    for n in ("q", "k", "v"):
+        t = x[n].clone()
+        t[bad] = float("nan")
+        y[n] = t
+    dn = dout.clone()
+    dn[bad] = float("nan")
+    announce("bwd NaN at invalid tokens")
+    got = run_gpu_bwd(y, out, lse, dn, dlse)
+    assert_grads_close(got, ref, mag, "nan_invalid")
+
+
+def test_bwd_query_slice_with_offset():
+    """Queries are a slice [a, a + n) of the sequence (query_offset = a), keys the whole sequence."""
+    c = dict(B=1, S=320, Hq=8, Hkv=2, D=128, E=64, structure="packed", doc_min=40, doc_max=200, seed=309)
+    x = W.custom(**c)
+    a, n = 97, 130
+    y = dict(x)
+    y["q"] = x["q"][:, a:a + n].contiguous()
+    y["profiles"] = x["profiles"][:, :, a:a + n].contiguous()
+    y["sink"] = x["sink"][:, a:a + n].contiguous()
+    y["valid"] = x["valid"][:, a:a + n].contiguous()
+    y["positions"] = x["positions"][:, a:a + n].contiguous()
+    y["key_valid"] = x["valid"]
+    y["key_positions"] = x["positions"]
+    y["query_offset"] = a
+    dout, dlse = _upstream(y, 2309)
+    announce(f"bwd query slice a={a} n={n}")
+    out, lse = oracle_fwd(y)
+    got = run_gpu_bwd(y, out, lse, dout, dlse)
+    ref = oracle_bwd(y, dout, dlse)
+    mag = oracle_bwd(y, dout, dlse, magnitudes=True)
+    assert_grads_close(got, ref, mag, "query_slice")
+
+
+def test_bwd_fed_by_gpu_forward():
+    c = dict(SMALL["single_G4_D128"])
+    x = W.custom(**c)
+    dout, dlse = _upstream(x, 2310)
+    announce("bwd after the GPU forward")
+    out, lse = binding.attn_fwd(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["profiles"].cuda(),
+                                x["sink"].cuda(), x["valid"].cuda(), positions=x["positions"].cuda())
+    got = run_gpu_bwd(x, out.cpu(), lse.cpu(), dout, dlse)
+    ref = oracle_bwd(x, dout, dlse)
+    mag = oracle_bwd(x, dout, dlse, magnitudes=True)
+    assert_grads_close(got, ref, mag, "after_gpu_forward")
+
+
+def test_bwd_no_keys_and_no_queries():
+    """Sk = 0 keys: dq = 0, dprofiles = 0, dsink = dlse; B * Sq = 0: dk = dv = 0."""
+    x = W.custom(B=1, S=40, Hq=4, Hkv=2, D=64, E=8, seed=310)
+    dout, dlse = _upstream(x, 2311)
+    q, sink, valid = x["q"].cuda(), x["sink"].cuda(), x["valid"].cuda()
+    kz = torch.empty(1, 0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    kvz = torch.empty(1, 0, dtype=torch.bool, device="cuda")
+    out = torch.zeros(1, 40, 4, 64, device="cuda")
+    lse = sink.clone()
+    announce("bwd Sk = 0")
+    dq, dk, dv, dp, ds = binding.attn_bwd(q, kz, kz, x["profiles"].cuda(), sink, valid, out, lse, dout.cuda(),
+                                          dlse.cuda(), key_valid=kvz, positions=x["positions"].cuda(),
+                                          key_positions=torch.empty(1, 0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dp == 0)
+    torch.testing.assert_close(ds.cpu(), dlse, rtol=0, atol=0)
+    announce("bwd Sq = 0")
+    qz = torch.empty(1, 0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    k, v = x["k"].cuda(), x["v"].cuda()
+    dk = torch.full((1, 40, 2, 64), 7.0, device="cuda")
+    dv = torch.full((1, 40, 2, 64), 7.0, device="cuda")
+    empty = torch.empty(1, 0, 4, device="cuda")
+    binding.attn_bwd(qz, k, v, torch.empty(1, 4, 0, 8, device="cuda"), empty, torch.empty(1, 0, dtype=torch.bool,
+                     device="cuda"), torch.empty(1, 0, 4, 64, device="cuda"), empty, torch.empty(1, 0, 4, 64,
+                     device="cuda"), None, key_valid=valid, key_positions=x["positions"].cuda(),
+                     grads=(torch.empty(1, 0, 4, 64, device="cuda"), dk, dv, torch.empty(1, 4, 0, 8, device="cuda"),
+                            torch.empty(1, 0, 4, device="cuda")))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_bwd_full_size_last_rows():
+    """The benchmark's full-causal workload in the launch configuration it times: the last 48
+    query rows (dq, dprofiles, dsink) and the last 48 keys (dk, dv, which only those rows see)
+    against the oracle."""
+    w = W.WORKLOADS["full_causal_8k"]
+    x = W.generate(w)
+    S, n = w.S, 48
+    lo = S - n
+    dout, dlse = _upstream(x, 2400)
+    announce(f"bwd full size {w.name}: last {n} rows")
+    d = {k: (x[k].cuda() if isinstance(x.get(k), torch.Tensor) else None) for k in ("q", "k", "v", "profiles",
+                                                                                   "sink", "valid", "positions")}
+    out, lse = binding.attn_fwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"],
+                                positions=d["positions"], window=w.window)
+    rows = torch.arange(lo, S, dtype=torch.int64)
+    o_r, l_r, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"],
+                                  positions=x["positions"], window=w.window, rows=rows)
+    out[0, lo:] = torch.from_numpy(o_r).float().cuda()
+    lse[0, lo:] = torch.from_numpy(l_r).float().cuda()
+    g = binding.attn_bwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"], out, lse, dout.cuda(),
+                         dlse.cuda(), positions=d["positions"], window=w.window)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy().astype(np.float64) for t in g]
+    ref = oracle_bwd(x, dout, dlse, row_lo=lo)
+    mag = oracle_bwd(x, dout, dlse, row_lo=lo, magnitudes=True)
+    sel = {"dq": (slice(None), slice(lo, S)), "dk": (slice(None), slice(lo, S)), "dv": (slice(None), slice(lo, S)),
+           "dprofiles": (slice(None), slice(None), slice(lo, S)), "dsink": (slice(None), slice(lo, S))}
+    assert_grads_close(got, ref, mag, w.name, sel=sel)

@@ -25,6 +25,7 @@ STATUS = {0: "INKATTN_OK", 1: "INKATTN_ERR_NULL", 2: "INKATTN_ERR_SHAPE", 3: "IN
 # Every symbol include/inkattn.h declares.
 EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
            "attn_debug_counts", "attn_debug_tiles", "flex_attn_workspace_size", "flex_attn_fwd",
+           "attn_bwd_workspace_size", "attn_bwd",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
 _lock = threading.Lock()
@@ -66,6 +67,11 @@ def load() -> ctypes.CDLL:
             lib.flex_attn_fwd.restype = I
             lib.flex_attn_fwd.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, ctypes.c_float,
                                           I, I, I, I, I, I, P, P, P, SZ, P]
+            lib.attn_bwd_workspace_size.restype = SZ
+            lib.attn_bwd_workspace_size.argtypes = [I, I, I, I, I, I]
+            lib.attn_bwd.restype = I
+            lib.attn_bwd.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64, I, I, I, I, I, I, I,
+                                     P, P, P, P, P, P, P, P, P, P, SZ, P]
             lib.attn_status_string.restype = ctypes.c_char_p
             lib.attn_status_string.argtypes = [I]
             lib.attn_last_error.restype = ctypes.c_char_p
@@ -185,6 +191,72 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.
     _check(load().attn_fwd(*args), "attn_fwd")
     del keep
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(load().attn_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.Tensor,
+             sink: torch.Tensor, valid: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, dlse: Optional[torch.Tensor] = None,
+             key_valid: Optional[torch.Tensor] = None, positions: Optional[torch.Tensor] = None,
+             key_positions: Optional[torch.Tensor] = None, window: Optional[int] = None,
+             query_offset: int = 0, grads: Optional[tuple] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of :func:`attn_fwd` for upstream ``dout [B,Sq,Hq,D]`` fp32 and ``dlse [B,Sq,Hq]``
+    fp32 (None: zero), given the forward's ``out`` and ``lse``.  Returns ``(dq, dk, dv, dprofiles,
+    dsink)``: dq / dk / dv fp32 in the layouts of q / k / v, dprofiles in the dtype and layout of
+    profiles, dsink fp32 [B,Sq,Hq].  ``grads`` may hold preallocated outputs in that order."""
+    dev = q.device
+    q = _dev(q, "q", (torch.bfloat16,), None)
+    k = _dev(k, "k", (torch.bfloat16,), dev)
+    v = _dev(v, "v", (torch.bfloat16,), dev)
+    profiles = _dev(profiles, "profiles", (torch.float32, torch.bfloat16), dev)
+    sink = _dev(sink, "sink", (torch.float32,), dev)
+    out = _dev(out, "out", (torch.float32,), dev)
+    lse = _dev(lse, "lse", (torch.float32,), dev)
+    dout = _dev(dout, "dout", (torch.float32,), dev)
+    dlse = _dev(dlse, "dlse", (torch.float32,), dev)
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or profiles.dim() != 4:
+        raise ValueError("q, k, v and profiles must be 4-d")
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    E = profiles.shape[3]
+    expect = {"k": (k, (B, Sk, Hkv, D)), "v": (v, (B, Sk, Hkv, D)), "profiles": (profiles, (B, Hq, Sq, E)),
+              "sink": (sink, (B, Sq, Hq)), "out": (out, (B, Sq, Hq, D)), "lse": (lse, (B, Sq, Hq)),
+              "dout": (dout, (B, Sq, Hq, D)), "dlse": (dlse, (B, Sq, Hq)), "valid": (valid_u8, (B, Sq)),
+              "key_valid": (kvalid_u8, (B, Sk)), "positions": (pos, (B, Sq)), "key_positions": (kpos, (B, Sk))}
+    for name, (t, shape) in expect.items():
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
+    if grads is None:
+        grads = (torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=dev),
+                 torch.empty((B, Sk, Hkv, D), dtype=torch.float32, device=dev),
+                 torch.empty((B, Sk, Hkv, D), dtype=torch.float32, device=dev),
+                 torch.empty((B, Hq, Sq, E), dtype=profiles.dtype, device=dev),
+                 torch.empty((B, Sq, Hq), dtype=torch.float32, device=dev))
+    dq, dk, dv, dprof, dsink = grads
+    dq = _dev(dq, "dq", (torch.float32,), dev)
+    dk = _dev(dk, "dk", (torch.float32,), dev)
+    dv = _dev(dv, "dv", (torch.float32,), dev)
+    dprof = _dev(dprof, "dprofiles", (profiles.dtype,), dev)
+    dsink = _dev(dsink, "dsink", (torch.float32,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D), 16), dtype=torch.uint8,
+                                device=dev)
+    pdt = INKATTN_BF16 if profiles.dtype == torch.bfloat16 else INKATTN_F32
+    rc = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(profiles), pdt, _ptr(sink), _ptr(valid_u8),
+                         _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), 0 if window is None else int(window),
+                         int(query_offset), B, Sq, Sk, Hq, Hkv, D, E, _ptr(out), _ptr(lse), _ptr(dout),
+                         _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dprof), _ptr(dsink), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv, dprof, dsink
 
 
 def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=None, key_positions=None,

@@ -12,7 +12,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "inkattn.hip")
+SRCS = [os.path.join(PKG, "csrc", "inkattn.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 LIB = os.path.join(PKG, "libinkattn.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
@@ -27,7 +27,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device-only feature flag: drop that notice
     noise = "'-packed-fp32-ops' is not a recognized feature"

@@ -1,0 +1,985 @@
+// attn_bwd.hip -- gradients of the learned-relative grouped-query attention
+// with per-query sinks, for AMD CDNA4 (gfx950 / MI355X).
+//
+// Operation: the backward of the forward in inkattn.hip.  The page
+// "nemo_automodel.components.models.inkling2.flex_attention" (module summary
+// and class Inkling2FlexAttention) makes the per-query sinks differentiable
+// and lets gradients reach the captured profiles and flow in through the
+// returned log-sum-exp.  With z_ij = scale <q_i, k_j> + bias_ij the allowed
+// logits, P_ij = e^{z_ij - lse_i} the weights of the forward (lse includes the
+// sink sigma_i) and upstream gradients dout, dlse:
+//   Delta_i  = <dout_i, out_i>
+//   dz_ij    = P_ij (<dout_i, v_j> - Delta_i + dlse_i)
+//   dq_i     = scale sum_j dz_ij k_j     dk_j = scale sum_i dz_ij q_i
+//   dv_j     = sum_i P_ij dout_i
+//   dprofiles[b,h,i,r] = dz_ij for the key j at distance r, 0 where none is
+//   dsink_i  = e^{sigma_i - lse_i} (dlse_i - Delta_i)
+//
+// Structure of one call:
+//   1. summarize_kernel (the forward's pre-pass): mask summaries per tile.
+//   2. bwd_prep_kernel: per row Delta - dlse, dsink and lse * log2(e); dout
+//      rounded to bf16 rows (0 on rows that are not real); per query its
+//      global column (-1 if not real) and document start column.
+//   3. bwd_stage_kernel: transposed bf16 tiles the products consume as their
+//      A operands: K^T per 64-key tile, Q^T and dO^T per 32-query tile, each
+//      tile's tokens in the order of the accumulator registers they meet.
+//   4. bwd_dq_kernel (query-parallel, one wave per (query head, 32 queries),
+//      keys on MFMA M as in the forward): per 64-key tile S^T = K Q^T and
+//      dP^T = V dO^T, then P and dS from the saved lse, dS written to the
+//      profile gradient row (a contiguous run per query), dQ^T += K^T dS^T.
+//      Every entry of a query's profile-gradient row is written by its wave:
+//      zeros where no tile it visits puts a value.
+//   5. bwd_dkdv_kernel (key-parallel, one wave per 32 keys, queries on MFMA
+//      M): per (32-query block, head of the group) S = Q K^T, dP = dO V^T,
+//      P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+// Products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
+// rounded to bf16 for the products that consume them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+#include "inkattn.h"
+
+namespace {
+
+using namespace inkattn;
+
+constexpr int BW_WAVES = 4;          // waves per workgroup of both gradient kernels
+constexpr int KV_KEYS = 32 * BW_WAVES;   // keys per dK / dV workgroup
+
+struct BwdParams {
+    const __bf16* q;               // [B, Sq, Hq, D]
+    const __bf16* k;               // [B, Sk, Hkv, D]
+    const __bf16* v;               // [B, Sk, Hkv, D]
+    const void* profiles;          // [B, Hq, Sq, E] fp32 or bf16
+    const float* sink;             // [B, Sq, Hq]
+    const float* out;              // [B, Sq, Hq, D]
+    const float* lse;              // [B, Sq, Hq]
+    const float* dout;             // [B, Sq, Hq, D]
+    const float* dlse;             // [B, Sq, Hq] or NULL
+    const uint8_t* valid;          // [B, Sq]
+    const uint8_t* key_valid;      // [B, Sk]
+    const int32_t* positions;      // [B, Sq] or NULL (global column)
+    const TileSummary* qsum;       // [B, nQB]
+    const TileSummary* ksum;       // [B, nKT]
+    const int* kanchor;            // [B, nKT * 64] key start column, INT_MIN if not real
+    int2* qinfo;                   // [B, Sq] {global column or -1, document start column}
+    float2* rowstat;               // [B, Hq, Sq] {lse * log2(e) (0 when lse = -inf), Delta - dlse}
+    __bf16* dob;                   // [B, Sq, Hq, D] bf16 dout, 0 on rows that are not real
+    __bf16* kt;                    // [B, Hkv, nKT, D, 64] K^T tiles
+    __bf16* qt;                    // [B, Hq, nQB, D, 32] Q^T tiles
+    __bf16* dot;                   // [B, Hq, nQB, D, 32] dO^T tiles
+    float* dq;                     // [B, Sq, Hq, D]
+    float* dk;                     // [B, Sk, Hkv, D]
+    float* dv;                     // [B, Sk, Hkv, D]
+    void* dprofiles;               // [B, Hq, Sq, E], dtype of profiles
+    float* dsink;                  // [B, Sq, Hq]
+    int B, Sq, Sk, Hq, Hkv, G, E;
+    int window;                    // <= 0: none
+    int qoff;
+    int hpw, tpw, nchunk, nQG;     // dQ workgroup shape (as the forward's)
+    int nQB, nKT, nKB;
+    float scale;                   // head_dim^-0.5
+    float c_log2;                  // scale * log2(e)
+};
+
+// Element order of the staged transposed tiles.  Slot 8 hh + t of each
+// 16-token step holds token 8 (t / 4) + 4 hh + ((t % 4) ^ X): X = 3 for the
+// key tiles (the dQ kernel's S^T rows run through the keys in groups of four
+// reversed, as in the forward), X = 0 for the query tiles (the dK / dV
+// kernel's S rows are the queries in order).
+__device__ __forceinline__ int stage_token(int slot, int X)
+{
+    const int sg = slot >> 3, t = slot & 7;
+    return 16 * (sg >> 1) + 8 * (t >> 2) + 4 * (sg & 1) + ((t & 3) ^ X);
+}
+
+// XOR swizzle of the 16-byte chunks of a staged row of D bf16 (row pitch
+// 2 D bytes): 16 consecutive rows read at one logical chunk hit 16 distinct
+// groups of 4 banks.
+template <int D> __device__ __forceinline__ int row_swz(int r)
+{
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics, bf16 dout, query descriptors.  TPR = D / 4 threads per
+// (batch row, query, head) row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p)
+{
+    constexpr int TPR = D / 4;
+    const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;   // (b Sq + i) Hq + h
+    const int t = threadIdx.x % TPR;
+    if (row >= (long long)p.B * p.Sq * p.Hq) return;   // a row's threads leave together
+    const int h = (int)(row % p.Hq);
+    const long long bi = row / p.Hq;
+    const int i = (int)(bi % p.Sq);
+    const int b = (int)(bi / p.Sq);
+    const bool real = p.valid[bi] != 0;
+    const f32x4 go = *(const f32x4*)(p.dout + row * D + 4 * t);
+    const f32x4 o = *(const f32x4*)(p.out + row * D + 4 * t);
+    float dot = go[0] * o[0] + go[1] * o[1] + go[2] * o[2] + go[3] * o[3];
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, TPR);
+    if (!real) dot = 0.0f;   // a row that is not real has out = 0; its dout is ignored
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = real ? (__bf16)go[e] : (__bf16)0.0f;   // round to nearest even
+    *(bf16x4*)(p.dob + row * D + 4 * t) = w;
+    if (t == 0) {
+        const float L = p.lse[row];
+        const float sg = p.sink[row];
+        const float dl = p.dlse ? p.dlse[row] : 0.0f;
+        const bool fin = L > -INFINITY;
+        p.dsink[row] = fin ? expf(sg - L) * (dl - dot) : 0.0f;
+        p.rowstat[((long long)b * p.Hq + h) * p.Sq + i] = make_float2(fin ? L * LOG2E : 0.0f, dot - dl);
+        if (h == 0) {
+            const int gi = p.qoff + i;
+            p.qinfo[bi] = make_int2(real ? gi : -1, real ? (p.positions ? gi - p.positions[bi] : 0) : 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed bf16 tiles: one workgroup of (T / 8) (D / 8) threads per (batch
+// row, head, T-token tile).  Thread (slot group sg, dim chunk dc) loads the 8
+// tokens of slots 8 sg .. 8 sg + 7 at dims 8 dc .. 8 dc + 7 (fp32 sources are
+// rounded to bf16, nearest even), transposes the 8 x 8 block in registers and
+// writes 8 rows of 16 bytes.  Tokens that are not real, and the padding past
+// S, are written as 0.
+// ---------------------------------------------------------------------------
+template <int D, int T, int X, bool F32>
+__global__ __launch_bounds__((T / 8) * (D / 8)) void bwd_stage_kernel(const void* __restrict__ src,
+                                                                     const uint8_t* __restrict__ real, int S,
+                                                                     int H, int nT, long long bs, long long ts,
+                                                                     long long hs, __bf16* __restrict__ dst)
+{
+    constexpr int CH = D / 8;
+    const int tile = blockIdx.x;              // (b H + h) nT + tt
+    const int tt = tile % nT;
+    const int h = (tile / nT) % H;
+    const int b = tile / (nT * H);
+    const int sg = threadIdx.x / CH, dc = threadIdx.x % CH;
+    bf16x8 rows[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int j = tt * T + stage_token(8 * sg + u, X);
+        bf16x8 y = bf16x8{};
+        if (j < S && real[(size_t)b * S + j]) {
+            const long long off = b * bs + j * ts + h * hs + 8 * dc;
+            if constexpr (F32) {
+                const f32x4 lo = *(const f32x4*)((const float*)src + off);
+                const f32x4 hi = *(const f32x4*)((const float*)src + off + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = (__bf16)lo[e];
+                    y[4 + e] = (__bf16)hi[e];
+                }
+            } else {
+                y = *(const bf16x8*)((const __bf16*)src + off);
+            }
+        }
+        rows[u] = y;
+    }
+    __bf16* d = dst + (size_t)tile * D * T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        bf16x8 o;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = rows[u][e];
+        *(bf16x8*)(d + (8 * dc + e) * T + 8 * sg) = o;
+    }
+}
+
+// Per-workgroup list of live tiles, built in rounds of NSCHED candidates (one
+// per thread) between barriers.  An entry is (candidate - base) in bits 0..15
+// and a 2-bit class per wave group in bits 16 + 2 x.
+template <int NSCHED>
+struct Schedule {
+    int* list;     // NSCHED entries + one count per wave
+    int base, n, i;
+};
+
+// Builds the round of candidates base .. base + NSCHED - 1 (classify returns
+// the entry's class bits, 0 for a dead candidate, or -1 past the end).
+template <int NSCHED, typename F>
+__device__ __forceinline__ void build_round(Schedule<NSCHED>& s, F classify)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int code = classify(s.base + tid);
+    const bool live = code > 0;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(live);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    __syncthreads();                                   // the previous round's entries are read
+    if (lane == 0) s.list[NSCHED + wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0, total = 0;
+    for (int w = 0; w < NSCHED / 64; ++w) {
+        const int cw = s.list[NSCHED + w];
+        off += w < wave ? cw : 0;
+        total += cw;
+    }
+    if (live) s.list[off + before] = (code << 16) | tid;
+    __syncthreads();
+    s.n = __builtin_amdgcn_readfirstlane(total);
+    s.i = 0;
+}
+
+// Next live entry (candidate index and class bits), or {-1, 0} at the end.
+template <int NSCHED, typename F>
+__device__ __forceinline__ int2 next_entry(Schedule<NSCHED>& s, int last, F classify)
+{
+    while (s.i >= s.n && s.base <= last) {
+        build_round(s, classify);
+        s.base += NSCHED;
+    }
+    if (s.i < s.n) {
+        const unsigned w = (unsigned)__builtin_amdgcn_readfirstlane(s.list[s.i]);
+        ++s.i;
+        return make_int2(s.base - NSCHED + (int)(w & 0xFFFFu), (int)(w >> 16));
+    }
+    return make_int2(-1, 0);
+}
+
+// Bias entry of a (query row, distance r) as float: 0 outside [0, E).
+template <bool PB>
+__device__ __forceinline__ float bias_at(const void* prow, int r, int E)
+{
+    if ((unsigned)r >= (unsigned)E) return 0.0f;
+    if constexpr (PB) return (float)((const __bf16*)prow)[r];
+    else return ((const float*)prow)[r];
+}
+
+template <bool PB>
+__device__ __forceinline__ void store_grad(void* prow, int r, float x)
+{
+    if constexpr (PB) ((__bf16*)prow)[r] = (__bf16)x;
+    else ((float*)prow)[r] = x;
+}
+
+// ---------------------------------------------------------------------------
+// dQ and the profile gradients.  One workgroup of 4 waves per (batch row, K/V
+// head, head chunk, group of 32-query blocks), the forward's decomposition;
+// wave = (query head, 32-query block), lane = (query qi, wave half hh).
+// ---------------------------------------------------------------------------
+template <int D, bool PB>
+__global__ __launch_bounds__(64 * BW_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdParams p)
+{
+    constexpr int NW = BW_WAVES;
+    constexpr int NKK = D / 16;              // k-steps over D
+    constexpr int NDB = D / 32;              // 32-row blocks of dQ^T
+    constexpr int CH = D / 8;                // 16-byte chunks per row
+    constexpr int TBYTES = BN * D * 2;       // one K, V or K^T tile
+    constexpr int K_OFF = 0, V_OFF = TBYTES, KT_OFF = 2 * TBYTES, CA_OFF = 3 * TBYTES;
+    constexpr int STAGE = 3 * TBYTES + BN * 4;
+    constexpr int NSCHED = 64 * NW;
+    constexpr int SCHED_OFF = 2 * STAGE;
+    constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
+    constexpr int CPT = BN * CH / (64 * NW);  // 16-byte chunks per thread of one K (or V, K^T) tile
+    static_assert(CPT >= 1 && BN * CH % (64 * NW) == 0, "tile chunks must divide among threads");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qi = lane & 31, hh = lane >> 5;
+
+    int idx = blockIdx.x;
+    const int ngroups = p.Hkv * p.nchunk;
+    const int hgi = idx % ngroups; idx /= ngroups;
+    const int b = idx % p.B; idx /= p.B;
+    const int qg = p.nQG - 1 - idx;
+    const int g = hgi / p.nchunk;
+    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + wave % p.hpw;
+    const int qb = qg * p.tpw + wave / p.hpw;
+    const int qb_first = qg * p.tpw;
+    const int qb_last = min(p.nQB - 1, qb_first + p.tpw - 1);
+    const int i0 = qb * BM;
+    const int i = i0 + qi;
+    const bool qin = qb < p.nQB && i < p.Sq;
+    const int gi = p.qoff + i;
+    const unsigned wlim = p.window > 0 ? (unsigned)p.window : 0x80000000u;
+
+    int2 qinf = make_int2(-1, 0);
+    float2 rs = make_float2(0.0f, 0.0f);
+    bf16x8 qreg[NKK], doreg[NKK];
+    {
+        const long long ro = (((long long)b * p.Sq + i) * p.Hq + h) * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            qreg[kk] = qin ? *(const bf16x8*)(p.q + ro + 16 * kk) : bf16x8{};
+            doreg[kk] = qin ? *(const bf16x8*)(p.dob + ro + 16 * kk) : bf16x8{};
+        }
+        if (qin) {
+            qinf = p.qinfo[(size_t)b * p.Sq + i];
+            rs = p.rowstat[((size_t)b * p.Hq + h) * p.Sq + i];
+        }
+    }
+    const int gi_eff = qinf.x, a_q = qinf.y;
+    if (qinf.x < 0) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) qreg[kk] = bf16x8{};
+    }
+    const float lse2 = rs.x, dlt = rs.y;
+    const size_t prow_off = (((size_t)b * p.Hq + h) * p.Sq + (qin ? i : 0)) * (size_t)p.E;
+    char* const dprow = (char*)p.dprofiles + prow_off * (PB ? 2 : 4);
+    const char* const prow = (const char*)p.profiles + prow_off * (PB ? 2 : 4);
+
+    f32x16 dqacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+
+    // ---- key-tile range of the workgroup (as the forward's)
+    int jlo = INT_MAX, jhi = -1;
+    for (int x = qb_first; x <= qb_last; ++x) {
+        const TileSummary s = p.qsum[(size_t)b * p.nQB + x];
+        if (s.nvalid == 0) continue;
+        const int xlo = p.qoff + x * BM;
+        const int xhi = p.qoff + min(p.Sq, x * BM + BM) - 1;
+        int lo = max(0, s.amin);
+        if (p.window > 0) lo = max(lo, xlo - p.window + 1);
+        jlo = min(jlo, lo);
+        jhi = max(jhi, min(p.Sk - 1, xhi));
+    }
+    const int kt_lo = jhi >= 0 ? jlo / BN : 0;
+    const int kt_hi = jhi >= 0 ? jhi / BN : -1;
+    // class of tile kt against block x (0 skip / 1 masked / 2 full) in bits 2 (x - qb_first)
+    auto classify = [&](int kt) -> int {
+        if (kt > kt_hi) return -1;
+        const int j0 = kt * BN;
+        const int kcount = min(BN, p.Sk - j0);
+        const TileSummary ks = p.ksum[(size_t)b * p.nKT + kt];
+        int code = 0;
+        for (int x = qb_first; x <= qb_last; ++x) {
+            const TileSummary qs = p.qsum[(size_t)b * p.nQB + x];
+            const int xc = min(BM, p.Sq - x * BM);
+            const int xlo = p.qoff + x * BM;
+            code |= classify_tile(qs, xlo, xlo + xc - 1, xc, ks, j0, j0 + kcount - 1, kcount, p.window)
+                    << (2 * (x - qb_first));
+        }
+        return code;
+    };
+    Schedule<NSCHED> sch;
+    sch.list = (int*)(smem + SCHED_OFF);
+    sch.base = kt_lo;
+    sch.n = 0;
+    sch.i = 0;
+
+    // ---- stage loads (registers) and stores (LDS) of one tile
+    i32x4 sk[CPT], sv[CPT], skt[CPT];
+    i32x4 sca = i32x4{};
+    auto stage_load = [&](int kt) {
+        const int j0 = kt * BN;
+#pragma unroll
+        for (int n = 0; n < CPT; ++n) {
+            const int u = tid + 64 * NW * n;
+            const int r = u / CH, c = u % CH;
+            const int j = j0 + r;
+            const bool ok = j < p.Sk && p.key_valid[(size_t)b * p.Sk + j];
+            const long long off = (((long long)b * p.Sk + j) * p.Hkv + g) * D + 8 * c;
+            sk[n] = ok ? *(const i32x4*)(p.k + off) : i32x4{};
+            sv[n] = ok ? *(const i32x4*)(p.v + off) : i32x4{};
+            skt[n] = *(const i32x4*)((const char*)p.kt + (((size_t)b * p.Hkv + g) * p.nKT + kt) * TBYTES + 16 * u);
+        }
+        if (tid < BN / 4) sca = *(const i32x4*)(p.kanchor + (size_t)b * p.nKT * BN + j0 + 4 * tid);
+    };
+    auto stage_store = [&](int buf) {
+        char* st = smem + buf * STAGE;
+#pragma unroll
+        for (int n = 0; n < CPT; ++n) {
+            const int u = tid + 64 * NW * n;
+            const int r = u / CH, c = u % CH;
+            const int pr = r * (2 * D) + 16 * (c ^ row_swz<D>(r));
+            *(i32x4*)(st + K_OFF + pr) = sk[n];
+            *(i32x4*)(st + V_OFF + pr) = sv[n];
+            // K^T: row d = u / 8 of 64 bf16 (128 B), chunk u % 8
+            const int d = u >> 3, cc = u & 7;
+            *(i32x4*)(st + KT_OFF + d * 128 + 16 * (cc ^ ((d >> 1) & 7))) = skt[n];
+        }
+        if (tid < BN / 4) *(i32x4*)(st + CA_OFF + 16 * tid) = sca;
+    };
+
+    int2 cur = next_entry(sch, kt_hi, classify);
+    if (cur.x >= 0) {
+        stage_load(cur.x);
+        stage_store(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    const int xw = qb - qb_first;
+    while (cur.x >= 0) {
+        const int2 nxt = next_entry(sch, kt_hi, classify);
+        if (nxt.x >= 0) stage_load(nxt.x);
+        const int j0 = cur.x * BN;
+        const int my_cls = (cur.y >> (2 * xw)) & 3;
+        const char* st = smem + buf * STAGE;
+
+        // ---- S^T = K Q^T and dP^T = V dO^T, keys 32 s + ((lane & 31) ^ 3) on M
+        f32x16 acc[2], dacc[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            acc[s2] = f32x16{};
+            dacc[s2] = f32x16{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int r = 32 * s2 + (qi ^ 3);
+                const int pr = r * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(r));
+                const bf16x8 ak = *(const bf16x8*)(st + K_OFF + pr);
+                const bf16x8 av = *(const bf16x8*)(st + V_OFF + pr);
+                acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], acc[s2], 0, 0, 0);
+                dacc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[kk], dacc[s2], 0, 0, 0);
+            }
+        }
+
+        // ---- P, dS, profile gradients.  Element (s, jj, e) is key
+        // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), distance rb + e with
+        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).
+        const int* ca = (const int*)(st + CA_OFF);
+        bf16x8 pd[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int kl = 32 * s2 + 8 * jj + 4 * hh;
+                const int rb = gi - (j0 + kl + 3);
+                float bias[4];
+                if (rb >= 0 && rb + 3 < p.E) {
+                    if constexpr (PB) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bias[e] = (float)((const __bf16*)prow)[rb + e];
+                    } else {
+                        const f32x4_u w = *(const f32x4_u*)((const float*)prow + rb);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bias[e] = w[e];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bias[e] = bias_at<PB>(prow, rb + e, p.E);
+                }
+                const i32x4 c4 = *(const i32x4*)(ca + kl);
+                float dz[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float z2 = __builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, bias[e] * LOG2E);
+                    float pr = __builtin_amdgcn_exp2f(z2 - lse2);
+                    if (my_cls != TILE_FULL && !key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
+                        pr = 0.0f;
+                    const float x = pr * (dacc[s2][4 * jj + e] - dlt);
+                    dz[e] = pr != 0.0f ? x : 0.0f;
+                    pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz[e];
+                }
+                if (qin) {
+                    if (rb >= 0 && rb + 3 < p.E && !PB) {
+                        *(f32x4_u*)((float*)dprow + rb) = f32x4_u{dz[0], dz[1], dz[2], dz[3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if ((unsigned)(rb + e) < (unsigned)p.E) store_grad<PB>(dprow, rb + e, dz[e]);
+                    }
+                }
+            }
+
+        // ---- dQ^T += K^T dS^T (K^T rows in the staged key order)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int d = 32 * db + qi;
+                const bf16x8 a = *(const bf16x8*)(st + KT_OFF + d * 128 + 16 * ((2 * c + hh) ^ ((d >> 1) & 7)));
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[c], dqacc[db], 0, 0, 0);
+            }
+
+        if (nxt.x >= 0) stage_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
+    }
+
+    if (!qin) return;
+    // ---- dq = scale * dQ^T
+    {
+        float* dqp = p.dq + (((size_t)b * p.Sq + i) * p.Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = dqacc[db][4 * jj + e] * p.scale;
+                *(f32x4*)(dqp + 32 * db + 8 * jj + 4 * hh) = w;
+            }
+    }
+
+    // ---- zeros at the profile-gradient entries no visited tile wrote: the
+    // distance r belongs to key column gi - r, so these are the columns
+    // outside [0, Sk) and those in tiles the workgroup did not visit.
+    // Each half of the wave takes every other run of 4 distances.
+    auto zero_range = [&](int rlo, int rhi) {   // distances rlo .. rhi of this lane's row
+        rlo = max(rlo, 0);
+        rhi = min(rhi, p.E - 1);
+        for (int r = rlo + 4 * hh; r <= rhi; r += 8)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (r + e <= rhi) store_grad<PB>(dprow, r + e, 0.0f);
+    };
+    zero_range(gi + 1, p.E - 1);                      // columns below 0
+    zero_range(0, gi - p.Sk);                         // columns at or past Sk
+    const int wlo_col = p.qoff + qb_first * BM - p.E + 1;
+    const int whi_col = min(p.Sk - 1, p.qoff + min(p.Sq, (qb_last + 1) * BM) - 1);
+    if (whi_col >= 0) {
+        for (int kt = max(0, wlo_col) / BN; kt <= whi_col / BN; ++kt) {
+            const int code = (kt >= kt_lo && kt <= kt_hi) ? classify(kt) : 0;
+            if (code > 0) continue;                   // visited: every entry written
+            zero_range(gi - (kt * BN + BN - 1), gi - kt * BN);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV.  One workgroup of 4 waves per (batch row, K/V head, 128 keys);
+// wave w owns keys 32 w .. 32 w + 31 of the block, lane = (key kl, half hh).
+// The workgroup walks the live 32-query blocks and, for each, every query
+// head of the group.
+// ---------------------------------------------------------------------------
+template <int D, bool PB>
+__global__ __launch_bounds__(64 * BW_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p)
+{
+    constexpr int NW = BW_WAVES;
+    constexpr int NKK = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int CH = D / 8;
+    constexpr int RBYTES = BM * D * 2;       // one 32-row Q / dO tile, or one Q^T / dO^T tile
+    constexpr int Q_OFF = 0, DO_OFF = RBYTES, QT_OFF = 2 * RBYTES, DOT_OFF = 3 * RBYTES;
+    constexpr int RS_OFF = 4 * RBYTES, QI_OFF = 4 * RBYTES + BM * 8;
+    constexpr int STAGE = 4 * RBYTES + 2 * BM * 8;
+    constexpr int NSCHED = 64 * NW;
+    constexpr int SCHED_OFF = 2 * STAGE;
+    constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
+    constexpr int CPT = BM * CH / (64 * NW);   // chunks per thread of one 32-row tile
+    static_assert(CPT >= 1 && BM * CH % (64 * NW) == 0, "tile chunks must divide among threads");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kl = lane & 31, hh = lane >> 5;
+
+    int idx = blockIdx.x;
+    const int g = idx % p.Hkv; idx /= p.Hkv;
+    const int b = idx % p.B; idx /= p.B;
+    const int kb = idx;                                // key blocks in increasing order
+    const int jb0 = kb * KV_KEYS;
+    const int j = jb0 + 32 * wave + kl;
+    const bool kin = j < p.Sk;
+    const int kt_first = jb0 / BN;
+    const int kt_last = min(p.nKT - 1, kt_first + KV_KEYS / BN - 1);
+    const int xk = (32 * wave) / BN;                   // this wave's key tile within the block
+
+    const int c_k = kin ? p.kanchor[(size_t)b * p.nKT * BN + j] : INT_MIN;
+    const unsigned wlim = p.window > 0 ? (unsigned)p.window : 0x80000000u;
+    bf16x8 kreg[NKK], vreg[NKK];
+    {
+        const bool ok = kin && c_k != INT_MIN;
+        const long long off = (((long long)b * p.Sk + j) * p.Hkv + g) * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            kreg[kk] = ok ? *(const bf16x8*)(p.k + off + 16 * kk) : bf16x8{};
+            vreg[kk] = ok ? *(const bf16x8*)(p.v + off + 16 * kk) : bf16x8{};
+        }
+    }
+    f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+
+    // ---- query-block range: causal (gi >= first key), window, document
+    int qlo_col = INT_MAX, qhi_col = -1;               // global query columns that may see the block
+    for (int x = kt_first; x <= kt_last; ++x) {
+        const TileSummary s = p.ksum[(size_t)b * p.nKT + x];
+        if (s.nvalid == 0) continue;
+        const int xlo = x * BN, xhi = min(p.Sk, x * BN + BN) - 1;
+        qlo_col = min(qlo_col, xlo);
+        int hi = p.qoff + p.Sq - 1;
+        if (p.window > 0) hi = min(hi, xhi + p.window - 1);
+        qhi_col = max(qhi_col, hi);
+    }
+    const int qb_lo = qhi_col >= 0 ? max(0, qlo_col - p.qoff) / BM : 0;
+    const int qb_hi = (qhi_col >= 0 && qhi_col >= p.qoff) ? min(p.nQB - 1, (qhi_col - p.qoff) / BM) : -1;
+    auto classify = [&](int x) -> int {
+        if (x > qb_hi) return -1;
+        const TileSummary qs = p.qsum[(size_t)b * p.nQB + x];
+        const int xc = min(BM, p.Sq - x * BM);
+        const int xlo = p.qoff + x * BM;
+        int code = 0;
+        for (int t = kt_first; t <= kt_last; ++t) {
+            const int j0 = t * BN;
+            const int kcount = min(BN, p.Sk - j0);
+            const TileSummary ks = p.ksum[(size_t)b * p.nKT + t];
+            code |= classify_tile(qs, xlo, xlo + xc - 1, xc, ks, j0, j0 + kcount - 1, kcount, p.window)
+                    << (2 * (t - kt_first));
+        }
+        return code;
+    };
+    Schedule<NSCHED> sch;
+    sch.list = (int*)(smem + SCHED_OFF);
+    sch.base = qb_lo;
+    sch.n = 0;
+    sch.i = 0;
+
+    // ---- stage loads / stores of one (query block, head)
+    i32x4 sq[CPT], sdo[CPT], sqt[CPT], sdt[CPT];
+    i32x4 saux = i32x4{};
+    auto stage_load = [&](int x, int h) {
+        const int i0 = x * BM;
+#pragma unroll
+        for (int n = 0; n < CPT; ++n) {
+            const int u = tid + 64 * NW * n;
+            const int r = u / CH, c = u % CH;
+            const int i = i0 + r;
+            const bool ok = i < p.Sq;
+            const long long off = (((long long)b * p.Sq + i) * p.Hq + h) * D + 8 * c;
+            sq[n] = ok ? *(const i32x4*)(p.q + off) : i32x4{};
+            sdo[n] = ok ? *(const i32x4*)(p.dob + off) : i32x4{};
+            const size_t to = (((size_t)b * p.Hq + h) * p.nQB + x) * RBYTES + 16 * (size_t)u;
+            sqt[n] = *(const i32x4*)((const char*)p.qt + to);
+            sdt[n] = *(const i32x4*)((const char*)p.dot + to);
+        }
+        // row statistics (threads 0..15) and query descriptors (16..31), 2 rows each
+        saux = i32x4{0, 0, -1, 0};
+        if (tid < 32) {
+            const int r = 2 * (tid & 15);
+            const int i = i0 + r;
+            if (tid < 16) {
+                const float2* rsp = p.rowstat + ((size_t)b * p.Hq + h) * p.Sq;
+                float2 a = make_float2(0.0f, 0.0f), c2 = make_float2(0.0f, 0.0f);
+                if (i < p.Sq) a = rsp[i];
+                if (i + 1 < p.Sq) c2 = rsp[i + 1];
+                saux = i32x4{__float_as_int(a.x), __float_as_int(a.y), __float_as_int(c2.x), __float_as_int(c2.y)};
+            } else {
+                int2 a = make_int2(-1, 0), c2 = make_int2(-1, 0);
+                if (i < p.Sq) a = p.qinfo[(size_t)b * p.Sq + i];
+                if (i + 1 < p.Sq) c2 = p.qinfo[(size_t)b * p.Sq + i + 1];
+                saux = i32x4{a.x, a.y, c2.x, c2.y};
+            }
+        }
+    };
+    auto stage_store = [&](int buf) {
+        char* st = smem + buf * STAGE;
+#pragma unroll
+        for (int n = 0; n < CPT; ++n) {
+            const int u = tid + 64 * NW * n;
+            const int r = u / CH, c = u % CH;
+            const int pr = r * (2 * D) + 16 * (c ^ row_swz<D>(r));
+            *(i32x4*)(st + Q_OFF + pr) = sq[n];
+            *(i32x4*)(st + DO_OFF + pr) = sdo[n];
+            // transposed tiles: row d = u / 4 of 32 bf16 (64 B), chunk u % 4
+            const int d = u >> 2, cc = u & 3;
+            const int pt = d * 64 + 16 * (cc ^ ((d >> 2) & 3));
+            *(i32x4*)(st + QT_OFF + pt) = sqt[n];
+            *(i32x4*)(st + DOT_OFF + pt) = sdt[n];
+        }
+        if (tid < 16) *(i32x4*)(st + RS_OFF + 16 * tid) = saux;
+        else if (tid < 32) *(i32x4*)(st + QI_OFF + 16 * (tid - 16)) = saux;
+    };
+    // bias of (query block x, head h) at this lane's key: element (jj, e) is
+    // query row 8 jj + 4 hh + e
+    float breg[16];
+    auto bias_load = [&](int x, int h) {
+        const size_t base = ((size_t)b * p.Hq + h) * p.Sq;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = x * BM + 8 * jj + 4 * hh + e;
+                const int r = p.qoff + i - j;
+                float w = 0.0f;
+                if (i < p.Sq && (unsigned)r < (unsigned)p.E) {
+                    const size_t o = (base + i) * (size_t)p.E + r;
+                    w = PB ? (float)((const __bf16*)p.profiles)[o] : ((const float*)p.profiles)[o];
+                }
+                breg[4 * jj + e] = w;
+            }
+    };
+
+    // iteration = (live query block, head of the group)
+    int2 cur = next_entry(sch, qb_hi, classify);
+    int hcur = 0;
+    if (cur.x >= 0) {
+        stage_load(cur.x, g * p.G);
+        stage_store(0);
+        bias_load(cur.x, g * p.G);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (cur.x >= 0) {
+        int2 nxt = cur;
+        int hn = hcur + 1;
+        if (hn == p.G) {
+            nxt = next_entry(sch, qb_hi, classify);
+            hn = 0;
+        }
+        const int my_cls = (cur.y >> (2 * xk)) & 3;
+        const char* st = smem + buf * STAGE;
+        if (nxt.x >= 0) stage_load(nxt.x, g * p.G + hn);
+
+        // ---- S = Q K^T and dP = dO V^T, queries on M (in order)
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int pr = kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl));
+            const bf16x8 aq = *(const bf16x8*)(st + Q_OFF + pr);
+            const bf16x8 ad = *(const bf16x8*)(st + DO_OFF + pr);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pacc, 0, 0, 0);
+        }
+        float bcur[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) bcur[t] = breg[t];
+        if (nxt.x >= 0) bias_load(nxt.x, g * p.G + hn);
+
+        // ---- P and dS; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
+        bf16x8 pb[2], pd[2];
+        const float* rsl = (const float*)(st + RS_OFF);
+        const int* qil = (const int*)(st + QI_OFF);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int m0 = 8 * jj + 4 * hh;
+            const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
+            const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+            const i32x4 qi01 = *(const i32x4*)(qil + 2 * m0);
+            const i32x4 qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
+                const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
+                const float z2 = __builtin_fmaf(sacc[4 * jj + e], p.c_log2, bcur[4 * jj + e] * LOG2E);
+                float pr = __builtin_amdgcn_exp2f(z2 - lse2);
+                if (my_cls != TILE_FULL) {
+                    const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
+                    const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
+                    if (!key_visible(gq, aq, j, c_k, wlim)) pr = 0.0f;
+                }
+                const float ds = pr != 0.0f ? pr * (pacc[4 * jj + e] - dlt) : 0.0f;
+                pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
+                pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)ds;
+            }
+        }
+
+        // ---- dV^T += dO^T P, dK^T += Q^T dS (transposed tiles in row order)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int d = 32 * db + kl;
+                const int pt = d * 64 + 16 * ((2 * c + hh) ^ ((d >> 2) & 3));
+                const bf16x8 ado = *(const bf16x8*)(st + DOT_OFF + pt);
+                const bf16x8 aqt = *(const bf16x8*)(st + QT_OFF + pt);
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[c], dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, pd[c], dkacc[db], 0, 0, 0);
+            }
+
+        if (nxt.x >= 0) stage_store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
+        hcur = hn;
+    }
+
+    if (!kin) return;
+    const size_t ko = (((size_t)b * p.Sk + j) * p.Hkv + g) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            f32x4 wk, wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wk[e] = dkacc[db][4 * jj + e] * p.scale;
+                wv[e] = dvacc[db][4 * jj + e];
+            }
+            const int d0 = 32 * db + 8 * jj + 4 * hh;
+            *(f32x4*)(p.dk + ko + d0) = wk;
+            *(f32x4*)(p.dv + ko + d0) = wv;
+        }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, size_t n)
+{
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < n; u += (size_t)gridDim.x * 256) x[u] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+    size_t qinfo, rowstat, dob, kt, qt, dot, total;
+};
+
+BwdLayout bwd_layout(int B, int Sq, int Sk, int Hq, int Hkv, int D)
+{
+    BwdLayout l;
+    const size_t nQB = (size_t)ceil_div(Sq, BM), nKT = (size_t)ceil_div(Sk, BN);
+    size_t o = summaries_bytes(B, Sq, Sk);
+    l.qinfo = o;   o += round256((size_t)B * Sq * 8);
+    l.rowstat = o; o += round256((size_t)B * Hq * Sq * 8);
+    l.dob = o;     o += round256((size_t)B * Sq * Hq * D * 2);
+    l.kt = o;      o += round256((size_t)B * Hkv * nKT * BN * D * 2);
+    l.qt = o;      o += round256((size_t)B * Hq * nQB * BM * D * 2);
+    l.dot = o;     o += round256((size_t)B * Hq * nQB * BM * D * 2);
+    l.total = o;
+    return l;
+}
+
+template <int D, bool PB>
+int launch_bwd(const BwdParams& p, hipStream_t st)
+{
+    const long long rows = (long long)p.B * p.Sq * p.Hq;
+    const int rpb = 256 / (D / 4);
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, p);
+    if (int rc = check_launch("bwd_prep_kernel")) return rc;
+    const unsigned nkt = (unsigned)((size_t)p.B * p.Hkv * p.nKT);
+    const unsigned nqt = (unsigned)((size_t)p.B * p.Hq * p.nQB);
+    if (nkt > 0)
+        hipLaunchKernelGGL((bwd_stage_kernel<D, BN, 3, false>), dim3(nkt), dim3((BN / 8) * (D / 8)), 0, st,
+                           (const void*)p.k, p.key_valid, p.Sk, p.Hkv, p.nKT, (long long)p.Sk * p.Hkv * D,
+                           (long long)p.Hkv * D, (long long)D, p.kt);
+    hipLaunchKernelGGL((bwd_stage_kernel<D, BM, 0, false>), dim3(nqt), dim3((BM / 8) * (D / 8)), 0, st,
+                       (const void*)p.q, p.valid, p.Sq, p.Hq, p.nQB, (long long)p.Sq * p.Hq * D,
+                       (long long)p.Hq * D, (long long)D, p.qt);
+    hipLaunchKernelGGL((bwd_stage_kernel<D, BM, 0, true>), dim3(nqt), dim3((BM / 8) * (D / 8)), 0, st,
+                       (const void*)p.dout, p.valid, p.Sq, p.Hq, p.nQB, (long long)p.Sq * p.Hq * D,
+                       (long long)p.Hq * D, (long long)D, p.dot);
+    if (int rc = check_launch("bwd_stage_kernel")) return rc;
+    const size_t ndq = (size_t)p.nQG * p.B * p.Hkv * p.nchunk;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, PB>), dim3((unsigned)ndq), dim3(64 * BW_WAVES), 0, st, p);
+    if (int rc = check_launch("bwd_dq_kernel")) return rc;
+    const size_t nkv = (size_t)p.nKB * p.B * p.Hkv;
+    if (nkv == 0) return INKATTN_OK;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, PB>), dim3((unsigned)nkv), dim3(64 * BW_WAVES), 0, st, p);
+    return check_launch("bwd_dkdv_kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D)
+{
+    if (B <= 0 || Sq < 0 || Sk < 0 || Hq < 0 || Hkv < 0 || D < 0) return 0;
+    return bwd_layout(B, Sq, Sk, Hq, Hkv, D).total;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* profiles, int profiles_dtype,
+             const float* sink, const uint8_t* valid, const uint8_t* key_valid, const int32_t* positions,
+             const int32_t* key_positions, int64_t window, int64_t query_offset, int B, int Sq, int Sk, int Hq,
+             int Hkv, int D, int E, const float* out, const float* lse, const float* dout, const float* dlse,
+             float* dq, float* dk, float* dv, void* dprofiles, float* dsink, void* workspace,
+             size_t workspace_bytes, void* stream)
+{
+    clear_error();
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(INKATTN_ERR_SHAPE, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+    if (E < 1) return fail(INKATTN_ERR_SHAPE, "relative extent E=%d must be >= 1", E);
+    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
+    if (profiles_dtype != INKATTN_F32 && profiles_dtype != INKATTN_BF16)
+        return fail(INKATTN_ERR_UNSUPPORTED, "profiles dtype %d unknown", profiles_dtype);
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
+        return rc;
+    if ((size_t)B * Sq * Hq * D >= (size_t(1) << 40) || (size_t)B * Hq * Sq * E >= (size_t(1) << 40))
+        return fail(INKATTN_ERR_SHAPE, "tensor too large");
+    if ((size_t)Sq * E * (profiles_dtype == INKATTN_F32 ? 4 : 2) >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one (batch row, head) block of profiles must stay below 4 GiB");
+    const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
+    if ((size_t)B * Hq * nQB >= (size_t(1) << 31) || (size_t)B * Hkv * nKT >= (size_t(1) << 31))
+        return fail(INKATTN_ERR_SHAPE, "too many tiles");
+    if ((size_t)B * Sq == 0 && (size_t)B * Sk == 0) return INKATTN_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if ((size_t)B * Sq == 0) {   // no query: every key gradient is 0 (no other tensor is read)
+        if (!dk || !dv) return fail(INKATTN_ERR_NULL, "dk or dv is NULL");
+        if (!aligned(dk, 16) || !aligned(dv, 16)) return fail(INKATTN_ERR_ALIGN, "dk and dv must be 16-byte aligned");
+        const size_t n = (size_t)B * Sk * Hkv * D;
+        const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, dk, n);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, dv, n);
+        return check_launch("fill_zero_kernel");
+    }
+    if (!q || !profiles || !sink || !out || !lse || !dout || !dq || !dprofiles || !dsink)
+        return fail(INKATTN_ERR_NULL, "q/profiles/sink/out/lse/dout/dq/dprofiles/dsink is NULL");
+    if (Sk > 0 && (!k || !v || !dk || !dv)) return fail(INKATTN_ERR_NULL, "k, v, dk or dv is NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+        (Sk > 0 && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))))
+        return fail(INKATTN_ERR_ALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+    const size_t pal = profiles_dtype == INKATTN_F32 ? 4 : 2;
+    if (!aligned(profiles, pal) || !aligned(dprofiles, pal) || !aligned(sink, 4) || !aligned(lse, 4) ||
+        !aligned(dsink, 4) || (dlse && !aligned(dlse, 4)))
+        return fail(INKATTN_ERR_ALIGN, "profiles / dprofiles / sink / lse / dlse / dsink misaligned");
+    const BwdLayout lay = bwd_layout(B, Sq, Sk, Hq, Hkv, D);
+    if (int rc = check_workspace(workspace, workspace_bytes, lay.total)) return rc;
+    const int w = (window <= 0 || window >= (int64_t(1) << 31)) ? 0 : (int)window;
+    if (int rc = launch_summaries(valid, positions, ma.key_valid, ma.key_positions, (int)query_offset, B, Sq, Sk,
+                                  workspace, st))
+        return rc;
+
+    char* ws = (char*)workspace;
+    BwdParams p;
+    p.q = (const __bf16*)q;
+    p.k = (const __bf16*)k;
+    p.v = (const __bf16*)v;
+    p.profiles = profiles;
+    p.sink = sink;
+    p.out = out;
+    p.lse = lse;
+    p.dout = dout;
+    p.dlse = dlse;
+    p.valid = valid;
+    p.key_valid = ma.key_valid;
+    p.positions = positions;
+    p.qsum = (const TileSummary*)ws;
+    p.ksum = p.qsum + (size_t)B * nQB;
+    p.kanchor = (const int*)(ws + tile_summary_bytes(B, Sq, Sk));
+    p.qinfo = (int2*)(ws + lay.qinfo);
+    p.rowstat = (float2*)(ws + lay.rowstat);
+    p.dob = (__bf16*)(ws + lay.dob);
+    p.kt = (__bf16*)(ws + lay.kt);
+    p.qt = (__bf16*)(ws + lay.qt);
+    p.dot = (__bf16*)(ws + lay.dot);
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dprofiles = dprofiles;
+    p.dsink = dsink;
+    p.B = B; p.Sq = Sq; p.Sk = Sk; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.E = E;
+    p.window = w;
+    p.qoff = (int)query_offset;
+    p.hpw = (p.G % 4 == 0) ? 4 : (p.G % 2 == 0) ? 2 : 1;
+    p.tpw = BW_WAVES / p.hpw;
+    p.nchunk = p.G / p.hpw;
+    p.nQB = nQB;
+    p.nKT = nKT;
+    p.nQG = ceil_div(nQB, p.tpw);
+    p.nKB = ceil_div(Sk, KV_KEYS);
+    p.scale = 1.0f / sqrtf((float)D);
+    p.c_log2 = p.scale * LOG2E;
+    if ((size_t)p.nQG * B * Hkv * p.nchunk >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
+    const bool pb = profiles_dtype == INKATTN_BF16;
+    if (D == 128) return pb ? launch_bwd<128, true>(p, st) : launch_bwd<128, false>(p, st);
+    return pb ? launch_bwd<64, true>(p, st) : launch_bwd<64, false>(p, st);
+}
+
+}  // extern "C"

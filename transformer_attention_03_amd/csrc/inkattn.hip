@@ -54,76 +54,21 @@
 #include <cstdio>
 #include <cstring>
 
+#include "common.h"
 #include "inkattn.h"
 
 namespace {
 
-constexpr int BM = 32;   // query tokens per wave (MFMA N)
-constexpr int BN = 64;   // keys per K/V tile (two MFMA M-blocks of 32)
+using namespace inkattn;
+
 constexpr int NWAVES = 8; // waves per attention workgroup (one workgroup per CU)
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
 // s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
 // vmcnt(0) lgkmcnt(0); lgkmcnt(0) alone
 constexpr int WAIT_VM_LGKM = 0x0070;
 constexpr int WAIT_LGKM = 0xC07F;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4_u __attribute__((ext_vector_type(4), aligned(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// Per-tile summary written by the pre-pass: document start columns of the
-// tile's real tokens (min, max) and how many real tokens it has.
-struct __attribute__((aligned(16))) TileSummary {
-    int amin, amax, nvalid, pad;
-};
-
-// ---------------------------------------------------------------------------
-// Mask predicate shared by the attention kernel and the debug exports.
-//
-// gi_eff: global column of the query, or -1 for a query that is not real
-//         (then no key passes the causal test).
-// a_q:    the query's document start column gi - positions[i].
-// j:      key column; c_k: the key's start column j - key_positions[j], or
-//         INT_MIN for a key that is not real or lies past Sk.
-// wlim:   window as an unsigned limit on gi - j (2^31 when there is none).
-// Same document implies positions[i] - key_positions[j] == gi - j, so the
-// window and causal tests both act on gi - j.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool key_visible(int gi_eff, int a_q, int j, int c_k, unsigned wlim)
-{
-    return (unsigned)(gi_eff - j) < wlim && c_k == a_q;
-}
-
-enum : int { TILE_SKIP = 0, TILE_MASKED = 1, TILE_FULL = 2 };
-
-// Class of (query block, key tile) from the two summaries and the column
-// ranges.  qlo / qhi: global columns of the block's first / last existing
-// query; j0: first key column of the tile; key_hi: last existing key column.
-__device__ __forceinline__ int classify_tile(const TileSummary& qs, int qlo, int qhi, int qcount,
-                                             const TileSummary& ks, int j0, int key_hi, int kcount,
-                                             int window)
-{
-    if (qcount <= 0 || qs.nvalid == 0 || ks.nvalid == 0) return TILE_SKIP;
-    if (j0 > qhi) return TILE_SKIP;                                 // causal
-    if (ks.amax < qs.amin || ks.amin > qs.amax) return TILE_SKIP;   // no common document
-    if (window > 0 && qlo - key_hi >= window) return TILE_SKIP;     // nearest pair outside the window
-    const bool one_doc = qs.amin == qs.amax && ks.amin == ks.amax && qs.amin == ks.amin;
-    const bool all_real = qs.nvalid == qcount && ks.nvalid == kcount && qcount == BM && kcount == BN;
-    const bool causal_full = key_hi <= qlo;
-    const bool window_full = window <= 0 || qhi - j0 < window;
-    return (one_doc && all_real && causal_full && window_full) ? TILE_FULL : TILE_MASKED;
-}
 
 // ---------------------------------------------------------------------------
 // Scheduler pre-pass: one wave per (batch row, tile); query tiles first, then
@@ -210,26 +155,6 @@ struct FwdParams {
     float c_log2;    // head_dim^-0.5 * log2(e)
 };
 
-// A value the compiler may not look through (no constant is split off it and
-// no two loads using such offsets are merged).  The empty asm only exists in
-// the device pass; the host pass never generates kernel code.
-__device__ __forceinline__ unsigned opaque(unsigned x)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("" : "+v"(x));
-#endif
-    return x;
-}
-
-// An empty use of a value in registers: its computation must happen before
-// this point (the device pass only; the host pass never generates kernel code).
-template <typename T>
-__device__ __forceinline__ void pin(const T& x)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("" ::"v"(x));
-#endif
-}
 
 // Wait for every outstanding memory operation of the wave, then meet the
 // workgroup.  The wait is the builtin so that the compiler's own wait counting
@@ -304,19 +229,6 @@ template <> struct TileLayout<64> {
     __device__ static constexpr int ksw(int t) { return t >> 1; }
 };
 
-// Staged value tiles.  The staging pass writes, per (batch row, K/V head,
-// 64-key tile), V^T as D rows of 64 fp16 values (128 B), the keys of each
-// 16-key step in the order the PV MFMA consumes them: slot 8 hh + t of a step
-// holds key 8 (t / 4) + 4 hh + ((t % 4) ^ 3), the key order of the P^T
-// operand taken from the S^T accumulator.  A lane then reads its 8 keys of a
-// step as one 16-byte chunk.  In LDS the 16-byte chunk c of row d sits at
-// chunk c ^ vt_swz(d), which spreads the 16 rows of one read phase over all
-// 64 banks.
-__host__ __device__ constexpr int vt_slot(int key)   // key within the tile -> slot
-{
-    return 16 * (key / 16) + 8 * ((key / 4) % 2) + 4 * ((key % 16) / 8) + ((key % 4) ^ 3);
-}
-__device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
 
 enum : int { BIAS_NONE = 0, BIAS_FAST = 1, BIAS_EDGE = 2 };
 
@@ -1044,9 +956,15 @@ __global__ void debug_tiles_kernel(const TileSummary* __restrict__ qsum, const T
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+
+}  // namespace
+
+namespace inkattn __attribute__((visibility("hidden"))) {
+
 thread_local char g_last_error[512] = "";
 
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error() { g_last_error[0] = '\0'; }
+
 int fail(int status, const char* fmt, ...)
 {
     va_list ap;
@@ -1058,7 +976,6 @@ int fail(int status, const char* fmt, ...)
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Workspace layout: [tile summaries][key start columns, int32 B*Sk][values in fp16, B*Sk*Hkv*D],
 // the first two parts each rounded up to 256 bytes.  summaries_bytes covers the
@@ -1081,11 +998,6 @@ size_t values_bytes(int B, int Sk, int Hkv, int D)
 }
 
 // Defaults of the optional arguments and the checks shared by every entry point.
-struct MaskArgs {
-    const uint8_t* key_valid;
-    const int32_t* positions;
-    const int32_t* key_positions;
-};
 
 int resolve_mask_args(const uint8_t* valid, const uint8_t* key_valid, const int32_t* positions,
                       const int32_t* key_positions, int64_t query_offset, int B, int Sq, int Sk,
@@ -1145,6 +1057,10 @@ int launch_summaries(const uint8_t* valid, const int32_t* positions, const uint8
                        key_valid, key_positions, Sk, nKT, B, qsum, ksum, kanchor);
     return check_launch("summarize_kernel");
 }
+
+}  // namespace inkattn
+
+namespace {
 
 // Checks of attn_fwd / attn_fwd_planned that need no device access.
 int check_fwd_args(const void* q, const void* k, const void* v, const void* profiles, int profiles_dtype,
