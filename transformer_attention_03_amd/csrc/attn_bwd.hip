@@ -106,6 +106,18 @@ template <int D> __device__ __forceinline__ int row_swz(int r)
     return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+// Buffer resource over nrec bytes from base (reads past nrec return 0,
+// writes past it are dropped).  The address and size go through
+// readfirstlane, so the resource is known to be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, size_t nrec)
+{
+    const unsigned long long a = (unsigned long long)base;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    const unsigned n = __builtin_amdgcn_readfirstlane((unsigned)nrec);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0, n, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics, bf16 dout, query descriptors.  TPR = D / 4 threads per
 // (batch row, query, head) row.
@@ -280,7 +292,8 @@ void bwd_dq_kernel(BwdParams p)
     constexpr int K_OFF = 0, V_OFF = TBYTES, KT_OFF = 2 * TBYTES, CA_OFF = 3 * TBYTES;
     constexpr int STAGE = 3 * TBYTES + BN * 4;
     constexpr int NSCHED = 64 * NW;
-    constexpr int SCHED_OFF = 2 * STAGE;
+    constexpr int B_OFF = 2 * STAGE;         // per-wave bias strips (32 values per lane)
+    constexpr int SCHED_OFF = B_OFF + NW * 32 * 64 * 4;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     constexpr int CPT = BN * CH / (64 * NW);  // 16-byte chunks per thread of one K (or V, K^T) tile
     static_assert(CPT >= 1 && BN * CH % (64 * NW) == 0, "tile chunks must divide among threads");
@@ -373,24 +386,67 @@ void bwd_dq_kernel(BwdParams p)
     sch.n = 0;
     sch.i = 0;
 
-    // ---- stage loads (registers) and stores (LDS) of one tile
+    // ---- staging.  Every global load of a tile is issued unconditionally at
+    // the start of the iteration before (buffer loads: rows past Sk and
+    // distances outside this query's row read as 0 or are masked on use) and
+    // stored to LDS at its end, so the loads have a whole iteration to land.
+    const unsigned krow = (unsigned)(p.Hkv * D * 2);          // bytes between consecutive keys
+    const unsigned knrec = p.Sk > 0 ? (unsigned)(p.Sk - 1) * krow + D * 2 : 0u;
+    const long long kvbase = ((long long)b * p.Sk * p.Hkv + g) * D;
+    const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(p.k + kvbase, knrec);
+    const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(p.v + kvbase, knrec);
+    constexpr int ES = PB ? 2 : 4;                               // profile element bytes
+    const size_t pblock = (size_t)p.Sq * p.E * ES;               // one (batch row, head) of profiles
+    const __amdgpu_buffer_rsrc_t prs =
+        uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
+    const __amdgpu_buffer_rsrc_t drs = uniform_rsrc((char*)p.dprofiles + ((size_t)b * p.Hq + h) * pblock, pblock);
+    const unsigned rowe = (unsigned)(qin ? i : 0) * (unsigned)p.E;   // this query's row, in entries
+    const bool edge_block = qb == 0 || qb >= p.nQB - 1;               // (wave-uniform)
     i32x4 sk[CPT], sv[CPT], skt[CPT];
-    i32x4 sca = i32x4{};
+    i32x4 sca;
+    float breg[32];    // bias of the next tile: index 16 s + 4 jj + e is distance rb + e (below)
     auto stage_load = [&](int kt) {
         const int j0 = kt * BN;
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
             const int u = tid + 64 * NW * n;
             const int r = u / CH, c = u % CH;
-            const int j = j0 + r;
-            const bool ok = j < p.Sk && p.key_valid[(size_t)b * p.Sk + j];
-            const long long off = (((long long)b * p.Sk + j) * p.Hkv + g) * D + 8 * c;
-            sk[n] = ok ? *(const i32x4*)(p.k + off) : i32x4{};
-            sv[n] = ok ? *(const i32x4*)(p.v + off) : i32x4{};
+            const unsigned off = (unsigned)(j0 + r) * krow + 16u * (unsigned)c;
+            sk[n] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+            sv[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
             skt[n] = *(const i32x4*)((const char*)p.kt + (((size_t)b * p.Hkv + g) * p.nKT + kt) * TBYTES + 16 * u);
         }
-        if (tid < BN / 4) sca = *(const i32x4*)(p.kanchor + (size_t)b * p.nKT * BN + j0 + 4 * tid);
+        sca = *(const i32x4*)(p.kanchor + (size_t)b * p.nKT * BN + j0 + 4 * (tid & 15));
+        // bias: rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3); entries outside [0, E) are zeroed on use
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rb = gi - (j0 + 32 * s2 + 8 * jj + 4 * hh + 3);
+                float* w = breg + 16 * s2 + 4 * jj;
+                const unsigned off = (rowe + (unsigned)rb) * (unsigned)ES;
+                // (per-element offsets wrap modulo 2^32 like the run's start: they
+                // are kept opaque so that no constant part moves into the
+                // instruction's offset field, which the hardware adds unwrapped)
+                if constexpr (PB) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = __uint_as_float(
+                            (unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, opaque(off + 2u * e), 0, 0) << 16);
+                } else if (edge_block) {
+                    // the first and last rows of the block may have runs that start
+                    // before or end after it: one dword at a time
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, opaque(off + 4u * e), 0, 0));
+                } else {
+                    const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = __int_as_float(x[e]);
+                }
+            }
     };
+    char* const bstrip = smem + B_OFF + wave * (32 * 64 * 4);   // this wave's bias, lane-major
     auto stage_store = [&](int buf) {
         char* st = smem + buf * STAGE;
 #pragma unroll
@@ -405,6 +461,9 @@ void bwd_dq_kernel(BwdParams p)
             *(i32x4*)(st + KT_OFF + d * 128 + 16 * (cc ^ ((d >> 1) & 7))) = skt[n];
         }
         if (tid < BN / 4) *(i32x4*)(st + CA_OFF + 16 * tid) = sca;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            *(f32x4*)(bstrip + t * 1024 + 16 * lane) = f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
     };
 
     int2 cur = next_entry(sch, kt_hi, classify);
@@ -412,6 +471,9 @@ void bwd_dq_kernel(BwdParams p)
         stage_load(cur.x);
         stage_store(0);
     }
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is outstanding inside it
+#endif
     __syncthreads();
     int buf = 0;
     const int xw = qb - qb_first;
@@ -444,7 +506,8 @@ void bwd_dq_kernel(BwdParams p)
 
         // ---- P, dS, profile gradients.  Element (s, jj, e) is key
         // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), distance rb + e with
-        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).
+        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).  Stores outside this
+        // query's row [0, E) get an offset past the buffer and are dropped.
         const int* ca = (const int*)(st + CA_OFF);
         bf16x8 pd[4];
 #pragma unroll
@@ -453,40 +516,24 @@ void bwd_dq_kernel(BwdParams p)
             for (int jj = 0; jj < 4; ++jj) {
                 const int kl = 32 * s2 + 8 * jj + 4 * hh;
                 const int rb = gi - (j0 + kl + 3);
-                float bias[4];
-                if (rb >= 0 && rb + 3 < p.E) {
-                    if constexpr (PB) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) bias[e] = (float)((const __bf16*)prow)[rb + e];
-                    } else {
-                        const f32x4_u w = *(const f32x4_u*)((const float*)prow + rb);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) bias[e] = w[e];
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) bias[e] = bias_at<PB>(prow, rb + e, p.E);
-                }
+                const f32x4 bias = *(const f32x4*)(bstrip + (4 * s2 + jj) * 1024 + 16 * lane);
                 const i32x4 c4 = *(const i32x4*)(ca + kl);
-                float dz[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float z2 = __builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, bias[e] * LOG2E);
+                    const bool inside = (unsigned)(rb + e) < (unsigned)p.E;
+                    const float z2 = __builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, inside ? bias[e] * LOG2E : 0.0f);
                     float pr = __builtin_amdgcn_exp2f(z2 - lse2);
                     if (my_cls != TILE_FULL && !key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
                         pr = 0.0f;
                     const float x = pr * (dacc[s2][4 * jj + e] - dlt);
-                    dz[e] = pr != 0.0f ? x : 0.0f;
-                    pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz[e];
-                }
-                if (qin) {
-                    if (rb >= 0 && rb + 3 < p.E && !PB) {
-                        *(f32x4_u*)((float*)dprow + rb) = f32x4_u{dz[0], dz[1], dz[2], dz[3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if ((unsigned)(rb + e) < (unsigned)p.E) store_grad<PB>(dprow, rb + e, dz[e]);
-                    }
+                    const float dz = pr != 0.0f ? x : 0.0f;
+                    pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz;
+                    const unsigned off = (inside && qin) ? (rowe + (unsigned)(rb + e)) * (unsigned)ES : 0xFFFFFFF0u;
+                    if constexpr (PB)
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(__float_as_uint((float)(__bf16)dz) >> 16),
+                                                               drs, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dz), drs, off, 0, 0);
                 }
             }
 
@@ -500,6 +547,7 @@ void bwd_dq_kernel(BwdParams p)
                 dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[c], dqacc[db], 0, 0, 0);
             }
 
+        // (this wave has read its bias strip: it takes the next tile's)
         if (nxt.x >= 0) stage_store(buf ^ 1);
         __syncthreads();
         buf ^= 1;
@@ -565,7 +613,8 @@ void bwd_dkdv_kernel(BwdParams p)
     constexpr int RS_OFF = 4 * RBYTES, QI_OFF = 4 * RBYTES + BM * 8;
     constexpr int STAGE = 4 * RBYTES + 2 * BM * 8;
     constexpr int NSCHED = 64 * NW;
-    constexpr int SCHED_OFF = 2 * STAGE;
+    constexpr int B_OFF = 2 * STAGE;                // per-wave bias strips (16 values per lane)
+    constexpr int SCHED_OFF = B_OFF + NW * 16 * 64 * 4;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     constexpr int CPT = BM * CH / (64 * NW);   // chunks per thread of one 32-row tile
     static_assert(CPT >= 1 && BM * CH % (64 * NW) == 0, "tile chunks must divide among threads");
@@ -641,44 +690,61 @@ void bwd_dkdv_kernel(BwdParams p)
     sch.n = 0;
     sch.i = 0;
 
-    // ---- stage loads / stores of one (query block, head)
+    // ---- staging of one (query block, head): every global load is issued
+    // unconditionally one iteration ahead (buffer loads; rows past Sq read as
+    // 0) and stored to LDS at the end of the iteration.
+    const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
+    const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
+    const long long qbase = (long long)b * p.Sq * p.Hq * D;
+    constexpr int ES = PB ? 2 : 4;
     i32x4 sq[CPT], sdo[CPT], sqt[CPT], sdt[CPT];
-    i32x4 saux = i32x4{};
+    i32x4 saux;        // rows 2 l, 2 l + 1 of the block (l = lane % 16): row statistics (even waves) or descriptors (odd)
+    float breg[16];    // bias of the next (block, head) at this lane's key: rows 8 jj + 4 hh + e
     auto stage_load = [&](int x, int h) {
         const int i0 = x * BM;
+        const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
+        const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
             const int u = tid + 64 * NW * n;
             const int r = u / CH, c = u % CH;
-            const int i = i0 + r;
-            const bool ok = i < p.Sq;
-            const long long off = (((long long)b * p.Sq + i) * p.Hq + h) * D + 8 * c;
-            sq[n] = ok ? *(const i32x4*)(p.q + off) : i32x4{};
-            sdo[n] = ok ? *(const i32x4*)(p.dob + off) : i32x4{};
+            const unsigned off = (unsigned)(i0 + r) * qrow + 16u * (unsigned)c;
+            sq[n] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+            sdo[n] = __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0);
             const size_t to = (((size_t)b * p.Hq + h) * p.nQB + x) * RBYTES + 16 * (size_t)u;
             sqt[n] = *(const i32x4*)((const char*)p.qt + to);
             sdt[n] = *(const i32x4*)((const char*)p.dot + to);
         }
-        // row statistics (threads 0..15) and query descriptors (16..31), 2 rows each
-        saux = i32x4{0, 0, -1, 0};
-        if (tid < 32) {
-            const int r = 2 * (tid & 15);
-            const int i = i0 + r;
-            if (tid < 16) {
-                const float2* rsp = p.rowstat + ((size_t)b * p.Hq + h) * p.Sq;
-                float2 a = make_float2(0.0f, 0.0f), c2 = make_float2(0.0f, 0.0f);
-                if (i < p.Sq) a = rsp[i];
-                if (i + 1 < p.Sq) c2 = rsp[i + 1];
-                saux = i32x4{__float_as_int(a.x), __float_as_int(a.y), __float_as_int(c2.x), __float_as_int(c2.y)};
-            } else {
-                int2 a = make_int2(-1, 0), c2 = make_int2(-1, 0);
-                if (i < p.Sq) a = p.qinfo[(size_t)b * p.Sq + i];
-                if (i + 1 < p.Sq) c2 = p.qinfo[(size_t)b * p.Sq + i + 1];
-                saux = i32x4{a.x, a.y, c2.x, c2.y};
-            }
+        {
+            const int r2 = 2 * (lane & 15);
+            const __amdgpu_buffer_rsrc_t rrs = uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
+            const __amdgpu_buffer_rsrc_t irs = uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8);
+            // one 8-byte row per load (each lies wholly inside or past the end)
+            const unsigned off = (unsigned)(i0 + r2) * 8u;
+            const __amdgpu_buffer_rsrc_t xrs = (wave & 1) ? irs : rrs;   // odd waves: descriptors
+            const auto lo = __builtin_amdgcn_raw_buffer_load_b64(xrs, off, 0, 0);
+            const auto hi = __builtin_amdgcn_raw_buffer_load_b64(xrs, off + 8u, 0, 0);
+            saux = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
         }
+        const size_t pblock = (size_t)p.Sq * p.E * ES;
+        const __amdgpu_buffer_rsrc_t prs =
+            uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = i0 + 8 * jj + 4 * hh + e;
+                const int r = p.qoff + i - j;
+                const unsigned off = ((unsigned)i * (unsigned)p.E + (unsigned)r) * (unsigned)ES;
+                if constexpr (PB)
+                    breg[4 * jj + e] =
+                        __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, off, 0, 0) << 16);
+                else
+                    breg[4 * jj + e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, 0));
+            }
     };
-    auto stage_store = [&](int buf) {
+    char* const bstrip = smem + B_OFF + wave * (16 * 64 * 4);   // this wave's bias, lane-major
+    auto stage_store = [&](int buf, int x) {
         char* st = smem + buf * STAGE;
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
@@ -693,27 +759,19 @@ void bwd_dkdv_kernel(BwdParams p)
             *(i32x4*)(st + QT_OFF + pt) = sqt[n];
             *(i32x4*)(st + DOT_OFF + pt) = sdt[n];
         }
-        if (tid < 16) *(i32x4*)(st + RS_OFF + 16 * tid) = saux;
-        else if (tid < 32) *(i32x4*)(st + QI_OFF + 16 * (tid - 16)) = saux;
-    };
-    // bias of (query block x, head h) at this lane's key: element (jj, e) is
-    // query row 8 jj + 4 hh + e
-    float breg[16];
-    auto bias_load = [&](int x, int h) {
-        const size_t base = ((size_t)b * p.Hq + h) * p.Sq;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = x * BM + 8 * jj + 4 * hh + e;
-                const int r = p.qoff + i - j;
-                float w = 0.0f;
-                if (i < p.Sq && (unsigned)r < (unsigned)p.E) {
-                    const size_t o = (base + i) * (size_t)p.E + r;
-                    w = PB ? (float)((const __bf16*)p.profiles)[o] : ((const float*)p.profiles)[o];
-                }
-                breg[4 * jj + e] = w;
+        if (wave < 2 && lane < 16) {
+            i32x4 a = saux;
+            if (wave == 1) {   // a row past Sq is not real
+                const int r2 = x * BM + 2 * lane;
+                if (r2 >= p.Sq) a[0] = -1;
+                if (r2 + 1 >= p.Sq) a[2] = -1;
             }
+            *(i32x4*)(st + (wave == 1 ? QI_OFF : RS_OFF) + 16 * lane) = a;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
+                f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
     };
 
     // iteration = (live query block, head of the group)
@@ -721,9 +779,11 @@ void bwd_dkdv_kernel(BwdParams p)
     int hcur = 0;
     if (cur.x >= 0) {
         stage_load(cur.x, g * p.G);
-        stage_store(0);
-        bias_load(cur.x, g * p.G);
+        stage_store(0, cur.x);
     }
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is outstanding inside it
+#endif
     __syncthreads();
     int buf = 0;
     while (cur.x >= 0) {
@@ -733,6 +793,7 @@ void bwd_dkdv_kernel(BwdParams p)
             nxt = next_entry(sch, qb_hi, classify);
             hn = 0;
         }
+        const int i0 = cur.x * BM;
         const int my_cls = (cur.y >> (2 * xk)) & 3;
         const char* st = smem + buf * STAGE;
         if (nxt.x >= 0) stage_load(nxt.x, g * p.G + hn);
@@ -747,10 +808,6 @@ void bwd_dkdv_kernel(BwdParams p)
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sacc, 0, 0, 0);
             pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pacc, 0, 0, 0);
         }
-        float bcur[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) bcur[t] = breg[t];
-        if (nxt.x >= 0) bias_load(nxt.x, g * p.G + hn);
 
         // ---- P and dS; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
         bf16x8 pb[2], pd[2];
@@ -763,11 +820,14 @@ void bwd_dkdv_kernel(BwdParams p)
             const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
             const i32x4 qi01 = *(const i32x4*)(qil + 2 * m0);
             const i32x4 qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
+            const f32x4 bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
                 const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
-                const float z2 = __builtin_fmaf(sacc[4 * jj + e], p.c_log2, bcur[4 * jj + e] * LOG2E);
+                const int r = p.qoff + i0 + m0 + e - j;
+                const float bz = (unsigned)r < (unsigned)p.E ? bias[e] * LOG2E : 0.0f;
+                const float z2 = __builtin_fmaf(sacc[4 * jj + e], p.c_log2, bz);
                 float pr = __builtin_amdgcn_exp2f(z2 - lse2);
                 if (my_cls != TILE_FULL) {
                     const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
@@ -793,7 +853,7 @@ void bwd_dkdv_kernel(BwdParams p)
                 dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, pd[c], dkacc[db], 0, 0, 0);
             }
 
-        if (nxt.x >= 0) stage_store(buf ^ 1);
+        if (nxt.x >= 0) stage_store(buf ^ 1, nxt.x);
         __syncthreads();
         buf ^= 1;
         cur = nxt;
@@ -903,8 +963,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* profiles, 
         return rc;
     if ((size_t)B * Sq * Hq * D >= (size_t(1) << 40) || (size_t)B * Hq * Sq * E >= (size_t(1) << 40))
         return fail(INKATTN_ERR_SHAPE, "tensor too large");
-    if ((size_t)Sq * E * (profiles_dtype == INKATTN_F32 ? 4 : 2) >= (size_t(1) << 32))
-        return fail(INKATTN_ERR_SHAPE, "one (batch row, head) block of profiles must stay below 4 GiB");
+    if ((size_t)Sq * E * (profiles_dtype == INKATTN_F32 ? 4 : 2) >= (size_t(1) << 32) - (size_t(1) << 20))
+        return fail(INKATTN_ERR_SHAPE, "one (batch row, head) block of profiles must stay below 4 GiB - 1 MiB");
+    if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32) || (size_t)Sq * Hq * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one batch row of q, k or v must stay below 4 GiB");
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
     if ((size_t)B * Hq * nQB >= (size_t(1) << 31) || (size_t)B * Hkv * nKT >= (size_t(1) << 31))
         return fail(INKATTN_ERR_SHAPE, "too many tiles");
