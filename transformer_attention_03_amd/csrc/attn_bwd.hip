@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -49,6 +50,8 @@ namespace {
 using namespace inkattn;
 
 constexpr int BW_WAVES = 4;          // waves per workgroup of both gradient kernels
+// bias class of a tile for one wave: no distance inside [0, E), all inside, mixed
+enum : int { BC_NONE = 0, BC_FULL = 1, BC_EDGE = 2 };
 constexpr int KV_KEYS = 32 * BW_WAVES;   // keys per dK / dV workgroup
 
 struct BwdParams {
@@ -386,38 +389,57 @@ void bwd_dq_kernel(BwdParams p)
     sch.n = 0;
     sch.i = 0;
 
-    // ---- staging.  Every global load of a tile is issued unconditionally at
-    // the start of the iteration before (buffer loads: rows past Sk and
-    // distances outside this query's row read as 0 or are masked on use) and
-    // stored to LDS at its end, so the loads have a whole iteration to land.
+    // ---- staging.  Every global load of a tile is a buffer load issued at
+    // the start of the iteration before and stored to LDS at its end, so the
+    // loads have a whole iteration to land.  Rows past Sk read as 0.
     const unsigned krow = (unsigned)(p.Hkv * D * 2);          // bytes between consecutive keys
     const unsigned knrec = p.Sk > 0 ? (unsigned)(p.Sk - 1) * krow + D * 2 : 0u;
     const long long kvbase = ((long long)b * p.Sk * p.Hkv + g) * D;
     const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(p.k + kvbase, knrec);
     const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(p.v + kvbase, knrec);
+    const __amdgpu_buffer_rsrc_t kts = uniform_rsrc(p.kt + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(BN * D),
+                                                    (size_t)p.nKT * TBYTES);
+    const __amdgpu_buffer_rsrc_t kas = uniform_rsrc(p.kanchor + (size_t)b * p.nKT * BN, (size_t)p.nKT * BN * 4);
     constexpr int ES = PB ? 2 : 4;                               // profile element bytes
     const size_t pblock = (size_t)p.Sq * p.E * ES;               // one (batch row, head) of profiles
     const __amdgpu_buffer_rsrc_t prs =
         uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
     const __amdgpu_buffer_rsrc_t drs = uniform_rsrc((char*)p.dprofiles + ((size_t)b * p.Hq + h) * pblock, pblock);
     const unsigned rowe = (unsigned)(qin ? i : 0) * (unsigned)p.E;   // this query's row, in entries
-    const bool edge_block = qb == 0 || qb >= p.nQB - 1;               // (wave-uniform)
+    // per-thread parts of the K / V row offsets (chunk u = tid + 256 n: row u / CH, chunk u % CH)
+    unsigned kvoff[CPT];
+#pragma unroll
+    for (int n = 0; n < CPT; ++n) {
+        const int u = tid + 64 * NW * n;
+        kvoff[n] = (unsigned)(u / CH) * krow + 16u * (unsigned)(u % CH);
+    }
+    // Bias class of a tile for this wave: no distance of its 32 x 64 pairs in
+    // [0, E) (no bias, no profile gradient), all inside (whole 16-byte runs),
+    // or mixed (entry by entry).  Wave-uniform.
+    const int qlo_w = p.qoff + i0, qhi_w = p.qoff + min(p.Sq, i0 + BM) - 1;
+    auto bias_class = [&](int j0t) -> int {
+        if (qb >= p.nQB) return BC_NONE;
+        const int rmin = qlo_w - (j0t + BN - 1), rmax = qhi_w - j0t;
+        if (rmax < 0 || rmin >= p.E) return BC_NONE;
+        return (rmin >= 0 && rmax < p.E) ? BC_FULL : BC_EDGE;
+    };
     i32x4 sk[CPT], sv[CPT], skt[CPT];
     i32x4 sca;
     float breg[32];    // bias of the next tile: index 16 s + 4 jj + e is distance rb + e (below)
+    int nbc = BC_NONE; // its class
     auto stage_load = [&](int kt) {
         const int j0 = kt * BN;
+        const unsigned kb0 = (unsigned)j0 * krow;
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
-            const int u = tid + 64 * NW * n;
-            const int r = u / CH, c = u % CH;
-            const unsigned off = (unsigned)(j0 + r) * krow + 16u * (unsigned)c;
-            sk[n] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-            sv[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-            skt[n] = *(const i32x4*)((const char*)p.kt + (((size_t)b * p.Hkv + g) * p.nKT + kt) * TBYTES + 16 * u);
+            sk[n] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff[n] + kb0, 0, 0);
+            sv[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, kvoff[n] + kb0, 0, 0);
+            skt[n] = __builtin_amdgcn_raw_buffer_load_b128(kts, 16u * (unsigned)(tid + 64 * NW * n), kt * TBYTES, 0);
         }
-        sca = *(const i32x4*)(p.kanchor + (size_t)b * p.nKT * BN + j0 + 4 * (tid & 15));
-        // bias: rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3); entries outside [0, E) are zeroed on use
+        sca = __builtin_amdgcn_raw_buffer_load_b128(kas, 16u * (unsigned)(tid & 15), j0 * 4, 0);
+        nbc = bias_class(j0);
+        if (nbc == BC_NONE) return;
+        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -425,17 +447,14 @@ void bwd_dq_kernel(BwdParams p)
                 const int rb = gi - (j0 + 32 * s2 + 8 * jj + 4 * hh + 3);
                 float* w = breg + 16 * s2 + 4 * jj;
                 const unsigned off = (rowe + (unsigned)rb) * (unsigned)ES;
-                // (per-element offsets wrap modulo 2^32 like the run's start: they
-                // are kept opaque so that no constant part moves into the
-                // instruction's offset field, which the hardware adds unwrapped)
                 if constexpr (PB) {
+                    // (entry offsets kept opaque: they may wrap modulo 2^32 like
+                    // the run's start, which the instruction's offset field would not)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         w[e] = __uint_as_float(
                             (unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, opaque(off + 2u * e), 0, 0) << 16);
-                } else if (edge_block) {
-                    // the first and last rows of the block may have runs that start
-                    // before or end after it: one dword at a time
+                } else if (nbc == BC_EDGE) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         w[e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, opaque(off + 4u * e), 0, 0));
@@ -461,9 +480,12 @@ void bwd_dq_kernel(BwdParams p)
             *(i32x4*)(st + KT_OFF + d * 128 + 16 * (cc ^ ((d >> 1) & 7))) = skt[n];
         }
         if (tid < BN / 4) *(i32x4*)(st + CA_OFF + 16 * tid) = sca;
+        if (nbc != BC_NONE) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-            *(f32x4*)(bstrip + t * 1024 + 16 * lane) = f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
+            for (int t = 0; t < 8; ++t)
+                *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
+                    f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
+        }
     };
 
     int2 cur = next_entry(sch, kt_hi, classify);
@@ -477,11 +499,13 @@ void bwd_dq_kernel(BwdParams p)
     __syncthreads();
     int buf = 0;
     const int xw = qb - qb_first;
+    const float nlse2 = -lse2;
     while (cur.x >= 0) {
         const int2 nxt = next_entry(sch, kt_hi, classify);
         if (nxt.x >= 0) stage_load(nxt.x);
         const int j0 = cur.x * BN;
         const int my_cls = (cur.y >> (2 * xw)) & 3;
+        const int bc = bias_class(j0);
         const char* st = smem + buf * STAGE;
 
         // ---- S^T = K Q^T and dP^T = V dO^T, keys 32 s + ((lane & 31) ^ 3) on M
@@ -506,36 +530,87 @@ void bwd_dq_kernel(BwdParams p)
 
         // ---- P, dS, profile gradients.  Element (s, jj, e) is key
         // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), distance rb + e with
-        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).  Stores outside this
-        // query's row [0, E) get an offset past the buffer and are dropped.
+        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).
         const int* ca = (const int*)(st + CA_OFF);
         bf16x8 pd[4];
+        auto body = [&](auto bct, auto mt) {
+            constexpr int BCT = decltype(bct)::value;
+            constexpr bool MASKED = decltype(mt)::value;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int kl = 32 * s2 + 8 * jj + 4 * hh;
-                const int rb = gi - (j0 + kl + 3);
-                const f32x4 bias = *(const f32x4*)(bstrip + (4 * s2 + jj) * 1024 + 16 * lane);
-                const i32x4 c4 = *(const i32x4*)(ca + kl);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int kl = 32 * s2 + 8 * jj + 4 * hh;
+                    const int rb = gi - (j0 + kl + 3);
+                    f32x4 pre;   // bias * log2(e) - lse2 per entry
+                    if constexpr (BCT == BC_NONE) {
+                        pre = f32x4{nlse2, nlse2, nlse2, nlse2};
+                    } else {
+                        const f32x4 bias = *(const f32x4*)(bstrip + (4 * s2 + jj) * 1024 + 16 * lane);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool inside = (unsigned)(rb + e) < (unsigned)p.E;
-                    const float z2 = __builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, inside ? bias[e] * LOG2E : 0.0f);
-                    float pr = __builtin_amdgcn_exp2f(z2 - lse2);
-                    if (my_cls != TILE_FULL && !key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim))
-                        pr = 0.0f;
-                    const float x = pr * (dacc[s2][4 * jj + e] - dlt);
-                    const float dz = pr != 0.0f ? x : 0.0f;
-                    pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz;
-                    const unsigned off = (inside && qin) ? (rowe + (unsigned)(rb + e)) * (unsigned)ES : 0xFFFFFFF0u;
-                    if constexpr (PB)
-                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(__float_as_uint((float)(__bf16)dz) >> 16),
-                                                               drs, off, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dz), drs, off, 0, 0);
+                        for (int e = 0; e < 4; ++e) {
+                            pre[e] = __builtin_fmaf(bias[e], LOG2E, nlse2);
+                            if constexpr (BCT == BC_EDGE)
+                                if ((unsigned)(rb + e) >= (unsigned)p.E) pre[e] = nlse2;
+                        }
+                    }
+                    i32x4 c4;
+                    if constexpr (MASKED) c4 = *(const i32x4*)(ca + kl);
+                    f32x4 dz;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, pre[e]));
+                        const float x = pr * (dacc[s2][4 * jj + e] - dlt);
+                        if constexpr (MASKED)   // (keys that are not real may hold any value)
+                            dz[e] = key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim) ? x : 0.0f;
+                        else
+                            dz[e] = x;
+                        pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz[e];
+                    }
+                    // profile gradients: stores outside this query's row [0, E)
+                    // get an offset past the buffer and are dropped
+                    if constexpr (BCT == BC_FULL) {
+                        const unsigned off = qin ? (rowe + (unsigned)rb) * (unsigned)ES : 0xFFFFFFF0u;
+                        if constexpr (PB) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    (unsigned short)(__float_as_uint((float)(__bf16)dz[e]) >> 16), drs,
+                                    opaque(off + 2u * e), 0, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                i32x4{__float_as_int(dz[0]), __float_as_int(dz[1]), __float_as_int(dz[2]),
+                                      __float_as_int(dz[3])},
+                                drs, off, 0, 0);
+                        }
+                    } else if constexpr (BCT == BC_EDGE) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const bool inside = qin && (unsigned)(rb + e) < (unsigned)p.E;
+                            const unsigned off = inside ? (rowe + (unsigned)(rb + e)) * (unsigned)ES : 0xFFFFFFF0u;
+                            if constexpr (PB)
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    (unsigned short)(__float_as_uint((float)(__bf16)dz[e]) >> 16), drs, off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dz[e]), drs, off, 0, 0);
+                        }
+                    }
                 }
-            }
+        };
+        using F = std::false_type;
+        using T = std::true_type;
+        using NONE = std::integral_constant<int, BC_NONE>;
+        using FULL = std::integral_constant<int, BC_FULL>;
+        using EDGE = std::integral_constant<int, BC_EDGE>;
+        if (my_cls == TILE_FULL) {
+            if (bc == BC_NONE) body(NONE{}, F{});
+            else if (bc == BC_FULL) body(FULL{}, F{});
+            else body(EDGE{}, F{});
+        } else {
+            if (bc == BC_NONE) body(NONE{}, T{});
+            else if (bc == BC_FULL) body(FULL{}, T{});
+            else body(EDGE{}, T{});
+        }
 
         // ---- dQ^T += K^T dS^T (K^T rows in the staged key order)
 #pragma unroll
@@ -669,8 +744,12 @@ void bwd_dkdv_kernel(BwdParams p)
     }
     const int qb_lo = qhi_col >= 0 ? max(0, qlo_col - p.qoff) / BM : 0;
     const int qb_hi = (qhi_col >= 0 && qhi_col >= p.qoff) ? min(p.nQB - 1, (qhi_col - p.qoff) / BM) : -1;
-    auto classify = [&](int x) -> int {
-        if (x > qb_hi) return -1;
+    // Query blocks are walked from the last down to the first, so that the
+    // workgroups on one XCD (one K/V head) stream the same query tiles at
+    // about the same time and share them in L2.  Candidate c is block qb_hi - c.
+    auto classify = [&](int c) -> int {
+        const int x = qb_hi - c;
+        if (x < qb_lo) return -1;
         const TileSummary qs = p.qsum[(size_t)b * p.nQB + x];
         const int xc = min(BM, p.Sq - x * BM);
         const int xlo = p.qoff + x * BM;
@@ -686,56 +765,74 @@ void bwd_dkdv_kernel(BwdParams p)
     };
     Schedule<NSCHED> sch;
     sch.list = (int*)(smem + SCHED_OFF);
-    sch.base = qb_lo;
+    sch.base = 0;
     sch.n = 0;
     sch.i = 0;
 
-    // ---- staging of one (query block, head): every global load is issued
-    // unconditionally one iteration ahead (buffer loads; rows past Sq read as
-    // 0) and stored to LDS at the end of the iteration.
+    // ---- staging of one (query block, head): every global load is a buffer
+    // load issued one iteration ahead (rows past Sq read as 0) and stored to
+    // LDS at the end of the iteration.
     const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
     const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
     const long long qbase = (long long)b * p.Sq * p.Hq * D;
     constexpr int ES = PB ? 2 : 4;
+    const size_t pblock = (size_t)p.Sq * p.E * ES;
+    unsigned qoffs[CPT];
+#pragma unroll
+    for (int n = 0; n < CPT; ++n) {
+        const int u = tid + 64 * NW * n;
+        qoffs[n] = (unsigned)(u / CH) * qrow + 16u * (unsigned)(u % CH);
+    }
+    // bias entry (jj, e) of this lane: row i0 + 8 jj + 4 hh + e, distance
+    // qoff + i - j: offset ((i0 + 4 hh) (E + 1) + qoff - j + (8 jj + e)(E + 1)) ES
+    const unsigned bstep = (unsigned)(p.E + 1) * (unsigned)ES;
+    // Bias class of a block for this wave (its 32 keys): wave-uniform.
+    const int jw = jb0 + 32 * wave;
+    auto bias_class = [&](int x) -> int {
+        const int rmin = p.qoff + x * BM - (jw + 31), rmax = p.qoff + x * BM + BM - 1 - jw;
+        if (rmax < 0 || rmin >= p.E) return BC_NONE;
+        return (rmin >= 0 && rmax < p.E && x * BM + BM <= p.Sq) ? BC_FULL : BC_EDGE;
+    };
     i32x4 sq[CPT], sdo[CPT], sqt[CPT], sdt[CPT];
     i32x4 saux;        // rows 2 l, 2 l + 1 of the block (l = lane % 16): row statistics (even waves) or descriptors (odd)
     float breg[16];    // bias of the next (block, head) at this lane's key: rows 8 jj + 4 hh + e
+    int nbc = BC_NONE;
     auto stage_load = [&](int x, int h) {
         const int i0 = x * BM;
         const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
         const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
+        const size_t tb = ((size_t)b * p.Hq + h) * p.nQB * (size_t)(BM * D);
+        const __amdgpu_buffer_rsrc_t qts = uniform_rsrc(p.qt + tb, (size_t)p.nQB * RBYTES);
+        const __amdgpu_buffer_rsrc_t dts = uniform_rsrc(p.dot + tb, (size_t)p.nQB * RBYTES);
+        const unsigned qb0 = (unsigned)i0 * qrow;
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
             const int u = tid + 64 * NW * n;
-            const int r = u / CH, c = u % CH;
-            const unsigned off = (unsigned)(i0 + r) * qrow + 16u * (unsigned)c;
-            sq[n] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-            sdo[n] = __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0);
-            const size_t to = (((size_t)b * p.Hq + h) * p.nQB + x) * RBYTES + 16 * (size_t)u;
-            sqt[n] = *(const i32x4*)((const char*)p.qt + to);
-            sdt[n] = *(const i32x4*)((const char*)p.dot + to);
+            sq[n] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoffs[n] + qb0, 0, 0);
+            sdo[n] = __builtin_amdgcn_raw_buffer_load_b128(drs, qoffs[n] + qb0, 0, 0);
+            sqt[n] = __builtin_amdgcn_raw_buffer_load_b128(qts, 16u * (unsigned)u, x * RBYTES, 0);
+            sdt[n] = __builtin_amdgcn_raw_buffer_load_b128(dts, 16u * (unsigned)u, x * RBYTES, 0);
         }
         {
-            const int r2 = 2 * (lane & 15);
-            const __amdgpu_buffer_rsrc_t rrs = uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
-            const __amdgpu_buffer_rsrc_t irs = uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8);
             // one 8-byte row per load (each lies wholly inside or past the end)
-            const unsigned off = (unsigned)(i0 + r2) * 8u;
-            const __amdgpu_buffer_rsrc_t xrs = (wave & 1) ? irs : rrs;   // odd waves: descriptors
+            const __amdgpu_buffer_rsrc_t xrs =
+                (wave & 1) ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
+                           : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
+            const unsigned off = (unsigned)(i0 + 2 * (lane & 15)) * 8u;
             const auto lo = __builtin_amdgcn_raw_buffer_load_b64(xrs, off, 0, 0);
             const auto hi = __builtin_amdgcn_raw_buffer_load_b64(xrs, off + 8u, 0, 0);
             saux = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
         }
-        const size_t pblock = (size_t)p.Sq * p.E * ES;
+        nbc = bias_class(x);
+        if (nbc == BC_NONE) return;
         const __amdgpu_buffer_rsrc_t prs =
             uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
+        const unsigned base = ((unsigned)(i0 + 4 * hh) * (unsigned)(p.E + 1) + (unsigned)(p.qoff - j)) * (unsigned)ES;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = i0 + 8 * jj + 4 * hh + e;
-                const int r = p.qoff + i - j;
-                const unsigned off = ((unsigned)i * (unsigned)p.E + (unsigned)r) * (unsigned)ES;
+                const unsigned off = base + (unsigned)(8 * jj + e) * bstep;
                 if constexpr (PB)
                     breg[4 * jj + e] =
                         __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, off, 0, 0) << 16);
@@ -768,14 +865,21 @@ void bwd_dkdv_kernel(BwdParams p)
             }
             *(i32x4*)(st + (wave == 1 ? QI_OFF : RS_OFF) + 16 * lane) = a;
         }
+        if (nbc != BC_NONE) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
-                f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
+            for (int t = 0; t < 4; ++t)
+                *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
+                    f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
+        }
     };
 
     // iteration = (live query block, head of the group)
-    int2 cur = next_entry(sch, qb_hi, classify);
+    auto next_block = [&]() -> int2 {
+        int2 e = next_entry(sch, qb_hi - qb_lo, classify);
+        if (e.x >= 0) e.x = qb_hi - e.x;
+        return e;
+    };
+    int2 cur = next_block();
     int hcur = 0;
     if (cur.x >= 0) {
         stage_load(cur.x, g * p.G);
@@ -790,11 +894,12 @@ void bwd_dkdv_kernel(BwdParams p)
         int2 nxt = cur;
         int hn = hcur + 1;
         if (hn == p.G) {
-            nxt = next_entry(sch, qb_hi, classify);
+            nxt = next_block();
             hn = 0;
         }
         const int i0 = cur.x * BM;
         const int my_cls = (cur.y >> (2 * xk)) & 3;
+        const int bc = bias_class(cur.x);
         const char* st = smem + buf * STAGE;
         if (nxt.x >= 0) stage_load(nxt.x, g * p.G + hn);
 
@@ -809,35 +914,61 @@ void bwd_dkdv_kernel(BwdParams p)
             pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pacc, 0, 0, 0);
         }
 
-        // ---- P and dS; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
+        // ---- P and dS; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4).
+        // dO is 0 on rows that are not real and V on keys that are not real,
+        // so dP is finite everywhere and P = 0 masks dS.
         bf16x8 pb[2], pd[2];
         const float* rsl = (const float*)(st + RS_OFF);
         const int* qil = (const int*)(st + QI_OFF);
+        auto body = [&](auto bct, auto mt) {
+            constexpr int BCT = decltype(bct)::value;
+            constexpr bool MASKED = decltype(mt)::value;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int m0 = 8 * jj + 4 * hh;
-            const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
-            const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
-            const i32x4 qi01 = *(const i32x4*)(qil + 2 * m0);
-            const i32x4 qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
-            const f32x4 bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
-                const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
-                const int r = p.qoff + i0 + m0 + e - j;
-                const float bz = (unsigned)r < (unsigned)p.E ? bias[e] * LOG2E : 0.0f;
-                const float z2 = __builtin_fmaf(sacc[4 * jj + e], p.c_log2, bz);
-                float pr = __builtin_amdgcn_exp2f(z2 - lse2);
-                if (my_cls != TILE_FULL) {
-                    const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
-                    const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
-                    if (!key_visible(gq, aq, j, c_k, wlim)) pr = 0.0f;
+            for (int jj = 0; jj < 4; ++jj) {
+                const int m0 = 8 * jj + 4 * hh;
+                const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
+                const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+                f32x4 bias = f32x4{};
+                if constexpr (BCT != BC_NONE) bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
+                i32x4 qi01, qi23;
+                if constexpr (MASKED) {
+                    qi01 = *(const i32x4*)(qil + 2 * m0);
+                    qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
                 }
-                const float ds = pr != 0.0f ? pr * (pacc[4 * jj + e] - dlt) : 0.0f;
-                pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
-                pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)ds;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
+                    const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
+                    float pre = -lse2;
+                    if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias[e], LOG2E, -lse2);
+                    if constexpr (BCT == BC_EDGE) {
+                        const int r = p.qoff + i0 + m0 + e - j;
+                        if ((unsigned)r < (unsigned)p.E) pre = __builtin_fmaf(bias[e], LOG2E, -lse2);
+                    }
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
+                    if constexpr (MASKED) {
+                        const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
+                        const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
+                        if (!key_visible(gq, aq, j, c_k, wlim)) pr = 0.0f;
+                    }
+                    pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
+                    pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)(pr * (pacc[4 * jj + e] - dlt));
+                }
             }
+        };
+        using F = std::false_type;
+        using T = std::true_type;
+        using NONE = std::integral_constant<int, BC_NONE>;
+        using FULL = std::integral_constant<int, BC_FULL>;
+        using EDGE = std::integral_constant<int, BC_EDGE>;
+        if (my_cls == TILE_FULL) {
+            if (bc == BC_NONE) body(NONE{}, F{});
+            else if (bc == BC_FULL) body(FULL{}, F{});
+            else body(EDGE{}, F{});
+        } else {
+            if (bc == BC_NONE) body(NONE{}, T{});
+            else if (bc == BC_FULL) body(FULL{}, T{});
+            else body(EDGE{}, T{});
         }
 
         // ---- dV^T += dO^T P, dK^T += Q^T dS (transposed tiles in row order)
