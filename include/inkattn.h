@@ -115,9 +115,8 @@ int attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace attn_bwd needs: the pre-pass summaries as for
  * attn_fwd, then per query 8 bytes and per (query, head) row 8 bytes of row
- * statistics, a bf16 copy of dout (B*Sq*Hq*D*2), K^T in whole 64-key tiles
- * (B*Hkv*ceil(Sk/64)*64*D*2) and Q^T and dout^T in whole 32-query tiles
- * (2 * B*Hq*ceil(Sq/32)*32*D*2); each part rounded up to 256 bytes.  Never
+ * statistics, a bf16 copy of dout (B*Sq*Hq*D*2) and K^T in whole 64-key tiles
+ * (B*Hkv*ceil(Sk/64)*64*D*2); each part rounded up to 256 bytes.  Never
  * fails; returns 0 for non-positive B.
  */
 size_t attn_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
@@ -152,8 +151,9 @@ size_t attn_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
  *   dsink      [B, Sq, Hq] fp32, written
  *   workspace  at least attn_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D) bytes,
  *              16-byte aligned; contents on entry are ignored
- * Inputs at tokens that are not valid (q, k, v, dout rows) never reach an
- * output other than their own row's out-of-mask zeros.  The products run in
+ * Inputs at tokens that are not valid never reach an output; as for the
+ * forward, q, k and v there must hold finite values (dout there may hold
+ * anything: it is ignored).  The products run in
  * bf16 MFMA with fp32 accumulation: P and dz are rounded to bf16 for dv / dq /
  * dk, dout for dz and dv.
  */

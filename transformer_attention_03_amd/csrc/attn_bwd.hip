@@ -20,9 +20,8 @@
 //   2. bwd_prep_kernel: per row Delta - dlse, dsink and lse * log2(e); dout
 //      rounded to bf16 rows (0 on rows that are not real); per query its
 //      global column (-1 if not real) and document start column.
-//   3. bwd_stage_kernel: transposed bf16 tiles the products consume as their
-//      A operands: K^T per 64-key tile, Q^T and dO^T per 32-query tile, each
-//      tile's tokens in the order of the accumulator registers they meet.
+//   3. bwd_stage_kernel: K^T per 64-key tile in bf16, the keys in the order of
+//      the dS^T registers the dQ product meets them in.
 //   4. bwd_dq_kernel (query-parallel, one wave per (query head, 32 queries),
 //      keys on MFMA M as in the forward): per 64-key tile S^T = K Q^T and
 //      dP^T = V dO^T, then P and dS from the saved lse, dS written to the
@@ -31,7 +30,10 @@
 //      zeros where no tile it visits puts a value.
 //   5. bwd_dkdv_kernel (key-parallel, one wave per 32 keys, queries on MFMA
 //      M): per (32-query block, head of the group) S = Q K^T, dP = dO V^T,
-//      P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+//      P, dS, then dV^T += dO^T P and dK^T += Q^T dS, the transposed operands
+//      read from the staged rows with transposing LDS reads.  The stages come
+//      by LDS DMA through a ring of three; S / dP of the next block run while
+//      P / dS of this one are computed.
 // Products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the products that consume them.
 #include <hip/hip_runtime.h>
@@ -74,8 +76,6 @@ struct BwdParams {
     float2* rowstat;               // [B, Hq, Sq] {lse * log2(e) (0 when lse = -inf), Delta - dlse}
     __bf16* dob;                   // [B, Sq, Hq, D] bf16 dout, 0 on rows that are not real
     __bf16* kt;                    // [B, Hkv, nKT, D, 64] K^T tiles
-    __bf16* qt;                    // [B, Hq, nQB, D, 32] Q^T tiles
-    __bf16* dot;                   // [B, Hq, nQB, D, 32] dO^T tiles
     float* dq;                     // [B, Sq, Hq, D]
     float* dk;                     // [B, Sk, Hkv, D]
     float* dv;                     // [B, Sk, Hkv, D]
@@ -365,8 +365,9 @@ void bwd_dq_kernel(BwdParams p)
         jlo = min(jlo, lo);
         jhi = max(jhi, min(p.Sk - 1, xhi));
     }
-    const int kt_lo = jhi >= 0 ? jlo / BN : 0;
-    const int kt_hi = jhi >= 0 ? jhi / BN : -1;
+    // (workgroup-uniform; loaded with vector loads, hence the readfirstlane)
+    const int kt_lo = __builtin_amdgcn_readfirstlane(jhi >= 0 ? jlo / BN : 0);
+    const int kt_hi = __builtin_amdgcn_readfirstlane(jhi >= 0 ? jhi / BN : -1);
     // class of tile kt against block x (0 skip / 1 masked / 2 full) in bits 2 (x - qb_first)
     auto classify = [&](int kt) -> int {
         if (kt > kt_hi) return -1;
@@ -683,16 +684,20 @@ void bwd_dkdv_kernel(BwdParams p)
     constexpr int NKK = D / 16;
     constexpr int NDB = D / 32;
     constexpr int CH = D / 8;
-    constexpr int RBYTES = BM * D * 2;       // one 32-row Q / dO tile, or one Q^T / dO^T tile
-    constexpr int Q_OFF = 0, DO_OFF = RBYTES, QT_OFF = 2 * RBYTES, DOT_OFF = 3 * RBYTES;
-    constexpr int RS_OFF = 4 * RBYTES, QI_OFF = 4 * RBYTES + BM * 8;
-    constexpr int STAGE = 4 * RBYTES + 2 * BM * 8;
+    constexpr int RBYTES = BM * D * 2;       // one 32-row Q / dO tile
+    // one stage: Q rows, dO rows, row statistics, query descriptors, and per
+    // wave its 16 bias values per lane; three stages in a ring
+    constexpr int Q_OFF = 0, DO_OFF = RBYTES;
+    constexpr int RS_OFF = 2 * RBYTES, QI_OFF = RS_OFF + BM * 8;
+    constexpr int BS_OFF = QI_OFF + BM * 8;
+    constexpr int STAGE = BS_OFF + NW * 16 * 64 * 4;
+    constexpr int NBUF = 3;
     constexpr int NSCHED = 64 * NW;
-    constexpr int B_OFF = 2 * STAGE;                // per-wave bias strips (16 values per lane)
-    constexpr int SCHED_OFF = B_OFF + NW * 16 * 64 * 4;
+    constexpr int SCHED_OFF = NBUF * STAGE;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
-    constexpr int CPT = BM * CH / (64 * NW);   // chunks per thread of one 32-row tile
-    static_assert(CPT >= 1 && BM * CH % (64 * NW) == 0, "tile chunks must divide among threads");
+    constexpr int NRI = RBYTES / 1024 / NW;    // 1 KB DMA instructions per wave and 32-row tile
+    static_assert(NRI >= 1 && RBYTES % (1024 * NW) == 0, "tile DMA groups must divide among waves");
+    constexpr int N_DMA = 2 * NRI + 1 + 16;    // DMA instructions per wave and stage
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -742,8 +747,10 @@ void bwd_dkdv_kernel(BwdParams p)
         if (p.window > 0) hi = min(hi, xhi + p.window - 1);
         qhi_col = max(qhi_col, hi);
     }
-    const int qb_lo = qhi_col >= 0 ? max(0, qlo_col - p.qoff) / BM : 0;
-    const int qb_hi = (qhi_col >= 0 && qhi_col >= p.qoff) ? min(p.nQB - 1, (qhi_col - p.qoff) / BM) : -1;
+    // (workgroup-uniform; loaded with vector loads, hence the readfirstlane)
+    const int qb_lo = __builtin_amdgcn_readfirstlane(qhi_col >= 0 ? max(0, qlo_col - p.qoff) / BM : 0);
+    const int qb_hi = __builtin_amdgcn_readfirstlane(
+        (qhi_col >= 0 && qhi_col >= p.qoff) ? min(p.nQB - 1, (qhi_col - p.qoff) / BM) : -1);
     // Query blocks are walked from the last down to the first, so that the
     // workgroups on one XCD (one K/V head) stream the same query tiles at
     // about the same time and share them in L2.  Candidate c is block qb_hi - c.
@@ -769,157 +776,195 @@ void bwd_dkdv_kernel(BwdParams p)
     sch.n = 0;
     sch.i = 0;
 
-    // ---- staging of one (query block, head): every global load is a buffer
-    // load issued one iteration ahead (rows past Sq read as 0) and stored to
-    // LDS at the end of the iteration.
+    // ---- staging by LDS DMA (buffer_load ... lds) into a ring of three
+    // stages: the stage of iteration t + 2 is requested at the start of
+    // iteration t.  Every wave issues the same N_DMA instructions per stage
+    // (a stage without bias requests its bias from past the buffer, which
+    // writes zeros), so one vmcnt value marks the stage it waits for.
     const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
     const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
     const long long qbase = (long long)b * p.Sq * p.Hq * D;
     constexpr int ES = PB ? 2 : 4;
     const size_t pblock = (size_t)p.Sq * p.E * ES;
-    unsigned qoffs[CPT];
+    // Q / dO rows: 1 KB group a (of RBYTES / 1024) holds rows RPI a .. RPI a + RPI - 1;
+    // lane -> (row, LDS chunk slot), it fetches the chunk that lands there
+    constexpr int CPR = D / 8, RPI = 1024 / (2 * D);
+    unsigned qv[NRI];
 #pragma unroll
-    for (int n = 0; n < CPT; ++n) {
-        const int u = tid + 64 * NW * n;
-        qoffs[n] = (unsigned)(u / CH) * qrow + 16u * (unsigned)(u % CH);
+    for (int u = 0; u < NRI; ++u) {
+        const int a = wave + NW * u;
+        const int r = RPI * a + lane / CPR, pc = lane % CPR;
+        qv[u] = (unsigned)r * qrow + 16u * (unsigned)(pc ^ row_swz<D>(r));
     }
+    // Transposing reads (ds_read_b64_tr_b16) of the row tiles give the A
+    // operands of dV^T = dO^T P and dK^T = Q^T dS: for query step c and
+    // d-block db, lane l reads 4 bf16 of row 16 c + 4 hh + (l % 16) / 4 (and 8
+    // rows further) at columns 32 db + 16 ((l / 16) % 2) + 4 (l % 4), and
+    // receives column d = 32 db + (l % 32) of the queries 16 c + 4 hh + t and
+    // 16 c + 8 + 4 hh + t, t < 4: the order of the P / dS registers.  trof[]
+    // are the byte offsets of the lane's 8 bytes in the swizzled rows.
+    int trof[2][2][NDB];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int r = 16 * c + 8 * hi + 4 * hh + (lane & 15) / 4;
+                const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // bf16 column
+                trof[c][hi][db] = r * (2 * D) + 16 * ((col / 8) ^ row_swz<D>(r)) + 2 * (col % 8);
+            }
     // bias entry (jj, e) of this lane: row i0 + 8 jj + 4 hh + e, distance
     // qoff + i - j: offset ((i0 + 4 hh) (E + 1) + qoff - j + (8 jj + e)(E + 1)) ES
     const unsigned bstep = (unsigned)(p.E + 1) * (unsigned)ES;
-    // Bias class of a block for this wave (its 32 keys): wave-uniform.
     const int jw = jb0 + 32 * wave;
+    // bias class of a block for this wave (its 32 keys): wave-uniform
     auto bias_class = [&](int x) -> int {
         const int rmin = p.qoff + x * BM - (jw + 31), rmax = p.qoff + x * BM + BM - 1 - jw;
         if (rmax < 0 || rmin >= p.E) return BC_NONE;
         return (rmin >= 0 && rmax < p.E && x * BM + BM <= p.Sq) ? BC_FULL : BC_EDGE;
     };
-    i32x4 sq[CPT], sdo[CPT], sqt[CPT], sdt[CPT];
-    i32x4 saux;        // rows 2 l, 2 l + 1 of the block (l = lane % 16): row statistics (even waves) or descriptors (odd)
-    float breg[16];    // bias of the next (block, head) at this lane's key: rows 8 jj + 4 hh + e
-    int nbc = BC_NONE;
-    auto stage_load = [&](int x, int h) {
+    auto issue = [&](int x, int h, int buf) {
+        char* st = smem + buf * STAGE;
         const int i0 = x * BM;
         const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
         const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
-        const size_t tb = ((size_t)b * p.Hq + h) * p.nQB * (size_t)(BM * D);
-        const __amdgpu_buffer_rsrc_t qts = uniform_rsrc(p.qt + tb, (size_t)p.nQB * RBYTES);
-        const __amdgpu_buffer_rsrc_t dts = uniform_rsrc(p.dot + tb, (size_t)p.nQB * RBYTES);
         const unsigned qb0 = (unsigned)i0 * qrow;
 #pragma unroll
-        for (int n = 0; n < CPT; ++n) {
-            const int u = tid + 64 * NW * n;
-            sq[n] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoffs[n] + qb0, 0, 0);
-            sdo[n] = __builtin_amdgcn_raw_buffer_load_b128(drs, qoffs[n] + qb0, 0, 0);
-            sqt[n] = __builtin_amdgcn_raw_buffer_load_b128(qts, 16u * (unsigned)u, x * RBYTES, 0);
-            sdt[n] = __builtin_amdgcn_raw_buffer_load_b128(dts, 16u * (unsigned)u, x * RBYTES, 0);
+        for (int u = 0; u < NRI; ++u) {
+            const int a = wave + NW * u;
+            const unsigned vo = qv[u] + qb0;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * a), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * a), 16, vo, 0, 0, 0);
         }
         {
-            // one 8-byte row per load (each lies wholly inside or past the end)
+            // row statistics (even waves) or query descriptors (odd waves; the two
+            // waves of a kind write the same bytes): one dword per lane, rows
+            // past Sq read as 0
             const __amdgpu_buffer_rsrc_t xrs =
                 (wave & 1) ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
                            : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
-            const unsigned off = (unsigned)(i0 + 2 * (lane & 15)) * 8u;
-            const auto lo = __builtin_amdgcn_raw_buffer_load_b64(xrs, off, 0, 0);
-            const auto hi = __builtin_amdgcn_raw_buffer_load_b64(xrs, off + 8u, 0, 0);
-            saux = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+            const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + ((wave & 1) ? QI_OFF : RS_OFF)), 4, vo, 0,
+                                                     0, 0);
         }
-        nbc = bias_class(x);
-        if (nbc == BC_NONE) return;
         const __amdgpu_buffer_rsrc_t prs =
             uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
-        const unsigned base = ((unsigned)(i0 + 4 * hh) * (unsigned)(p.E + 1) + (unsigned)(p.qoff - j)) * (unsigned)ES;
+        const bool nobias = bias_class(x) == BC_NONE;
+        const unsigned base =
+            nobias ? 0xFFFFFF00u
+                   : ((unsigned)(i0 + 4 * hh) * (unsigned)(p.E + 1) + (unsigned)(p.qoff - j)) * (unsigned)ES;
+        const unsigned step = nobias ? 0u : bstep;
+        char* bs = st + BS_OFF + wave * (16 * 256);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const unsigned off = base + (unsigned)(8 * jj + e) * bstep;
-                if constexpr (PB)
-                    breg[4 * jj + e] =
-                        __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, off, 0, 0) << 16);
-                else
-                    breg[4 * jj + e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, off, 0, 0));
-            }
-    };
-    char* const bstrip = smem + B_OFF + wave * (16 * 64 * 4);   // this wave's bias, lane-major
-    auto stage_store = [&](int buf, int x) {
-        char* st = smem + buf * STAGE;
-#pragma unroll
-        for (int n = 0; n < CPT; ++n) {
-            const int u = tid + 64 * NW * n;
-            const int r = u / CH, c = u % CH;
-            const int pr = r * (2 * D) + 16 * (c ^ row_swz<D>(r));
-            *(i32x4*)(st + Q_OFF + pr) = sq[n];
-            *(i32x4*)(st + DO_OFF + pr) = sdo[n];
-            // transposed tiles: row d = u / 4 of 32 bf16 (64 B), chunk u % 4
-            const int d = u >> 2, cc = u & 3;
-            const int pt = d * 64 + 16 * (cc ^ ((d >> 2) & 3));
-            *(i32x4*)(st + QT_OFF + pt) = sqt[n];
-            *(i32x4*)(st + DOT_OFF + pt) = sdt[n];
-        }
-        if (wave < 2 && lane < 16) {
-            i32x4 a = saux;
-            if (wave == 1) {   // a row past Sq is not real
-                const int r2 = x * BM + 2 * lane;
-                if (r2 >= p.Sq) a[0] = -1;
-                if (r2 + 1 >= p.Sq) a[2] = -1;
-            }
-            *(i32x4*)(st + (wave == 1 ? QI_OFF : RS_OFF) + 16 * lane) = a;
-        }
-        if (nbc != BC_NONE) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
-                    f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
+        for (int k = 0; k < 16; ++k) {   // k = 4 jj + e
+            const unsigned vo = opaque(base + (unsigned)(8 * (k >> 2) + (k & 3)) * step);
+            // (a 2-byte request lands zero-extended in the lane's dword)
+            if constexpr (PB)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 256 * k), 2, vo, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 256 * k), 4, vo, 0, 0, 0);
         }
     };
 
-    // iteration = (live query block, head of the group)
-    auto next_block = [&]() -> int2 {
-        int2 e = next_entry(sch, qb_hi - qb_lo, classify);
-        if (e.x >= 0) e.x = qb_hi - e.x;
-        return e;
+    // iteration = (live query block, head of the group); descriptors of the
+    // next two are kept for the DMA ahead
+    struct It {
+        int x, code, hs;   // x < 0: none
     };
-    int2 cur = next_block();
-    int hcur = 0;
-    if (cur.x >= 0) {
-        stage_load(cur.x, g * p.G);
-        stage_store(0, cur.x);
-    }
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is outstanding inside it
-#endif
-    __syncthreads();
-    int buf = 0;
-    while (cur.x >= 0) {
-        int2 nxt = cur;
-        int hn = hcur + 1;
-        if (hn == p.G) {
-            nxt = next_block();
-            hn = 0;
+    auto next_block = [&]() -> It {
+        const int2 e = next_entry(sch, qb_hi - qb_lo, classify);
+        It r;
+        r.x = e.x >= 0 ? qb_hi - e.x : -1;
+        r.code = e.y;
+        r.hs = 0;
+        return r;
+    };
+    auto succ = [&](It d) -> It {
+        if (d.x < 0) return d;
+        if (d.hs + 1 < p.G) {
+            d.hs += 1;
+            return d;
         }
-        const int i0 = cur.x * BM;
-        const int my_cls = (cur.y >> (2 * xk)) & 3;
-        const int bc = bias_class(cur.x);
-        const char* st = smem + buf * STAGE;
-        if (nxt.x >= 0) stage_load(nxt.x, g * p.G + hn);
-
-        // ---- S = Q K^T and dP = dO V^T, queries on M (in order)
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        return next_block();
+    };
+    // Software pipeline: iteration t waits for stage t + 1, requests stage
+    // t + 2, runs S / dP of t + 1 on the matrix cores while P / dS of t run on
+    // the vector units, then dV / dK of t.
+    f32x16 sacc, pacc;                 // S, dP of the current iteration
+    auto qk_dp = [&](int bufx, f32x16& sa, f32x16& pa) {
+        const char* st = smem + bufx * STAGE;
+        sa = f32x16{};
+        pa = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const int pr = kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl));
             const bf16x8 aq = *(const bf16x8*)(st + Q_OFF + pr);
             const bf16x8 ad = *(const bf16x8*)(st + DO_OFF + pr);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pacc, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sa, 0, 0, 0);
+            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pa, 0, 0, 0);
         }
+    };
 
-        // ---- P and dS; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4).
-        // dO is 0 on rows that are not real and V on keys that are not real,
-        // so dP is finite everywhere and P = 0 masks dS.
+    It cur = next_block();
+    It n1 = succ(cur);
+    if (cur.x >= 0) {
+        issue(cur.x, g * p.G + cur.hs, 0);
+        if (n1.x >= 0) issue(n1.x, g * p.G + n1.hs, 1);
+        else issue(cur.x, g * p.G + cur.hs, 1);   // (nothing reads it: keeps the count)
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_s_waitcnt((N_DMA & 15) | ((N_DMA >> 4) << 14) | 0x0070);   // vmcnt(N_DMA) lgkmcnt(0)
+#endif
+        asm volatile("s_barrier" ::: "memory");
+        qk_dp(0, sacc, pacc);
+    }
+    int buf = 0;
+    while (cur.x >= 0) {
+        const It n2 = succ(n1);
+        const int nbuf = buf == 2 ? 0 : buf + 1;
+        // every wave's DMA of the next stage has landed, and every wave is done
+        // with the stage the new request overwrites
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+#endif
+        asm volatile("s_barrier" ::: "memory");
+        const char* st = smem + buf * STAGE;
+        // transposed operands of this stage, read while no DMA is in flight
+        // (the compiler would wait for every outstanding DMA before such a read)
+        bf16x8 aqt[2][NDB], adt[2][NDB];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + Q_OFF + trof[c][0][db]));
+                const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + Q_OFF + trof[c][1][db]));
+                const s16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + DO_OFF + trof[c][0][db]));
+                const s16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + DO_OFF + trof[c][1][db]));
+                aqt[c][db] = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
+                adt[c][db] = __builtin_bit_cast(bf16x8, s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]});
+            }
+        {
+            const It d = n2.x >= 0 ? n2 : cur;       // (a copy nothing reads: keeps the count)
+            issue(d.x, g * p.G + d.hs, buf >= 1 ? buf - 1 : 2);   // stage t + 2 -> buffer (buf + 2) % 3
+        }
+        asm volatile("" ::: "memory");
+        const int i0 = cur.x * BM;
+        const int my_cls = (cur.code >> (2 * xk)) & 3;
+        const int bc = bias_class(cur.x);
+
+        // ---- S / dP of the next iteration (matrix cores)
+        f32x16 sn, pn;
+        if (n1.x >= 0) qk_dp(nbuf, sn, pn);
+
+        // ---- P and dS of this one; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4).
+        // dO (and so dP) is 0 on rows that are not real or lie past Sq, and V
+        // on keys that are not real, so dP is finite everywhere and P = 0
+        // masks dS.  (Rows past Sq read as 0 everywhere: whatever weight they
+        // get meets dO = 0 and Q = 0.)
         bf16x8 pb[2], pd[2];
         const float* rsl = (const float*)(st + RS_OFF);
         const int* qil = (const int*)(st + QI_OFF);
+        const float* bsl = (const float*)(st + BS_OFF + wave * (16 * 256));
         auto body = [&](auto bct, auto mt) {
             constexpr int BCT = decltype(bct)::value;
             constexpr bool MASKED = decltype(mt)::value;
@@ -928,8 +973,6 @@ void bwd_dkdv_kernel(BwdParams p)
                 const int m0 = 8 * jj + 4 * hh;
                 const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
                 const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
-                f32x4 bias = f32x4{};
-                if constexpr (BCT != BC_NONE) bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
                 i32x4 qi01, qi23;
                 if constexpr (MASKED) {
                     qi01 = *(const i32x4*)(qil + 2 * m0);
@@ -940,16 +983,24 @@ void bwd_dkdv_kernel(BwdParams p)
                     const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
                     const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
                     float pre = -lse2;
-                    if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias[e], LOG2E, -lse2);
-                    if constexpr (BCT == BC_EDGE) {
-                        const int r = p.qoff + i0 + m0 + e - j;
-                        if ((unsigned)r < (unsigned)p.E) pre = __builtin_fmaf(bias[e], LOG2E, -lse2);
+                    if constexpr (BCT != BC_NONE) {
+                        float bias;
+                        if constexpr (PB)
+                            bias = __uint_as_float(((const unsigned*)bsl)[64 * (4 * jj + e) + lane] << 16);
+                        else
+                            bias = bsl[64 * (4 * jj + e) + lane];
+                        const float wb = __builtin_fmaf(bias, LOG2E, -lse2);
+                        if constexpr (BCT == BC_FULL) pre = wb;
+                        if constexpr (BCT == BC_EDGE) {
+                            const int r = p.qoff + i0 + m0 + e - j;
+                            pre = (unsigned)r < (unsigned)p.E ? wb : pre;
+                        }
                     }
                     float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
                     if constexpr (MASKED) {
                         const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
                         const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
-                        if (!key_visible(gq, aq, j, c_k, wlim)) pr = 0.0f;
+                        pr = key_visible(gq, aq, j, c_k, wlim) ? pr : 0.0f;
                     }
                     pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
                     pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)(pr * (pacc[4 * jj + e] - dlt));
@@ -971,25 +1022,24 @@ void bwd_dkdv_kernel(BwdParams p)
             else body(EDGE{}, T{});
         }
 
-        // ---- dV^T += dO^T P, dK^T += Q^T dS (transposed tiles in row order)
+        // ---- dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int d = 32 * db + kl;
-                const int pt = d * 64 + 16 * ((2 * c + hh) ^ ((d >> 2) & 3));
-                const bf16x8 ado = *(const bf16x8*)(st + DOT_OFF + pt);
-                const bf16x8 aqt = *(const bf16x8*)(st + QT_OFF + pt);
-                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[c], dvacc[db], 0, 0, 0);
-                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt, pd[c], dkacc[db], 0, 0, 0);
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt[c][db], pb[c], dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt[c][db], pd[c], dkacc[db], 0, 0, 0);
             }
-
-        if (nxt.x >= 0) stage_store(buf ^ 1, nxt.x);
-        __syncthreads();
-        buf ^= 1;
-        cur = nxt;
-        hcur = hn;
+        asm volatile("" ::: "memory");
+        sacc = sn;
+        pacc = pn;
+        buf = nbuf;
+        cur = n1;
+        n1 = n2;
     }
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(0);   // no DMA outstanding at exit
+#endif
 
     if (!kin) return;
     const size_t ko = (((size_t)b * p.Sk + j) * p.Hkv + g) * D;
@@ -1018,20 +1068,18 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, s
 // Host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    size_t qinfo, rowstat, dob, kt, qt, dot, total;
+    size_t qinfo, rowstat, dob, kt, total;
 };
 
 BwdLayout bwd_layout(int B, int Sq, int Sk, int Hq, int Hkv, int D)
 {
     BwdLayout l;
-    const size_t nQB = (size_t)ceil_div(Sq, BM), nKT = (size_t)ceil_div(Sk, BN);
+    const size_t nKT = (size_t)ceil_div(Sk, BN);
     size_t o = summaries_bytes(B, Sq, Sk);
     l.qinfo = o;   o += round256((size_t)B * Sq * 8);
     l.rowstat = o; o += round256((size_t)B * Hq * Sq * 8);
     l.dob = o;     o += round256((size_t)B * Sq * Hq * D * 2);
     l.kt = o;      o += round256((size_t)B * Hkv * nKT * BN * D * 2);
-    l.qt = o;      o += round256((size_t)B * Hq * nQB * BM * D * 2);
-    l.dot = o;     o += round256((size_t)B * Hq * nQB * BM * D * 2);
     l.total = o;
     return l;
 }
@@ -1044,17 +1092,10 @@ int launch_bwd(const BwdParams& p, hipStream_t st)
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, p);
     if (int rc = check_launch("bwd_prep_kernel")) return rc;
     const unsigned nkt = (unsigned)((size_t)p.B * p.Hkv * p.nKT);
-    const unsigned nqt = (unsigned)((size_t)p.B * p.Hq * p.nQB);
     if (nkt > 0)
         hipLaunchKernelGGL((bwd_stage_kernel<D, BN, 3, false>), dim3(nkt), dim3((BN / 8) * (D / 8)), 0, st,
                            (const void*)p.k, p.key_valid, p.Sk, p.Hkv, p.nKT, (long long)p.Sk * p.Hkv * D,
                            (long long)p.Hkv * D, (long long)D, p.kt);
-    hipLaunchKernelGGL((bwd_stage_kernel<D, BM, 0, false>), dim3(nqt), dim3((BM / 8) * (D / 8)), 0, st,
-                       (const void*)p.q, p.valid, p.Sq, p.Hq, p.nQB, (long long)p.Sq * p.Hq * D,
-                       (long long)p.Hq * D, (long long)D, p.qt);
-    hipLaunchKernelGGL((bwd_stage_kernel<D, BM, 0, true>), dim3(nqt), dim3((BM / 8) * (D / 8)), 0, st,
-                       (const void*)p.dout, p.valid, p.Sq, p.Hq, p.nQB, (long long)p.Sq * p.Hq * D,
-                       (long long)p.Hq * D, (long long)D, p.dot);
     if (int rc = check_launch("bwd_stage_kernel")) return rc;
     const size_t ndq = (size_t)p.nQG * p.B * p.Hkv * p.nchunk;
     hipLaunchKernelGGL((bwd_dq_kernel<D, PB>), dim3((unsigned)ndq), dim3(64 * BW_WAVES), 0, st, p);
@@ -1150,8 +1191,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* profiles, 
     p.rowstat = (float2*)(ws + lay.rowstat);
     p.dob = (__bf16*)(ws + lay.dob);
     p.kt = (__bf16*)(ws + lay.kt);
-    p.qt = (__bf16*)(ws + lay.qt);
-    p.dot = (__bf16*)(ws + lay.dot);
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
