@@ -690,14 +690,15 @@ void bwd_dkdv_kernel(BwdParams p)
     constexpr int Q_OFF = 0, DO_OFF = RBYTES;
     constexpr int RS_OFF = 2 * RBYTES, QI_OFF = RS_OFF + BM * 8;
     constexpr int BS_OFF = QI_OFF + BM * 8;
-    constexpr int STAGE = BS_OFF + NW * 16 * 64 * 4;
+    constexpr int ES = PB ? 2 : 4;             // profile element bytes
+    constexpr int BSW = 32 * 32 * ES;          // one wave's bias strip: 32 rows x 32 keys
+    constexpr int STAGE = BS_OFF + NW * BSW;
     constexpr int NBUF = 3;
     constexpr int NSCHED = 64 * NW;
     constexpr int SCHED_OFF = NBUF * STAGE;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     constexpr int NRI = RBYTES / 1024 / NW;    // 1 KB DMA instructions per wave and 32-row tile
     static_assert(NRI >= 1 && RBYTES % (1024 * NW) == 0, "tile DMA groups must divide among waves");
-    constexpr int N_DMA = 2 * NRI + 1 + 16;    // DMA instructions per wave and stage
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -778,13 +779,10 @@ void bwd_dkdv_kernel(BwdParams p)
 
     // ---- staging by LDS DMA (buffer_load ... lds) into a ring of three
     // stages: the stage of iteration t + 2 is requested at the start of
-    // iteration t.  Every wave issues the same N_DMA instructions per stage
-    // (a stage without bias requests its bias from past the buffer, which
-    // writes zeros), so one vmcnt value marks the stage it waits for.
+    // iteration t, after the wait for stage t + 1.
     const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
     const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
     const long long qbase = (long long)b * p.Sq * p.Hq * D;
-    constexpr int ES = PB ? 2 : 4;
     const size_t pblock = (size_t)p.Sq * p.E * ES;
     // Q / dO rows: 1 KB group a (of RBYTES / 1024) holds rows RPI a .. RPI a + RPI - 1;
     // lane -> (row, LDS chunk slot), it fetches the chunk that lands there
@@ -814,10 +812,23 @@ void bwd_dkdv_kernel(BwdParams p)
                 const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // bf16 column
                 trof[c][hi][db] = r * (2 * D) + 16 * ((col / 8) ^ row_swz<D>(r)) + 2 * (col % 8);
             }
-    // bias entry (jj, e) of this lane: row i0 + 8 jj + 4 hh + e, distance
-    // qoff + i - j: offset ((i0 + 4 hh) (E + 1) + qoff - j + (8 jj + e)(E + 1)) ES
-    const unsigned bstep = (unsigned)(p.E + 1) * (unsigned)ES;
+    // Bias strip of a wave: for each of its 32 rows the run of 32 distances
+    // of its keys, qoff + i - (jw + 31) .. qoff + i - jw (one contiguous run
+    // of the row, key jw + kl at entry 31 - kl).  Row m = 8 jj + 4 hh + e sits
+    // at slot 8 jj + 2 e + hh, so the two wave halves read adjacent slots.
+    // DMA: 16-byte pieces, lane -> (slot, piece); RSL rows per 1 KB instruction.
+    constexpr int RUNB = 32 * ES;                // bytes of one run
+    constexpr int PPR = RUNB / 16;               // 16-byte pieces per run
+    constexpr int RSL = 64 / PPR;                // slots per DMA instruction
+    constexpr int NBI = 32 / RSL;                // bias DMA instructions per wave
     const int jw = jb0 + 32 * wave;
+    unsigned bvo[NBI];   // per instruction: (row offset within the block) * (E + 1) * ES + piece * 16
+#pragma unroll
+    for (int k = 0; k < NBI; ++k) {
+        const int slot = RSL * k + lane / PPR, piece = lane % PPR;
+        const int m = 8 * (slot / 8) + 4 * (slot & 1) + (slot % 8) / 2;
+        bvo[k] = (unsigned)m * (unsigned)(p.E + 1) * (unsigned)ES + 16u * (unsigned)piece;
+    }
     // bias class of a block for this wave (its 32 keys): wave-uniform
     auto bias_class = [&](int x) -> int {
         const int rmin = p.qoff + x * BM - (jw + 31), rmax = p.qoff + x * BM + BM - 1 - jw;
@@ -837,33 +848,26 @@ void bwd_dkdv_kernel(BwdParams p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * a), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * a), 16, vo, 0, 0, 0);
         }
-        {
-            // row statistics (even waves) or query descriptors (odd waves; the two
-            // waves of a kind write the same bytes): one dword per lane, rows
-            // past Sq read as 0
+        if (wave < 2) {
+            // row statistics (wave 0) or query descriptors (wave 1): one dword
+            // per lane, rows past Sq read as 0
             const __amdgpu_buffer_rsrc_t xrs =
-                (wave & 1) ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
-                           : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
+                wave ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
+                     : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
             const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + ((wave & 1) ? QI_OFF : RS_OFF)), 4, vo, 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + (wave ? QI_OFF : RS_OFF)), 4, vo, 0, 0, 0);
         }
+        if (bias_class(x) == BC_NONE) return;
+        // row i0 + m, run start qoff + i0 + m - jw - 31: entry offset
+        // (i0 + m) E + qoff + i0 + m - jw - 31 = m (E + 1) + i0 (E + 1) + qoff - jw - 31
         const __amdgpu_buffer_rsrc_t prs =
             uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
-        const bool nobias = bias_class(x) == BC_NONE;
-        const unsigned base =
-            nobias ? 0xFFFFFF00u
-                   : ((unsigned)(i0 + 4 * hh) * (unsigned)(p.E + 1) + (unsigned)(p.qoff - j)) * (unsigned)ES;
-        const unsigned step = nobias ? 0u : bstep;
-        char* bs = st + BS_OFF + wave * (16 * 256);
+        const unsigned base = ((unsigned)i0 * (unsigned)(p.E + 1) + (unsigned)(p.qoff - jw - 31)) * (unsigned)ES;
+        char* bs = st + BS_OFF + wave * BSW;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {   // k = 4 jj + e
-            const unsigned vo = opaque(base + (unsigned)(8 * (k >> 2) + (k & 3)) * step);
-            // (a 2-byte request lands zero-extended in the lane's dword)
-            if constexpr (PB)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 256 * k), 2, vo, 0, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 256 * k), 4, vo, 0, 0, 0);
+        for (int k = 0; k < NBI; ++k) {
+            const unsigned vo = opaque(base + bvo[k]);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 1024 * k), 16, vo, 0, 0, 0);
         }
     };
 
@@ -911,9 +915,8 @@ void bwd_dkdv_kernel(BwdParams p)
     if (cur.x >= 0) {
         issue(cur.x, g * p.G + cur.hs, 0);
         if (n1.x >= 0) issue(n1.x, g * p.G + n1.hs, 1);
-        else issue(cur.x, g * p.G + cur.hs, 1);   // (nothing reads it: keeps the count)
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_s_waitcnt((N_DMA & 15) | ((N_DMA >> 4) << 14) | 0x0070);   // vmcnt(N_DMA) lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
 #endif
         asm volatile("s_barrier" ::: "memory");
         qk_dp(0, sacc, pacc);
@@ -943,12 +946,10 @@ void bwd_dkdv_kernel(BwdParams p)
                 aqt[c][db] = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
                 adt[c][db] = __builtin_bit_cast(bf16x8, s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]});
             }
-        {
-            const It d = n2.x >= 0 ? n2 : cur;       // (a copy nothing reads: keeps the count)
-            issue(d.x, g * p.G + d.hs, buf >= 1 ? buf - 1 : 2);   // stage t + 2 -> buffer (buf + 2) % 3
-        }
+        if (n2.x >= 0) issue(n2.x, g * p.G + n2.hs, buf >= 1 ? buf - 1 : 2);   // stage t + 2 -> buffer (buf + 2) % 3
         asm volatile("" ::: "memory");
         const int i0 = cur.x * BM;
+        const int hcur = g * p.G + cur.hs;
         const int my_cls = (cur.code >> (2 * xk)) & 3;
         const int bc = bias_class(cur.x);
 
@@ -964,7 +965,7 @@ void bwd_dkdv_kernel(BwdParams p)
         bf16x8 pb[2], pd[2];
         const float* rsl = (const float*)(st + RS_OFF);
         const int* qil = (const int*)(st + QI_OFF);
-        const float* bsl = (const float*)(st + BS_OFF + wave * (16 * 256));
+        const char* bsl = st + BS_OFF + wave * BSW + ES * (31 - kl);   // + slot * RUNB
         auto body = [&](auto bct, auto mt) {
             constexpr int BCT = decltype(bct)::value;
             constexpr bool MASKED = decltype(mt)::value;
@@ -985,15 +986,23 @@ void bwd_dkdv_kernel(BwdParams p)
                     float pre = -lse2;
                     if constexpr (BCT != BC_NONE) {
                         float bias;
+                        const int slot = 8 * jj + 2 * e + hh;
                         if constexpr (PB)
-                            bias = __uint_as_float(((const unsigned*)bsl)[64 * (4 * jj + e) + lane] << 16);
+                            bias = __uint_as_float((unsigned)*(const unsigned short*)(bsl + slot * RUNB) << 16);
                         else
-                            bias = bsl[64 * (4 * jj + e) + lane];
-                        const float wb = __builtin_fmaf(bias, LOG2E, -lse2);
-                        if constexpr (BCT == BC_FULL) pre = wb;
+                            bias = *(const float*)(bsl + slot * RUNB);
+                        if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
                         if constexpr (BCT == BC_EDGE) {
                             const int r = p.qoff + i0 + m0 + e - j;
-                            pre = (unsigned)r < (unsigned)p.E ? wb : pre;
+                            // a run that starts before the block reads as 0 from a DMA
+                            // piece at a wrapped offset: the block's first 8 entries are
+                            // loaded here (first query blocks only)
+                            const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
+                            if (ent < 8 && (unsigned)r < (unsigned)p.E) {
+                                const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
+                                bias = PB ? (float)((const __bf16*)pr0)[ent] : ((const float*)pr0)[ent];
+                            }
+                            pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
                         }
                     }
                     float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
