@@ -898,16 +898,23 @@ void bwd_dkdv_kernel(BwdParams p)
     f32x16 sacc, pacc;                 // S, dP of the current iteration
     auto qk_dp = [&](int bufx, f32x16& sa, f32x16& pa) {
         const char* st = smem + bufx * STAGE;
+        // every A operand is requested first (one LDS latency for the lot)
+        bf16x8 aq[NKK], ad[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int pr = kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl));
+            aq[kk] = *(const bf16x8*)(st + Q_OFF + pr);
+            ad[kk] = *(const bf16x8*)(st + DO_OFF + pr);
+        }
         sa = f32x16{};
         pa = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const int pr = kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl));
-            const bf16x8 aq = *(const bf16x8*)(st + Q_OFF + pr);
-            const bf16x8 ad = *(const bf16x8*)(st + DO_OFF + pr);
-            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kreg[kk], sa, 0, 0, 0);
-            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vreg[kk], pa, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kreg[kk], sa, 0, 0, 0);
+            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[kk], vreg[kk], pa, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);   // MFMA
     };
 
     It cur = next_block();
