@@ -54,7 +54,8 @@ using namespace inkattn;
 constexpr int BW_WAVES = 4;          // waves per workgroup of both gradient kernels
 // bias class of a tile for one wave: no distance inside [0, E), all inside, mixed
 enum : int { BC_NONE = 0, BC_FULL = 1, BC_EDGE = 2 };
-constexpr int KV_KEYS = 32 * BW_WAVES;   // keys per dK / dV workgroup
+constexpr int KV_WAVES = 8;          // waves per dK / dV workgroup (two per 32-key group)
+constexpr int KV_KEYS = 128;         // keys per dK / dV workgroup
 
 struct BwdParams {
     const __bf16* q;               // [B, Sq, Hq, D]
@@ -671,40 +672,45 @@ void bwd_dq_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV.  One workgroup of 4 waves per (batch row, K/V head, 128 keys);
-// wave w owns keys 32 w .. 32 w + 31 of the block, lane = (key kl, half hh).
-// The workgroup walks the live 32-query blocks and, for each, every query
-// head of the group.
+// dK and dV.  One workgroup of 8 waves per (batch row, K/V head, 128 keys);
+// two waves share each 32-key group (on one SIMD): the P wave (waves 0..3)
+// holds K, computes S = Q K^T and P and accumulates dV^T += dO^T P; the dS
+// wave (waves 4..7) holds V, computes dP = dO V^T, takes P from the P wave
+// through LDS, forms dS and accumulates dK^T += Q^T dS.  Lane = (key kl,
+// half hh).  The workgroup walks the live 32-query blocks (from the last
+// down) and, for each, every query head of the group.
 // ---------------------------------------------------------------------------
 template <int D, bool PB>
-__global__ __launch_bounds__(64 * BW_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * KV_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p)
 {
-    constexpr int NW = BW_WAVES;
+    constexpr int NW = KV_WAVES;
     constexpr int NKK = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int CH = D / 8;
     constexpr int RBYTES = BM * D * 2;       // one 32-row Q / dO tile
-    // one stage: Q rows, dO rows, row statistics, query descriptors, and per
-    // wave its 16 bias values per lane; three stages in a ring
+    // one stage: Q rows, dO rows, row statistics, query descriptors, and the
+    // P waves' bias strips; three stages in a ring, then the P exchange
     constexpr int Q_OFF = 0, DO_OFF = RBYTES;
     constexpr int RS_OFF = 2 * RBYTES, QI_OFF = RS_OFF + BM * 8;
     constexpr int BS_OFF = QI_OFF + BM * 8;
     constexpr int ES = PB ? 2 : 4;             // profile element bytes
-    constexpr int BSW = 32 * 32 * ES;          // one wave's bias strip: 32 rows x 32 keys
-    constexpr int STAGE = BS_OFF + NW * BSW;
-    constexpr int NBUF = 3;
+    constexpr int BSW = 32 * 32 * ES;          // one key group's bias strip: 32 rows x 32 keys
+    constexpr int STAGE = BS_OFF + 4 * BSW;
+    constexpr int NBUF = 4;
+    constexpr int XP_OFF = NBUF * STAGE;       // P of each key group, bf16 in register order (2 KB), two slots
     constexpr int NSCHED = 64 * NW;
-    constexpr int SCHED_OFF = NBUF * STAGE;
+    constexpr int SCHED_OFF = XP_OFF + 2 * 4 * 2048;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     constexpr int NRI = RBYTES / 1024 / NW;    // 1 KB DMA instructions per wave and 32-row tile
-    static_assert(NRI >= 1 && RBYTES % (1024 * NW) == 0, "tile DMA groups must divide among waves");
+    static_assert(NRI >= 1 || RBYTES == 1024 * 4, "");
+    constexpr int NRT = RBYTES / 1024;         // 1 KB groups of a 32-row tile
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3, role = wave >> 2;   // key group; 0: P wave, 1: dS wave
     const int kl = lane & 31, hh = lane >> 5;
 
     int idx = blockIdx.x;
@@ -712,33 +718,30 @@ void bwd_dkdv_kernel(BwdParams p)
     const int b = idx % p.B; idx /= p.B;
     const int kb = idx;                                // key blocks in increasing order
     const int jb0 = kb * KV_KEYS;
-    const int j = jb0 + 32 * wave + kl;
+    const int jw = jb0 + 32 * kg;
+    const int j = jw + kl;
     const bool kin = j < p.Sk;
     const int kt_first = jb0 / BN;
     const int kt_last = min(p.nKT - 1, kt_first + KV_KEYS / BN - 1);
-    const int xk = (32 * wave) / BN;                   // this wave's key tile within the block
+    const int xk = (32 * kg) / BN;                     // this group's key tile within the block
 
     const int c_k = kin ? p.kanchor[(size_t)b * p.nKT * BN + j] : INT_MIN;
     const unsigned wlim = p.window > 0 ? (unsigned)p.window : 0x80000000u;
-    bf16x8 kreg[NKK], vreg[NKK];
+    // K (P waves) or V (dS waves) as the B operand: lane holds 8 d's of its key
+    bf16x8 kvreg[NKK];
     {
         const bool ok = kin && c_k != INT_MIN;
+        const __bf16* src = role ? p.v : p.k;
         const long long off = (((long long)b * p.Sk + j) * p.Hkv + g) * D + 8 * hh;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            kreg[kk] = ok ? *(const bf16x8*)(p.k + off + 16 * kk) : bf16x8{};
-            vreg[kk] = ok ? *(const bf16x8*)(p.v + off + 16 * kk) : bf16x8{};
-        }
+        for (int kk = 0; kk < NKK; ++kk) kvreg[kk] = ok ? *(const bf16x8*)(src + off + 16 * kk) : bf16x8{};
     }
-    f32x16 dkacc[NDB], dvacc[NDB];
+    f32x16 acc[NDB];   // dV^T (P waves) or dK^T (dS waves): rows d, column = key
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-        dkacc[db] = f32x16{};
-        dvacc[db] = f32x16{};
-    }
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
     // ---- query-block range: causal (gi >= first key), window, document
-    int qlo_col = INT_MAX, qhi_col = -1;               // global query columns that may see the block
+    int qlo_col = INT_MAX, qhi_col = -1;
     for (int x = kt_first; x <= kt_last; ++x) {
         const TileSummary s = p.ksum[(size_t)b * p.nKT + x];
         if (s.nvalid == 0) continue;
@@ -778,22 +781,85 @@ void bwd_dkdv_kernel(BwdParams p)
     sch.i = 0;
 
     // ---- staging by LDS DMA (buffer_load ... lds) into a ring of three
-    // stages: the stage of iteration t + 2 is requested at the start of
-    // iteration t, after the wait for stage t + 1.
+    // stages: the stage of iteration t + 2 is requested in iteration t.  Each
+    // wave issues the same number of DMA instructions for every stage (a P
+    // wave asks for its bias from past the buffer when the stage has none),
+    // so one vmcnt value per wave marks the stage it waits for.
     const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
     const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
     const long long qbase = (long long)b * p.Sq * p.Hq * D;
     const size_t pblock = (size_t)p.Sq * p.E * ES;
-    // Q / dO rows: 1 KB group a (of RBYTES / 1024) holds rows RPI a .. RPI a + RPI - 1;
-    // lane -> (row, LDS chunk slot), it fetches the chunk that lands there
+    // Q / dO rows: 1 KB group a holds rows RPI a .. RPI a + RPI - 1; wave w
+    // takes group w of each tile (groups past NRT: none); lane -> (row, LDS
+    // chunk slot), it fetches the chunk that lands there
     constexpr int CPR = D / 8, RPI = 1024 / (2 * D);
-    unsigned qv[NRI];
-#pragma unroll
-    for (int u = 0; u < NRI; ++u) {
-        const int a = wave + NW * u;
+    const bool has_rows = wave < NRT;
+    unsigned qv;
+    {
+        const int a = has_rows ? wave : 0;
         const int r = RPI * a + lane / CPR, pc = lane % CPR;
-        qv[u] = (unsigned)r * qrow + 16u * (unsigned)(pc ^ row_swz<D>(r));
+        qv = (unsigned)r * qrow + 16u * (unsigned)(pc ^ row_swz<D>(r));
     }
+    // Bias strip of a key group: for each of its 32 rows the run of 32
+    // distances of its keys, qoff + i - (jw + 31) .. qoff + i - jw (key jw + kl
+    // at entry 31 - kl).  Row m = 8 jj + 4 hh + e sits at slot 8 jj + 2 e + hh,
+    // so the two wave halves read adjacent slots.
+    constexpr int RUNB = 32 * ES;                // bytes of one run
+    constexpr int PPR = RUNB / 16;               // 16-byte pieces per run
+    constexpr int RSL = 64 / PPR;                // slots per DMA instruction
+    constexpr int NBI = 32 / RSL;                // bias DMA instructions of a P wave
+    unsigned bvo[NBI];
+#pragma unroll
+    for (int k = 0; k < NBI; ++k) {
+        const int slot = RSL * k + lane / PPR, piece = lane % PPR;
+        const int m = 8 * (slot / 8) + 4 * (slot & 1) + (slot % 8) / 2;
+        bvo[k] = (unsigned)m * (unsigned)(p.E + 1) * (unsigned)ES + 16u * (unsigned)piece;
+    }
+    // bias class of a block for a key group (wave-uniform)
+    auto bias_class = [&](int x) -> int {
+        const int rmin = p.qoff + x * BM - (jw + 31), rmax = p.qoff + x * BM + BM - 1 - jw;
+        if (rmax < 0 || rmin >= p.E) return BC_NONE;
+        return (rmin >= 0 && rmax < p.E && x * BM + BM <= p.Sq) ? BC_FULL : BC_EDGE;
+    };
+    // DMA instructions of one stage for this wave (the same for every stage)
+    const int n_dma = (has_rows ? 2 : 0) + (wave < 2 ? 1 : 0) + (role == 0 ? NBI : 0);
+    auto issue = [&](int x, int h, int buf) {
+        char* st = smem + buf * STAGE;
+        const int i0 = x * BM;
+        if (has_rows) {
+            const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
+            const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
+            const unsigned vo = qv + (unsigned)i0 * qrow;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * wave), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * wave), 16, vo, 0, 0, 0);
+        }
+        if (wave < 2) {
+            // row statistics (wave 0) or query descriptors (wave 1): one dword
+            // per lane, rows past Sq read as 0
+            const __amdgpu_buffer_rsrc_t xrs =
+                wave ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
+                     : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
+            const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + (wave ? QI_OFF : RS_OFF)), 4, vo, 0, 0, 0);
+        }
+        if (role == 0) {
+            // row i0 + m, run start qoff + i0 + m - jw - 31: entry offset
+            // (i0 + m) E + qoff + i0 + m - jw - 31 = m (E + 1) + i0 (E + 1) + qoff - jw - 31
+            const __amdgpu_buffer_rsrc_t prs =
+                uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
+            const bool nobias = bias_class(x) == BC_NONE;
+            const unsigned base =
+                nobias ? 0xFFFFF000u
+                       : ((unsigned)i0 * (unsigned)(p.E + 1) + (unsigned)(p.qoff - jw - 31)) * (unsigned)ES;
+            const unsigned step = nobias ? 0u : 1u;
+            char* bs = st + BS_OFF + kg * BSW;
+#pragma unroll
+            for (int k = 0; k < NBI; ++k) {
+                const unsigned vo = opaque(base + bvo[k] * step);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 1024 * k), 16, vo, 0, 0, 0);
+            }
+        }
+    };
     // Transposing reads (ds_read_b64_tr_b16) of the row tiles give the A
     // operands of dV^T = dO^T P and dK^T = Q^T dS: for query step c and
     // d-block db, lane l reads 4 bf16 of row 16 c + 4 hh + (l % 16) / 4 (and 8
@@ -812,64 +878,6 @@ void bwd_dkdv_kernel(BwdParams p)
                 const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // bf16 column
                 trof[c][hi][db] = r * (2 * D) + 16 * ((col / 8) ^ row_swz<D>(r)) + 2 * (col % 8);
             }
-    // Bias strip of a wave: for each of its 32 rows the run of 32 distances
-    // of its keys, qoff + i - (jw + 31) .. qoff + i - jw (one contiguous run
-    // of the row, key jw + kl at entry 31 - kl).  Row m = 8 jj + 4 hh + e sits
-    // at slot 8 jj + 2 e + hh, so the two wave halves read adjacent slots.
-    // DMA: 16-byte pieces, lane -> (slot, piece); RSL rows per 1 KB instruction.
-    constexpr int RUNB = 32 * ES;                // bytes of one run
-    constexpr int PPR = RUNB / 16;               // 16-byte pieces per run
-    constexpr int RSL = 64 / PPR;                // slots per DMA instruction
-    constexpr int NBI = 32 / RSL;                // bias DMA instructions per wave
-    const int jw = jb0 + 32 * wave;
-    unsigned bvo[NBI];   // per instruction: (row offset within the block) * (E + 1) * ES + piece * 16
-#pragma unroll
-    for (int k = 0; k < NBI; ++k) {
-        const int slot = RSL * k + lane / PPR, piece = lane % PPR;
-        const int m = 8 * (slot / 8) + 4 * (slot & 1) + (slot % 8) / 2;
-        bvo[k] = (unsigned)m * (unsigned)(p.E + 1) * (unsigned)ES + 16u * (unsigned)piece;
-    }
-    // bias class of a block for this wave (its 32 keys): wave-uniform
-    auto bias_class = [&](int x) -> int {
-        const int rmin = p.qoff + x * BM - (jw + 31), rmax = p.qoff + x * BM + BM - 1 - jw;
-        if (rmax < 0 || rmin >= p.E) return BC_NONE;
-        return (rmin >= 0 && rmax < p.E && x * BM + BM <= p.Sq) ? BC_FULL : BC_EDGE;
-    };
-    auto issue = [&](int x, int h, int buf) {
-        char* st = smem + buf * STAGE;
-        const int i0 = x * BM;
-        const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
-        const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
-        const unsigned qb0 = (unsigned)i0 * qrow;
-#pragma unroll
-        for (int u = 0; u < NRI; ++u) {
-            const int a = wave + NW * u;
-            const unsigned vo = qv[u] + qb0;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * a), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * a), 16, vo, 0, 0, 0);
-        }
-        if (wave < 2) {
-            // row statistics (wave 0) or query descriptors (wave 1): one dword
-            // per lane, rows past Sq read as 0
-            const __amdgpu_buffer_rsrc_t xrs =
-                wave ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
-                     : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
-            const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + (wave ? QI_OFF : RS_OFF)), 4, vo, 0, 0, 0);
-        }
-        if (bias_class(x) == BC_NONE) return;
-        // row i0 + m, run start qoff + i0 + m - jw - 31: entry offset
-        // (i0 + m) E + qoff + i0 + m - jw - 31 = m (E + 1) + i0 (E + 1) + qoff - jw - 31
-        const __amdgpu_buffer_rsrc_t prs =
-            uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
-        const unsigned base = ((unsigned)i0 * (unsigned)(p.E + 1) + (unsigned)(p.qoff - jw - 31)) * (unsigned)ES;
-        char* bs = st + BS_OFF + wave * BSW;
-#pragma unroll
-        for (int k = 0; k < NBI; ++k) {
-            const unsigned vo = opaque(base + bvo[k]);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 1024 * k), 16, vo, 0, 0, 0);
-        }
-    };
 
     // iteration = (live query block, head of the group); descriptors of the
     // next two are kept for the DMA ahead
@@ -892,164 +900,182 @@ void bwd_dkdv_kernel(BwdParams p)
         }
         return next_block();
     };
-    // Software pipeline: iteration t waits for stage t + 1, requests stage
-    // t + 2, runs S / dP of t + 1 on the matrix cores while P / dS of t run on
-    // the vector units, then dV / dK of t.
-    f32x16 sacc, pacc;                 // S, dP of the current iteration
-    auto qk_dp = [&](int bufx, f32x16& sa, f32x16& pa) {
-        const char* st = smem + bufx * STAGE;
-        // every A operand is requested first (one LDS latency for the lot)
-        bf16x8 aq[NKK], ad[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const int pr = kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl));
-            aq[kk] = *(const bf16x8*)(st + Q_OFF + pr);
-            ad[kk] = *(const bf16x8*)(st + DO_OFF + pr);
-        }
-        sa = f32x16{};
-        pa = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kreg[kk], sa, 0, 0, 0);
-            pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[kk], vreg[kk], pa, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);   // MFMA
-    };
-
+    // The dS wave runs one iteration behind its P wave: in iteration t the P
+    // wave forms P of (block, head) t from stage t and the dS wave uses P of
+    // t - 1 (exchange slot (t - 1) % 2) with stage t - 1, so the two need no
+    // barrier between them; a last iteration drains the dS waves.  Stages:
+    // t - 1 and t in use, t + 1 in flight, t + 2 requested: a ring of four.
     It cur = next_block();
     It n1 = succ(cur);
+    It prv;
+    prv.x = -1;
+    prv.code = 0;
+    prv.hs = 0;
     if (cur.x >= 0) {
         issue(cur.x, g * p.G + cur.hs, 0);
-        if (n1.x >= 0) issue(n1.x, g * p.G + n1.hs, 1);
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-#endif
-        asm volatile("s_barrier" ::: "memory");
-        qk_dp(0, sacc, pacc);
+        const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads: keeps the count)
+        issue(d.x, g * p.G + d.hs, 1);
     }
-    int buf = 0;
-    while (cur.x >= 0) {
+    int buf = 0, par = 0;
+    while (cur.x >= 0 || prv.x >= 0) {
         const It n2 = succ(n1);
-        const int nbuf = buf == 2 ? 0 : buf + 1;
-        // every wave's DMA of the next stage has landed, and every wave is done
-        // with the stage the new request overwrites
+        // this wave's DMA of stage t has landed (stage t + 1's may still be in
+        // flight); after the barrier every wave's has, every wave is done with
+        // the buffer the next request overwrites and with the exchange slot
+        // the P waves write now
+        switch (n_dma) {   // s_waitcnt vmcnt(n_dma) lgkmcnt(0) (operand must be a constant)
 #if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0073); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0075); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0077); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0070); break;
 #endif
+        }
         asm volatile("s_barrier" ::: "memory");
-        const char* st = smem + buf * STAGE;
-        // transposed operands of this stage, read while no DMA is in flight
-        // (the compiler would wait for every outstanding DMA before such a read)
-        bf16x8 aqt[2][NDB], adt[2][NDB];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const s16x4 q0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + Q_OFF + trof[c][0][db]));
-                const s16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + Q_OFF + trof[c][1][db]));
-                const s16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + DO_OFF + trof[c][0][db]));
-                const s16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + DO_OFF + trof[c][1][db]));
-                aqt[c][db] = __builtin_bit_cast(bf16x8, s16x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
-                adt[c][db] = __builtin_bit_cast(bf16x8, s16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]});
-            }
-        if (n2.x >= 0) issue(n2.x, g * p.G + n2.hs, buf >= 1 ? buf - 1 : 2);   // stage t + 2 -> buffer (buf + 2) % 3
+        {
+            const It d = n2.x >= 0 ? n2 : (cur.x >= 0 ? cur : prv);   // (a copy nothing reads: keeps the count)
+            issue(d.x, g * p.G + d.hs, (buf + 2) & 3);                // stage t + 2
+        }
         asm volatile("" ::: "memory");
-        const int i0 = cur.x * BM;
-        const int hcur = g * p.G + cur.hs;
-        const int my_cls = (cur.code >> (2 * xk)) & 3;
-        const int bc = bias_class(cur.x);
+        // the P wave's work is (block, head) t; the dS wave's is t - 1
+        const It w = role ? prv : cur;
+        if (w.x >= 0) {
+            const char* st = smem + (role ? ((buf + 3) & 3) : buf) * STAGE;
+            char* const xp = smem + XP_OFF + (role ? par ^ 1 : par) * 8192 + kg * 2048 + 32 * lane;
+            const int i0 = w.x * BM;
+            const int hcur = g * p.G + w.hs;
+            const int my_cls = (w.code >> (2 * xk)) & 3;
+            const float* rsl = (const float*)(st + RS_OFF);
 
-        // ---- S / dP of the next iteration (matrix cores)
-        f32x16 sn, pn;
-        if (n1.x >= 0) qk_dp(nbuf, sn, pn);
+            // ---- S (P waves) or dP (dS waves): A operands are the Q or dO rows
+            f32x16 sacc;
+            {
+                const char* rows = st + (role ? DO_OFF : Q_OFF);
+                bf16x8 ar[NKK];
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+                    ar[kk] = *(const bf16x8*)(rows + kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl)));
+                sacc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[kk], kvreg[kk], sacc, 0, 0, 0);
+            }
 
-        // ---- P and dS of this one; pb / pd hold queries 16 c + 8 (t / 4) + 4 hh + (t % 4).
-        // dO (and so dP) is 0 on rows that are not real or lie past Sq, and V
-        // on keys that are not real, so dP is finite everywhere and P = 0
-        // masks dS.  (Rows past Sq read as 0 everywhere: whatever weight they
-        // get meets dO = 0 and Q = 0.)
-        bf16x8 pb[2], pd[2];
-        const float* rsl = (const float*)(st + RS_OFF);
-        const int* qil = (const int*)(st + QI_OFF);
-        const char* bsl = st + BS_OFF + wave * BSW + ES * (31 - kl);   // + slot * RUNB
-        auto body = [&](auto bct, auto mt) {
-            constexpr int BCT = decltype(bct)::value;
-            constexpr bool MASKED = decltype(mt)::value;
+            bf16x8 pb[2];   // P (P waves) / dS (dS waves): queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
+            if (role == 0) {
+                // ---- P = exp2(S c + bias log2(e) - lse2), masked
+                const int bc = bias_class(w.x);
+                const int* qil = (const int*)(st + QI_OFF);
+                const char* bsl = st + BS_OFF + kg * BSW + ES * (31 - kl);   // + slot * RUNB
+                auto body = [&](auto bct, auto mt) {
+                    constexpr int BCT = decltype(bct)::value;
+                    constexpr bool MASKED = decltype(mt)::value;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int m0 = 8 * jj + 4 * hh;
-                const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
-                const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
-                i32x4 qi01, qi23;
-                if constexpr (MASKED) {
-                    qi01 = *(const i32x4*)(qil + 2 * m0);
-                    qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
-                }
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int m0 = 8 * jj + 4 * hh;
+                        const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
+                        const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+                        i32x4 qi01, qi23;
+                        if constexpr (MASKED) {
+                            qi01 = *(const i32x4*)(qil + 2 * m0);
+                            qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
+                        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
-                    const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
-                    float pre = -lse2;
-                    if constexpr (BCT != BC_NONE) {
-                        float bias;
-                        const int slot = 8 * jj + 2 * e + hh;
-                        if constexpr (PB)
-                            bias = __uint_as_float((unsigned)*(const unsigned short*)(bsl + slot * RUNB) << 16);
-                        else
-                            bias = *(const float*)(bsl + slot * RUNB);
-                        if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
-                        if constexpr (BCT == BC_EDGE) {
-                            const int r = p.qoff + i0 + m0 + e - j;
-                            // a run that starts before the block reads as 0 from a DMA
-                            // piece at a wrapped offset: the block's first 8 entries are
-                            // loaded here (first query blocks only)
-                            const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
-                            if (ent < 8 && (unsigned)r < (unsigned)p.E) {
-                                const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
-                                bias = PB ? (float)((const __bf16*)pr0)[ent] : ((const float*)pr0)[ent];
+                        for (int e = 0; e < 4; ++e) {
+                            const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
+                            float pre = -lse2;
+                            if constexpr (BCT != BC_NONE) {
+                                const int slot = 8 * jj + 2 * e + hh;
+                                float bias;
+                                if constexpr (PB)
+                                    bias = __uint_as_float((unsigned)*(const unsigned short*)(bsl + slot * RUNB) << 16);
+                                else
+                                    bias = *(const float*)(bsl + slot * RUNB);
+                                if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
+                                if constexpr (BCT == BC_EDGE) {
+                                    const int r = p.qoff + i0 + m0 + e - j;
+                                    // a run that starts before the block reads as 0 from a DMA
+                                    // piece at a wrapped offset: the block's first 8 entries are
+                                    // loaded here (first query blocks only)
+                                    const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
+                                    if (ent < 8 && (unsigned)r < (unsigned)p.E) {
+                                        const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
+                                        bias = PB ? (float)((const __bf16*)pr0)[ent] : ((const float*)pr0)[ent];
+                                    }
+                                    pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
+                                }
                             }
-                            pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
+                            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
+                            if constexpr (MASKED) {
+                                const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
+                                const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
+                                pr = key_visible(gq, aq, j, c_k, wlim) ? pr : 0.0f;
+                            }
+                            pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
                         }
                     }
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
-                    if constexpr (MASKED) {
-                        const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
-                        const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
-                        pr = key_visible(gq, aq, j, c_k, wlim) ? pr : 0.0f;
+                };
+                using F = std::false_type;
+                using T = std::true_type;
+                using NONE = std::integral_constant<int, BC_NONE>;
+                using FULL = std::integral_constant<int, BC_FULL>;
+                using EDGE = std::integral_constant<int, BC_EDGE>;
+                if (my_cls == TILE_FULL) {
+                    if (bc == BC_NONE) body(NONE{}, F{});
+                    else if (bc == BC_FULL) body(FULL{}, F{});
+                    else body(EDGE{}, F{});
+                } else {
+                    if (bc == BC_NONE) body(NONE{}, T{});
+                    else if (bc == BC_FULL) body(FULL{}, T{});
+                    else body(EDGE{}, T{});
+                }
+                *(bf16x8*)(xp) = pb[0];
+                *(bf16x8*)(xp + 16) = pb[1];
+            } else {
+                // ---- dS = P (dP - (Delta - dlse)); dO (so dP) is 0 on rows that
+                // are not real or lie past Sq, and V on keys that are not real, so
+                // dP is finite everywhere and P = 0 masks dS
+                const bf16x8 p0 = *(const bf16x8*)(xp);
+                const bf16x8 p1 = *(const bf16x8*)(xp + 16);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int m0 = 8 * jj + 4 * hh;
+                    const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
+                    const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
+                        const int t = 4 * (jj & 1) + e;
+                        const float pr = (float)((jj >> 1) ? p1[t] : p0[t]);
+                        pb[jj >> 1][t] = (__bf16)(pr * (sacc[4 * jj + e] - dlt));
                     }
-                    pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
-                    pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)(pr * (pacc[4 * jj + e] - dlt));
                 }
             }
-        };
-        using F = std::false_type;
-        using T = std::true_type;
-        using NONE = std::integral_constant<int, BC_NONE>;
-        using FULL = std::integral_constant<int, BC_FULL>;
-        using EDGE = std::integral_constant<int, BC_EDGE>;
-        if (my_cls == TILE_FULL) {
-            if (bc == BC_NONE) body(NONE{}, F{});
-            else if (bc == BC_FULL) body(FULL{}, F{});
-            else body(EDGE{}, F{});
-        } else {
-            if (bc == BC_NONE) body(NONE{}, T{});
-            else if (bc == BC_FULL) body(FULL{}, T{});
-            else body(EDGE{}, T{});
-        }
 
-        // ---- dV^T += dO^T P, dK^T += Q^T dS
+            // ---- dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves); the
+            // transposed operands come from the rows by transposing LDS reads
+            {
+                const char* rows = st + (role ? Q_OFF : DO_OFF);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adt[c][db], pb[c], dvacc[db], 0, 0, 0);
-                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aqt[c][db], pd[c], dkacc[db], 0, 0, 0);
+                    for (int db = 0; db < NDB; ++db) {
+                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + trof[c][0][db]));
+                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + trof[c][1][db]));
+                        const bf16x8 a =
+                            __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[db], 0, 0, 0);
+                    }
             }
+        }
         asm volatile("" ::: "memory");
-        sacc = sn;
-        pacc = pn;
-        buf = nbuf;
+        buf = (buf + 1) & 3;
+        par ^= 1;
+        prv = cur;
         cur = n1;
         n1 = n2;
     }
@@ -1059,19 +1085,16 @@ void bwd_dkdv_kernel(BwdParams p)
 
     if (!kin) return;
     const size_t ko = (((size_t)b * p.Sk + j) * p.Hkv + g) * D;
+    float* const dst = role ? p.dk : p.dv;
+    const float sc = role ? p.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            f32x4 wk, wv;
+            f32x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wk[e] = dkacc[db][4 * jj + e] * p.scale;
-                wv[e] = dvacc[db][4 * jj + e];
-            }
-            const int d0 = 32 * db + 8 * jj + 4 * hh;
-            *(f32x4*)(p.dk + ko + d0) = wk;
-            *(f32x4*)(p.dv + ko + d0) = wv;
+            for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * jj + e] * sc;
+            *(f32x4*)(dst + ko + 32 * db + 8 * jj + 4 * hh) = w;
         }
 }
 
@@ -1118,7 +1141,7 @@ int launch_bwd(const BwdParams& p, hipStream_t st)
     if (int rc = check_launch("bwd_dq_kernel")) return rc;
     const size_t nkv = (size_t)p.nKB * p.B * p.Hkv;
     if (nkv == 0) return INKATTN_OK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, PB>), dim3((unsigned)nkv), dim3(64 * BW_WAVES), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, PB>), dim3((unsigned)nkv), dim3(64 * KV_WAVES), 0, st, p);
     return check_launch("bwd_dkdv_kernel");
 }
 
