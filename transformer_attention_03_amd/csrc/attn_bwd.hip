@@ -103,11 +103,13 @@ __device__ __forceinline__ int stage_token(int slot, int X)
 }
 
 // XOR swizzle of the 16-byte chunks of a staged row of D bf16 (row pitch
-// 2 D bytes): 16 consecutive rows read at one logical chunk hit 16 distinct
-// groups of 4 banks.
+// 2 D bytes).  D = 128: the two 2-bit fields of r mod 16 are swapped, so that
+// 16 consecutive rows read at one logical chunk hit 16 distinct groups of 4
+// banks, and so do 4 consecutive rows read at 4 consecutive logical chunks
+// (the pattern of a transposing read).
 template <int D> __device__ __forceinline__ int row_swz(int r)
 {
-    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
 }
 
 // Buffer resource over nrec bytes from base (reads past nrec return 0,
@@ -945,7 +947,7 @@ void bwd_dkdv_kernel(BwdParams p)
         const It w = role ? prv : cur;
         if (w.x >= 0) {
             const char* st = smem + (role ? ((buf + 3) & 3) : buf) * STAGE;
-            char* const xp = smem + XP_OFF + (role ? par ^ 1 : par) * 8192 + kg * 2048 + 32 * lane;
+            char* const xp = smem + XP_OFF + (role ? par ^ 1 : par) * 8192 + kg * 2048 + 16 * lane;   // + 1024 h
             const int i0 = w.x * BM;
             const int hcur = g * p.G + w.hs;
             const int my_cls = (w.code >> (2 * xk)) & 3;
@@ -1034,13 +1036,13 @@ void bwd_dkdv_kernel(BwdParams p)
                     else body(EDGE{}, T{});
                 }
                 *(bf16x8*)(xp) = pb[0];
-                *(bf16x8*)(xp + 16) = pb[1];
+                *(bf16x8*)(xp + 1024) = pb[1];
             } else {
                 // ---- dS = P (dP - (Delta - dlse)); dO (so dP) is 0 on rows that
                 // are not real or lie past Sq, and V on keys that are not real, so
                 // dP is finite everywhere and P = 0 masks dS
                 const bf16x8 p0 = *(const bf16x8*)(xp);
-                const bf16x8 p1 = *(const bf16x8*)(xp + 16);
+                const bf16x8 p1 = *(const bf16x8*)(xp + 1024);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int m0 = 8 * jj + 4 * hh;
