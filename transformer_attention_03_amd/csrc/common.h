@@ -109,6 +109,18 @@ __host__ __device__ constexpr int vt_slot(int key)   // key within the tile -> s
 }
 __device__ __forceinline__ int vt_swz(int d) { return (d >> 1) & 7; }
 
+// Buffer resource over nrec bytes from base (reads past nrec return 0,
+// writes past it are dropped).  The address and size go through
+// readfirstlane, so the resource is known to be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, size_t nrec)
+{
+    const unsigned long long a = (unsigned long long)base;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    const unsigned n = __builtin_amdgcn_readfirstlane((unsigned)nrec);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((unsigned long long)hi << 32) | lo), 0, n, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // Host helpers (inkattn.hip)
 // ---------------------------------------------------------------------------

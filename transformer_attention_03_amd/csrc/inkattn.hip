@@ -286,12 +286,15 @@ void attn_fwd_kernel(FwdParams p)
     // decreasing order (longest first for causal work).
     int idx = blockIdx.x;
     const int ngroups = p.Hkv * p.nchunk;
-    const int hgi = idx % ngroups; idx /= ngroups;
-    const int b = idx % p.B; idx /= p.B;
-    const int qg = p.nQG - 1 - idx;
-    const int g = hgi / p.nchunk;
-    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + wave % p.hpw;
-    const int qb = qg * p.tpw + wave / p.hpw;        // this wave's query block (may be past the end)
+    // (divisions by kernel arguments go through the vector unit: readfirstlane
+    // tells the compiler that these wave-uniform values are, so the buffer
+    // resources built from them stay in scalar registers)
+    const int hgi = __builtin_amdgcn_readfirstlane(idx % ngroups); idx /= ngroups;
+    const int b = __builtin_amdgcn_readfirstlane(idx % p.B); idx /= p.B;
+    const int qg = __builtin_amdgcn_readfirstlane(p.nQG - 1 - idx);
+    const int g = __builtin_amdgcn_readfirstlane(hgi / p.nchunk);
+    const int h = __builtin_amdgcn_readfirstlane(g * p.G + (hgi - g * p.nchunk) * p.hpw + wave % p.hpw);
+    const int qb = __builtin_amdgcn_readfirstlane(qg * p.tpw + wave / p.hpw);   // this wave's query block (may be past the end)
     const int i0 = qb * BM;
 
     // query blocks of the workgroup: qg*tpw .. qg*tpw + tpw - 1
@@ -407,11 +410,9 @@ void attn_fwd_kernel(FwdParams p)
     // covers the staged tiles of this (batch row, K/V head).
     const int krow = (int)p.k_ts * 2;                   // bytes between consecutive keys
     const unsigned nrec = p.Sk > 0 ? (unsigned)((size_t)(p.Sk - 1) * krow + D * 2) : 0u;
-    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.k + b * p.k_bs + g * p.k_hs), 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.v16 + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(D * BN)), 0,
-        (unsigned)p.nKT * (unsigned)VBYTES, 0x00020000);
+    const __amdgpu_buffer_rsrc_t krsrc = uniform_rsrc(p.k + b * p.k_bs + g * p.k_hs, nrec);
+    const __amdgpu_buffer_rsrc_t vrsrc = uniform_rsrc(
+        p.v16 + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(D * BN), (size_t)p.nKT * VBYTES);
     // K: lane -> (row t of its DMA group, LDS chunk slot pc): it fetches the chunk that lands there
     const int dt = lane / CPR, dpc = lane % CPR;
     const int kvoff = dt * krow + 16 * (dpc ^ L::ksw(dt));
@@ -419,8 +420,7 @@ void attn_fwd_kernel(FwdParams p)
     // groups of a wave all have the parity of the wave (NW is even)
     const int vvoff = (lane / 8) * 128 + 16 * ((lane % 8) ^ vt_swz(8 * (wave & 1) + lane / 8));
     // key start columns of this batch row, padded to whole tiles with INT_MIN
-    const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.kanchor + (size_t)b * p.nKT * BN), 0, (unsigned)p.nKT * BN * 4u, 0x00020000);
+    const __amdgpu_buffer_rsrc_t arsrc = uniform_rsrc(p.kanchor + (size_t)b * p.nKT * BN, (size_t)p.nKT * BN * 4);
     auto issue_tile = [&](const TileDesc& d, int bufsel, int vsel) {
         const int j0 = d.kt * BN;
 #pragma unroll
@@ -473,9 +473,8 @@ void attn_fwd_kernel(FwdParams p)
     // a buffer resource over this (batch row, head)'s [Sq, E] block, and reads
     // outside the block return 0.
     constexpr int PE = PROF_BF16 ? 2 : 4;               // bytes per profile entry
-    const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)p.profiles + ((size_t)b * p.Hq + h) * p.Sq * p.E * PE), 0,
-        (unsigned)((size_t)p.Sq * p.E * PE), 0x00020000);
+    const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(
+        (const char*)p.profiles + ((size_t)b * p.Hq + h) * p.Sq * p.E * PE, (size_t)p.Sq * p.E * PE);
     // Byte offset of distance gi - 4 hh - 30 in this lane's row, in wrapping
     // 32-bit arithmetic (it may lie before the row: every entry read below is
     // at most 30 entries after it).  The buffer hardware range-checks the
