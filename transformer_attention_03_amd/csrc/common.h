@@ -29,6 +29,7 @@ typedef float f32x4_u __attribute__((ext_vector_type(4), aligned(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // Per-tile summary written by the pre-pass: document start columns of the
@@ -81,6 +82,26 @@ __device__ __forceinline__ unsigned opaque(unsigned x)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("" : "+v"(x));
+#endif
+    return x;
+}
+
+// A wave-uniform value the compiler may not look through (kept in a scalar
+// register; values derived from it are recomputed where they are used).
+__device__ __forceinline__ unsigned opaque_s(unsigned x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+s"(x));
+#endif
+    return x;
+}
+
+// An LDS address the compiler may not look through: derived addresses are
+// recomputed where they are used instead of being held in registers.
+__device__ __forceinline__ lds_char* opaque_lds(lds_char* x)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+s"(x));
 #endif
     return x;
 }

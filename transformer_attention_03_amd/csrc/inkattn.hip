@@ -269,7 +269,7 @@ void attn_fwd_kernel(FwdParams p)
     // tile schedule: one entry per live key tile of a round of NSCHED tiles,
     // plus a count per wave
     constexpr int NSCHED = 64 * NW;
-    constexpr int SCHED_OFF = B_OFF + (PROF_BF16 ? 0 : NW * BSTRIP);
+    constexpr int SCHED_OFF = B_OFF + NW * BSTRIP;
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
     // vector-memory instructions of one tile's K / V / start-column DMA (per wave)
     constexpr int N_KV_DMA = NGRP / NW + NVG / NW + 1;
@@ -463,9 +463,7 @@ void attn_fwd_kernel(FwdParams p)
     const int kbase_even = krowbase + 32 * (ksw >> 1);
     const int kbase_odd = krowbase - 32 * (ksw >> 1);
     // V^T operand of 16-key step c: row qi (+ 32 per d-block), chunk 2 c + hh
-    int voff[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) voff[c] = qi * 128 + 16 * ((2 * c + hh) ^ vt_swz(qi));
+    // (offsets in phase_pv)
 
     // ---- relative bias.  Element (jj, e) of half s of a tile's S^T
     // accumulator is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance
@@ -481,7 +479,12 @@ void attn_fwd_kernel(FwdParams p)
     // offset register as an unsigned value, so every register offset handed to
     // it is the exact offset of an entry (never a base to be completed by the
     // constant operand), and offsets before the block wrap out of range.
-    const unsigned prow_off = ((unsigned)i * (unsigned)p.E + (unsigned)(gi - 4 * hh - 30)) * PE;
+    // (derived from the lane id where it is used, not held in registers)
+    auto prow_off_now = [&]() -> unsigned {
+        const unsigned ln = opaque((unsigned)lane);
+        const unsigned ii = (unsigned)i0 + (ln & 31u);
+        return (ii * (unsigned)p.E + ii + (unsigned)p.qoff - 4u * (ln >> 5) - 30u) * PE;
+    };
     constexpr float INV_SCALE = D == 128 ? 11.313708498984761f : 8.0f;   // sqrt(D)
     constexpr int BIAS_DMA = 16;   // code bit: the tile's strip was copied row by row
 
@@ -496,12 +499,10 @@ void attn_fwd_kernel(FwdParams p)
     //    distance in [0, E)) as 4 runs of 4 entries, run jj of lane l at
     //    1024 jj + 16 l; an edge half entry by entry, entry 4 jj + e of lane l
     //    at 256 (4 jj + e) + 4 l, zeroed outside [0, E) on reading.
-    // bf16 profiles: entries are gathered into the registers bias_reg[s]
-    // instead (bf16 tiles are edge halves, loaded entry by entry).
+    // bf16 profiles: every non-empty half is loaded entry by entry as an
+    // edge half; a 2-byte DMA lands zero-extended in the lane's dword, i.e.
+    // as the upper half of the fp32 value.
     char* bstrip = smem + B_OFF + wave * BSTRIP;
-    const int brow = lane >> 4;   // row of the lane within a row-copy instruction (+ 4 u)
-    const unsigned bdma_lane = (unsigned)brow * (unsigned)(p.E + 1) * 4u;
-    f32x16 bias_reg[2];           // bf16 profiles only
 
     // loads of a fast half: vo = exact offset of its lowest distance (run jj = 3)
     auto fetch_fast_half = [&](unsigned vo, int s) {
@@ -514,7 +515,8 @@ void attn_fwd_kernel(FwdParams p)
     };
     // loads of an edge half (keys js .. js + 31), entry by entry
     auto fetch_edge_half = [&](int js, int s) {
-        const unsigned vo = prow_off - (unsigned)js * PE;
+        const unsigned vo = prow_off_now() - (unsigned)js * PE;
+        lds_char* const bs = opaque_lds((lds_char*)bstrip);   // (recomputed per tile, not held in registers)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
@@ -524,11 +526,11 @@ void attn_fwd_kernel(FwdParams p)
                 // before the block (which would read the whole load as 0)
                 const unsigned off = opaque(vo + (30 - 8 * jj - (e ^ 3)) * PE);
                 if constexpr (PROF_BF16) {
-                    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(prsrc, off, 0, 0);
-                    bias_reg[s][4 * jj + e] = __uint_as_float((unsigned)u);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        prsrc, (lds_void*)(bs + 4096 * s + 256 * (4 * jj + e)), 2, off, 0, 0, 0);
                 } else {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        prsrc, (lds_void*)(bstrip + 4096 * s + 256 * (4 * jj + e)), 4, off, 0, 0, 0);
+                        prsrc, (lds_void*)(bs + 4096 * s + 256 * (4 * jj + e)), 4, off, 0, 0, 0);
                 }
             }
         }
@@ -538,30 +540,36 @@ void attn_fwd_kernel(FwdParams p)
     auto load_bias = [&](const TileDesc& d) -> int {
         if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE | (BIAS_NONE << 2);
         const int j0n = d.kt * BN;
-        const int c0 = bias_class(qlo, qhi, j0n, p.E);
-        const int c1 = bias_class(qlo, qhi, j0n + 32, p.E);
+        int c0 = bias_class(qlo, qhi, j0n, p.E);
+        int c1 = bias_class(qlo, qhi, j0n + 32, p.E);
         if constexpr (PROF_BF16) {
-            if (c0 != BIAS_NONE) fetch_edge_half(j0n, 0);
-            if (c1 != BIAS_NONE) fetch_edge_half(j0n + 32, 1);
-            return c0 | (c1 << 2);
-        } else {
+            if (c0 == BIAS_FAST) c0 = BIAS_EDGE;
+            if (c1 == BIAS_FAST) c1 = BIAS_EDGE;
+        }
+        {
             if (c0 == BIAS_NONE && c1 == BIAS_NONE) return 0;
             __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // earlier reads of the strip are done
-            if (c0 == BIAS_FAST && c1 == BIAS_FAST) {
+            if (!PROF_BF16 && c0 == BIAS_FAST && c1 == BIAS_FAST) {
                 // row i0 + r, distance qlo + r - j0n - 63 + 4 c': the strip of row r
                 const unsigned tile_off = (unsigned)((i0 * p.E + qlo - j0n - 63) * 4);
+                // chunk (lane % 16) ^ (r % 16) of row r = 4 u + brow: (r % 16) = 4 (u % 4) | brow
+                const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
+                const unsigned bl = (ln >> 4) * (unsigned)(p.E + 1) * 4u;
+                const unsigned rstep = opaque_s((unsigned)(p.E + 1) * 16u);   // bytes between rows 4 apart, + 16
+                const unsigned xb = 16u * ((ln & 15u) ^ (ln >> 4));
+                lds_char* const bs = opaque_lds((lds_char*)bstrip);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int r = 4 * u + brow;
-                    const unsigned voff = opaque(tile_off + (unsigned)(4 * u) * (unsigned)(p.E + 1) * 4u +
-                                                 bdma_lane + 16u * (unsigned)((lane & 15) ^ (r & 15)));
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bstrip + 1024 * u), 16, voff, 0,
+                    const unsigned voff = opaque(tile_off + (unsigned)u * rstep + bl +
+                                                 (xb ^ (64u * (unsigned)(u & 3))));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 1024 * u), 16, voff, 0,
                                                              0, 0);
                 }
                 return c0 | (c1 << 2) | BIAS_DMA;
             }
-            const unsigned vo0 = opaque(prow_off + (3 - j0n) * PE);
-            const unsigned vo1 = opaque(prow_off + (3 - j0n - 32) * PE);
+            const unsigned po = prow_off_now();
+            const unsigned vo0 = opaque(po + (3 - j0n) * PE);
+            const unsigned vo1 = opaque(po + (3 - j0n - 32) * PE);
             if (c0 == BIAS_FAST) fetch_fast_half(vo0, 0);
             else if (c0 != BIAS_NONE) fetch_edge_half(j0n, 0);
             if (c1 == BIAS_FAST) fetch_fast_half(vo1, 1);
@@ -577,63 +585,57 @@ void attn_fwd_kernel(FwdParams p)
     };
     // a + the entry (jj, e) of the half starting at key js times sqrt(D), or a
     // outside [0, E).
-    auto add_edge = [&](int js, int jj, int e, float raw, float a) -> float {
-        const unsigned r = (unsigned)(gi - js - 8 * jj - 4 * hh - (e ^ 3));
+    // (rb = gi - 4 hh - js, opaque: the distances are recomputed per tile
+    // rather than held in registers)
+    auto add_edge = [&](unsigned rb, int jj, int e, float raw, float a) -> float {
+        const unsigned r = rb - (unsigned)(8 * jj + (e ^ 3));
         return __builtin_fmaf(r < (unsigned)p.E ? raw : 0.0f, INV_SCALE, a);
     };
     // Adds tile j0t's bias (code as load_bias returned it) to the accumulators.
     // Its loads were issued before this wave's DMA of the next K / V tile,
     // which may stay outstanding (N_KV_DMA instructions).
     auto bias_add_tile = [&](int code, int j0t, f32x16* a) {
-        if constexpr (PROF_BF16) {
+        if ((code & 15) == 0) return;
+        wait_vm_keep(N_KV_DMA);
+        if (!PROF_BF16 && (code & BIAS_DMA)) {
+            // chunk k = 15 - 8 s - 2 jj - hh (distances R - 32 s - 8 jj - 4 hh - 3 ..) of
+            // row qi sits at chunk slot k ^ (qi % 16) = (15 ^ hh ^ (qi % 16)) ^ (8 s + 2 jj)
+            const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
+            const unsigned rb = (ln & 31u) * 256u + 16u * (15u ^ (ln >> 5) ^ (ln & 15u));
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                if (((code >> (2 * s2)) & 3) == BIAS_NONE) continue;
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x4 w = *(const f32x4*)(bstrip + (rb ^ (unsigned)(16 * (8 * s2 + 2 * jj))));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+                }
+            return;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int c = (code >> (2 * s2)) & 3;
+            if (!PROF_BF16 && c == BIAS_FAST) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const f32x4 w = *(const f32x4*)(bstrip + 4096 * s2 + 1024 * jj + 16 * opaque((unsigned)lane));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+                }
+            } else if (c != BIAS_NONE) {
+                const unsigned rb = opaque((unsigned)(gi - 4 * hh - j0t - 32 * s2));
+                const char* ep = bstrip + 4096 * s2 + 4 * opaque((unsigned)lane);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a[s2][4 * jj + e] = add_edge(
-                            j0t + 32 * s2, jj, e, __uint_as_float(__float_as_uint(bias_reg[s2][4 * jj + e]) << 16),
-                            a[s2][4 * jj + e]);
-            }
-        } else {
-            if ((code & 15) == 0) return;
-            wait_vm_keep(N_KV_DMA);
-            if (code & BIAS_DMA) {
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int k = 15 - 8 * s2 - 2 * jj - hh;   // distances R - 32 s - 8 jj - 4 hh - 3 ..
-                        const f32x4 w = *(const f32x4*)(bstrip + qi * 256 + 16 * (k ^ (qi & 15)));
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned u = *(const unsigned*)(ep + 256 * (4 * jj + e));
+                        // bf16: the entry is the upper half of the fp32 value
+                        const float raw = __uint_as_float(PROF_BF16 ? u << 16 : u);
+                        a[s2][4 * jj + e] = add_edge(rb, jj, e, raw, a[s2][4 * jj + e]);
                     }
-                return;
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int c = (code >> (2 * s2)) & 3;
-                if (c == BIAS_FAST) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const f32x4 w = *(const f32x4*)(bstrip + 4096 * s2 + 1024 * jj + 16 * lane);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
-                    }
-                } else if (c == BIAS_EDGE) {
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            a[s2][4 * jj + e] = add_edge(
-                                j0t + 32 * s2, jj, e,
-                                *(const float*)(bstrip + 4096 * s2 + 256 * (4 * jj + e) + 4 * lane),
-                                a[s2][4 * jj + e]);
-                }
             }
         }
     };
@@ -675,23 +677,44 @@ void attn_fwd_kernel(FwdParams p)
         asm volatile("" ::: "memory");
         const char* kb = smem + K_OFF + kbuf * KBYTES;
         const char* vbp = smem + V_OFF + vprev * VBYTES;
+        // V^T chunk 2 c + hh of row qi sits at slot (2 c + hh) ^ vt_swz(qi) = (hh ^ vt_swz(qi)) ^ 2 c
+        const unsigned ln = opaque((unsigned)lane);   // (derived here, not held in registers)
+        const unsigned vb = (ln & 31u) * 128u + 16u * ((ln >> 5) ^ (unsigned)vt_swz((int)(ln & 31u)));
 
-        // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains
+        // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains.  The
+        // operands of k-step kk + 2 are read from LDS while k-step kk multiplies.
+        auto kread = [&](int kk, int h2) -> bf16x8 {
+            return *(const bf16x8*)(kb + ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk + h2 * KHALF);
+        };
         f32x16 acc[2];
         {
-            const bf16x8 a0 = *(const bf16x8*)(kb + kbase_even);
-            const bf16x8 a1 = *(const bf16x8*)(kb + kbase_even + KHALF);
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[0], f32x16{}, 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[0], f32x16{}, 0, 0, 0);
-        }
+            bf16x8 ka[NKK][2];
+            ka[0][0] = kread(0, 0);
+            ka[0][1] = kread(0, 1);
+            ka[1][0] = kread(1, 0);
+            ka[1][1] = kread(1, 1);
 #pragma unroll
-        for (int kk = 1; kk < NKK; ++kk) {
-            const int ko = ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk;
-            const bf16x8 a0 = *(const bf16x8*)(kb + ko);
-            const bf16x8 a1 = *(const bf16x8*)(kb + ko + KHALF);
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], acc[1], 0, 0, 0);
+            for (int kk = 0; kk < NKK; ++kk) {
+                if (kk + 2 < NKK) {
+                    ka[kk + 2][0] = kread(kk + 2, 0);
+                    ka[kk + 2][1] = kread(kk + 2, 1);
+                }
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][0], qreg[kk], kk ? acc[0] : f32x16{}, 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][1], qreg[kk], kk ? acc[1] : f32x16{}, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads
+#pragma unroll
+            for (int kk = 0; kk + 2 < NKK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);       // MFMA
         }
+        // operands of step 0 of the previous tile's PV product (read while the
+        // chains above finish)
+        f16x8 avn[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vbp + vb + db * 32 * 128);
         // ---- + bias * sqrt(D) (nothing on tiles this wave skips); the bias
         // registers / strip then take the next tile's
         bias_add_tile(bcode, j0, acc);
@@ -717,27 +740,25 @@ void attn_fwd_kernel(FwdParams p)
         }
 
         // ---- step 0 of the previous tile's O^T += V^T P^T, with this tile's
-        // row max (log2 units) on the vector units meanwhile
-        {
-            f16x8 av[NDB];
+        // row max (log2 units) on the vector units meanwhile; the operands of
+        // step 1 are read meanwhile
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) av[db] = *(const f16x8*)(vbp + voff[0] + db * 32 * 128);
+        for (int db = 0; db < NDB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avn[db], pbp[0], oacc[db], 0, 0, 0);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pbp[0], oacc[db], 0, 0, 0);
-        }
+        for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vbp + (vb ^ 32u) + db * 32 * 128);
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             mx = fmaxf(mx, acc[0][t]);
             mx = fmaxf(mx, acc[1][t]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
         mx = half_max(mx * p.c_log2);
         const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
         const float m_new = move ? mx : m;
@@ -780,13 +801,19 @@ void attn_fwd_kernel(FwdParams p)
         for (int c = 1; c < 4; ++c) {
             f16x8 av[NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) av[db] = *(const f16x8*)(vbp + voff[c] + db * 32 * 128);
+            for (int db = 0; db < NDB; ++db) av[db] = avn[db];
+            // the operands of step c + 1 are read while step c multiplies
+            if (c < 3) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    avn[db] = *(const f16x8*)(vbp + (vb ^ (32u * (c + 1))) + db * 32 * 128);
+            }
             if (c == 1) make_p(0);
             make_p(c);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pbp[c], oacc[db], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
+            if (c < 3) __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -814,12 +841,14 @@ void attn_fwd_kernel(FwdParams p)
     // ---- the last tile's O^T += V^T P^T
     {
         const char* vbp = smem + V_OFF + vprev * VBYTES;
+        const unsigned ln = opaque((unsigned)lane);
+        const unsigned vb = (ln & 31u) * 128u + 16u * ((ln >> 5) ^ (unsigned)vt_swz((int)(ln & 31u)));
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    *(const f16x8*)(vbp + voff[c] + db * 32 * 128), pbp[c], oacc[db], 0, 0, 0);
+                    *(const f16x8*)(vbp + (vb ^ (32u * c)) + db * 32 * 128), pbp[c], oacc[db], 0, 0, 0);
     }
 
     // ---- epilogue
