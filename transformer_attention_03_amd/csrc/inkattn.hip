@@ -53,6 +53,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "common.h"
 #include "inkattn.h"
@@ -654,17 +655,21 @@ void attn_fwd_kernel(FwdParams p)
         f32x4* z = (f32x4*)(smem + V_OFF + 2 * VBYTES);
         for (int t = tid; t < VBYTES / 16; t += 64 * NW) z[t] = f32x4{};
     }
-    if (cur.kt <= kt_hi) {
-        issue_tile(cur, 0, 0);
-        bcode = load_bias(cur);
-    }
+    // Tiles before kt_split carry no bias for any wave of the workgroup (every
+    // distance of the workgroup's first query column to the tile's last key is
+    // at least E); they run a loop body without the bias code.
+    const int qlo_wg = p.qoff + qb_first * BM;
+    const int kt_split = p.E <= 0 ? INT_MAX : (qlo_wg - p.E - (BN - 1) >= 0 ? (qlo_wg - p.E - (BN - 1)) / BN + 1 : 0);
+    if (cur.kt <= kt_hi) issue_tile(cur, 0, 0);
     wait_all_and_barrier();
     int kbuf = 0, vbuf = 0, vprev = 2;
     f16x8 pbp[4];   // P^T of the previous tile (zero when this wave did not compute it)
 #pragma unroll
     for (int c = 0; c < 4; ++c) pbp[c] = f16x8{};
     constexpr int KHALF = (32 / L::RPI) * L::KGP;   // +32 keys in the K buffer
-    while (cur.kt <= kt_hi) {
+    // One tile of the pipeline; WB: with the bias code.
+    auto step = [&](auto with_bias) {
+        constexpr bool WB = decltype(with_bias)::value;
         const TileDesc nxt = next_live();
         const int j0 = cur.kt * BN;
         const int vnext = vbuf == 2 ? 0 : vbuf + 1;
@@ -717,10 +722,13 @@ void attn_fwd_kernel(FwdParams p)
         for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vbp + vb + db * 32 * 128);
         // ---- + bias * sqrt(D) (nothing on tiles this wave skips); the bias
         // registers / strip then take the next tile's
-        bias_add_tile(bcode, j0, acc);
-        asm volatile("" ::: "memory");
-        const int ncode = load_bias(nxt);   // bias code of the next tile
-        asm volatile("" ::: "memory");
+        int ncode = 0;   // bias code of the next tile
+        if constexpr (WB) {
+            bias_add_tile(bcode, j0, acc);
+            asm volatile("" ::: "memory");
+            ncode = load_bias(nxt);
+            asm volatile("" ::: "memory");
+        }
 
         // ---- mask (every key of a tile this wave skips is masked: no allowed
         // pair).  Element (jj, e) of half s is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3).
@@ -831,13 +839,17 @@ void attn_fwd_kernel(FwdParams p)
 
         // this wave's part of the next tile's DMA has landed (the bias loads
         // issued after it may still be in flight); then every wave's has
-        wait_dma_and_barrier(bias_loads(ncode));
+        wait_dma_and_barrier(WB ? bias_loads(ncode) : 0);
         bcode = ncode;
         kbuf ^= 1;
         vprev = vbuf;
         vbuf = vnext;
         cur = nxt;
-    }
+        };
+    while (cur.kt <= kt_hi && cur.kt < kt_split) step(std::false_type{});
+    // the first tile that may carry bias: its loads overlap its own QK^T
+    if (cur.kt <= kt_hi) bcode = load_bias(cur);
+    while (cur.kt <= kt_hi) step(std::true_type{});
     // ---- the last tile's O^T += V^T P^T
     {
         const char* vbp = smem + V_OFF + vprev * VBYTES;
