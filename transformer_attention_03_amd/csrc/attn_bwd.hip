@@ -419,7 +419,8 @@ void bwd_dq_kernel(BwdParams p)
     i32x4 sca;
     float breg[32];    // bias of the next tile: index 16 s + 4 jj + e is distance rb + e (below)
     int nbc = BC_NONE; // its class
-    auto stage_load = [&](int kt) {
+    auto stage_load = [&](int kt, auto with_bias) {
+        constexpr bool WB = decltype(with_bias)::value;
         const int j0 = kt * BN;
         const unsigned kb0 = (unsigned)j0 * krow;
 #pragma unroll
@@ -429,6 +430,10 @@ void bwd_dq_kernel(BwdParams p)
             skt[n] = __builtin_amdgcn_raw_buffer_load_b128(kts, 16u * (unsigned)(tid + 64 * NW * n), kt * TBYTES, 0);
         }
         sca = __builtin_amdgcn_raw_buffer_load_b128(kas, 16u * (unsigned)(tid & 15), j0 * 4, 0);
+        if constexpr (!WB) {
+            nbc = BC_NONE;
+            return;
+        }
         nbc = bias_class(j0);
         if (nbc == BC_NONE) return;
         // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3)
@@ -458,7 +463,8 @@ void bwd_dq_kernel(BwdParams p)
             }
     };
     char* const bstrip = smem + B_OFF + wave * (32 * 64 * 4);   // this wave's bias, lane-major
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int buf, auto with_bias) {
+        constexpr bool WB = decltype(with_bias)::value;
         char* st = smem + buf * STAGE;
 #pragma unroll
         for (int n = 0; n < CPT; ++n) {
@@ -472,7 +478,7 @@ void bwd_dq_kernel(BwdParams p)
             *(i32x4*)(st + KT_OFF + d * 128 + 16 * (cc ^ ((d >> 1) & 7))) = skt[n];
         }
         if (tid < BN / 4) *(i32x4*)(st + CA_OFF + 16 * tid) = sca;
-        if (nbc != BC_NONE) {
+        if (WB && nbc != BC_NONE) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
@@ -480,10 +486,20 @@ void bwd_dq_kernel(BwdParams p)
         }
     };
 
+    using F = std::false_type;
+    using T = std::true_type;
+    // Tiles before kt_split carry no bias for any wave of the workgroup (every
+    // distance of its first query column to the tile's last key is at least
+    // E); while the current and the next tile are such, a loop body without
+    // the bias code runs.  The schedule is read one tile ahead for that.
+    const int qlo_wg = p.qoff + qb_first * BM;
+    const int kt_split = p.E <= 0 ? INT_MAX : (qlo_wg - p.E - (BN - 1) >= 0 ? (qlo_wg - p.E - (BN - 1)) / BN + 1 : 0);
     int2 cur = next_entry(sch, kt_hi, classify);
+    int2 nxt = make_int2(-1, 0);
     if (cur.x >= 0) {
-        stage_load(cur.x);
-        stage_store(0);
+        stage_load(cur.x, T{});
+        stage_store(0, T{});
+        nxt = next_entry(sch, kt_hi, classify);
     }
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is outstanding inside it
@@ -492,12 +508,12 @@ void bwd_dq_kernel(BwdParams p)
     int buf = 0;
     const int xw = qb - qb_first;
     const float nlse2 = -lse2;
-    while (cur.x >= 0) {
-        const int2 nxt = next_entry(sch, kt_hi, classify);
-        if (nxt.x >= 0) stage_load(nxt.x);
+    auto step = [&](auto with_bias) {
+        constexpr bool WB = decltype(with_bias)::value;
+        if (nxt.x >= 0) stage_load(nxt.x, with_bias);
         const int j0 = cur.x * BN;
         const int my_cls = (cur.y >> (2 * xw)) & 3;
-        const int bc = bias_class(j0);
+        const int bc = WB ? bias_class(j0) : (int)BC_NONE;
         const char* st = smem + buf * STAGE;
 
         // ---- S^T = K Q^T and dP^T = V dO^T, keys 32 s + ((lane & 31) ^ 3) on M
@@ -589,12 +605,13 @@ void bwd_dq_kernel(BwdParams p)
                     }
                 }
         };
-        using F = std::false_type;
-        using T = std::true_type;
         using NONE = std::integral_constant<int, BC_NONE>;
         using FULL = std::integral_constant<int, BC_FULL>;
         using EDGE = std::integral_constant<int, BC_EDGE>;
-        if (my_cls == TILE_FULL) {
+        if constexpr (!WB) {
+            if (my_cls == TILE_FULL) body(NONE{}, F{});
+            else body(NONE{}, T{});
+        } else if (my_cls == TILE_FULL) {
             if (bc == BC_NONE) body(NONE{}, F{});
             else if (bc == BC_FULL) body(FULL{}, F{});
             else body(EDGE{}, F{});
@@ -615,11 +632,14 @@ void bwd_dq_kernel(BwdParams p)
             }
 
         // (this wave has read its bias strip: it takes the next tile's)
-        if (nxt.x >= 0) stage_store(buf ^ 1);
+        if (nxt.x >= 0) stage_store(buf ^ 1, with_bias);
         __syncthreads();
         buf ^= 1;
         cur = nxt;
-    }
+        nxt = cur.x >= 0 ? next_entry(sch, kt_hi, classify) : make_int2(-1, 0);
+    };
+    while (cur.x >= 0 && cur.x < kt_split && nxt.x < kt_split) step(F{});
+    while (cur.x >= 0) step(T{});
 
     if (!qin) return;
     // ---- dq = scale * dQ^T
