@@ -338,7 +338,6 @@ void bwd_dq_kernel(BwdParams p)
     const float lse2 = rs.x, dlt = rs.y;
     const size_t prow_off = (((size_t)b * p.Hq + h) * p.Sq + (qin ? i : 0)) * (size_t)p.E;
     char* const dprow = (char*)p.dprofiles + prow_off * (PB ? 2 : 4);
-    const char* const prow = (const char*)p.profiles + prow_off * (PB ? 2 : 4);
 
     f32x16 dqacc[NDB];
 #pragma unroll

@@ -66,8 +66,8 @@ constexpr int NWAVES = 8; // waves per attention workgroup (one workgroup per CU
 constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
 // s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
 // vmcnt(0) lgkmcnt(0); lgkmcnt(0) alone
-constexpr int WAIT_VM_LGKM = 0x0070;
-constexpr int WAIT_LGKM = 0xC07F;
+[[maybe_unused]] constexpr int WAIT_VM_LGKM = 0x0070;   // (used by the device pass only)
+[[maybe_unused]] constexpr int WAIT_LGKM = 0xC07F;
 
 
 
