@@ -185,8 +185,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel()}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the forward shards by head group or by query range, which is not built here.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "a multi-GPU forward would shard by head group or by query range, which is not implemented.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
