@@ -789,11 +789,10 @@ void bwd_dkdv_kernel(BwdParams p)
     sch.n = 0;
     sch.i = 0;
 
-    // ---- staging by LDS DMA (buffer_load ... lds) into a ring of three
-    // stages: the stage of iteration t + 2 is requested in iteration t.  Each
-    // wave issues the same number of DMA instructions for every stage (a P
-    // wave asks for its bias from past the buffer when the stage has none),
-    // so one vmcnt value per wave marks the stage it waits for.
+    // ---- staging by LDS DMA (buffer_load ... lds) into a ring of four
+    // stages: the stage of iteration t + 2 is requested in iteration t.  A
+    // wave waits until at most the DMA instructions of the last stage it
+    // requested are outstanding: the stage before has then landed.
     const unsigned qrow = (unsigned)(p.Hq * D * 2);            // bytes between consecutive queries
     const unsigned qnrec = (unsigned)(p.Sq - 1) * qrow + D * 2;
     const long long qbase = (long long)b * p.Sq * p.Hq * D;
@@ -830,9 +829,11 @@ void bwd_dkdv_kernel(BwdParams p)
         if (rmax < 0 || rmin >= p.E) return BC_NONE;
         return (rmin >= 0 && rmax < p.E && x * BM + BM <= p.Sq) ? BC_FULL : BC_EDGE;
     };
-    // DMA instructions of one stage for this wave (the same for every stage)
-    const int n_dma = (has_rows ? 2 : 0) + (wave < 2 ? 1 : 0) + (role == 0 ? NBI : 0);
-    auto issue = [&](int x, int h, int buf) {
+    // Issues this wave's DMA of one stage; returns the number of DMA
+    // instructions (a P wave fetches no bias runs for a block without bias:
+    // its strip is not read then).
+    auto issue = [&](int x, int h, int buf) -> int {
+        int n = 0;
         char* st = smem + buf * STAGE;
         const int i0 = x * BM;
         if (has_rows) {
@@ -841,6 +842,7 @@ void bwd_dkdv_kernel(BwdParams p)
             const unsigned vo = qv + (unsigned)i0 * qrow;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * wave), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * wave), 16, vo, 0, 0, 0);
+            n += 2;
         }
         if (wave < 2) {
             // row statistics (wave 0) or query descriptors (wave 1): one dword
@@ -850,24 +852,23 @@ void bwd_dkdv_kernel(BwdParams p)
                      : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
             const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + (wave ? QI_OFF : RS_OFF)), 4, vo, 0, 0, 0);
+            n += 1;
         }
-        if (role == 0) {
+        if (role == 0 && bias_class(x) != BC_NONE) {
             // row i0 + m, run start qoff + i0 + m - jw - 31: entry offset
             // (i0 + m) E + qoff + i0 + m - jw - 31 = m (E + 1) + i0 (E + 1) + qoff - jw - 31
             const __amdgpu_buffer_rsrc_t prs =
                 uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
-            const bool nobias = bias_class(x) == BC_NONE;
-            const unsigned base =
-                nobias ? 0xFFFFF000u
-                       : ((unsigned)i0 * (unsigned)(p.E + 1) + (unsigned)(p.qoff - jw - 31)) * (unsigned)ES;
-            const unsigned step = nobias ? 0u : 1u;
+            const unsigned base = ((unsigned)i0 * (unsigned)(p.E + 1) + (unsigned)(p.qoff - jw - 31)) * (unsigned)ES;
             char* bs = st + BS_OFF + kg * BSW;
 #pragma unroll
             for (int k = 0; k < NBI; ++k) {
-                const unsigned vo = opaque(base + bvo[k] * step);
+                const unsigned vo = opaque(base + bvo[k]);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 1024 * k), 16, vo, 0, 0, 0);
             }
+            n += NBI;
         }
+        return n;
     };
     // Transposing reads (ds_read_b64_tr_b16) of the row tiles give the A
     // operands of dV^T = dO^T P and dK^T = Q^T dS: for query step c and
@@ -920,10 +921,11 @@ void bwd_dkdv_kernel(BwdParams p)
     prv.x = -1;
     prv.code = 0;
     prv.hs = 0;
+    int n_flight = 0;   // DMA instructions of the last stage requested
     if (cur.x >= 0) {
         issue(cur.x, g * p.G + cur.hs, 0);
-        const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads: keeps the count)
-        issue(d.x, g * p.G + d.hs, 1);
+        const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads)
+        n_flight = issue(d.x, g * p.G + d.hs, 1);
     }
     int buf = 0, par = 0;
     while (cur.x >= 0 || prv.x >= 0) {
@@ -932,7 +934,7 @@ void bwd_dkdv_kernel(BwdParams p)
         // flight); after the barrier every wave's has, every wave is done with
         // the buffer the next request overwrites and with the exchange slot
         // the P waves write now
-        switch (n_dma) {   // s_waitcnt vmcnt(n_dma) lgkmcnt(0) (operand must be a constant)
+        switch (n_flight) {   // s_waitcnt vmcnt(n_flight) lgkmcnt(0) (operand must be a constant)
 #if defined(__HIP_DEVICE_COMPILE__)
         case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
         case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
@@ -946,8 +948,8 @@ void bwd_dkdv_kernel(BwdParams p)
         }
         asm volatile("s_barrier" ::: "memory");
         {
-            const It d = n2.x >= 0 ? n2 : (cur.x >= 0 ? cur : prv);   // (a copy nothing reads: keeps the count)
-            issue(d.x, g * p.G + d.hs, (buf + 2) & 3);                // stage t + 2
+            const It d = n2.x >= 0 ? n2 : (cur.x >= 0 ? cur : prv);   // (a copy nothing reads)
+            n_flight = issue(d.x, g * p.G + d.hs, (buf + 2) & 3);     // stage t + 2
         }
         asm volatile("" ::: "memory");
         // the P wave's work is (block, head) t; the dS wave's is t - 1
