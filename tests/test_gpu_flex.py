@@ -114,6 +114,23 @@ def test_flex_count_probe(name):
         assert np.array_equal(got[:, h, :], cnt), f"{name}: head {h} counts differ"
 
 
+def test_flex_launcher_equals_the_call():
+    """flex_forward_launcher (the bench's timed path) gives flex_attn_fwd's bits, launch after launch."""
+    x = SMALL["block_causal_G4"]()
+    announce("flex launcher on block_causal_G4, twice")
+    ref_out, ref_lse = run_flex(x)
+    launch, out, lse = binding.flex_forward_launcher(
+        x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), _to(x["sink_weights"]), _to(x["tokens"]), x["eos_id"],
+        x["fixed_block_size"], x["sliding_window"], x["scale"])
+    for _ in range(2):
+        out.zero_()
+        lse.fill_(float("nan"))
+        launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy(), ref_out)
+        assert np.array_equal(lse.cpu().numpy(), ref_lse)
+
+
 def test_flex_rejects_host_tensors():
     x = SMALL["causal_G4_D128"]()
     with pytest.raises(ValueError):

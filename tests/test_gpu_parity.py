@@ -70,6 +70,28 @@ def test_determinism_bitwise():
         assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
 
 
+def test_marshal_once_launchers_equal_the_calls():
+    """planned_forward_launchers (the bench's timed path) gives attn_fwd's bits, launch after launch."""
+    x = SMALL["packed_G2_D128"]()
+    d = to_device(x)
+    announce("marshal-once launchers: plan / stage_values / attention on packed_G2_D128, twice")
+    ref_out, ref_lse = run_hip(x, d=d)
+    ws = torch.empty(binding.attn_fwd_workspace_size(*d["q"].shape[:2], d["k"].shape[1], d["k"].shape[2],
+                                                     d["q"].shape[3]), dtype=torch.uint8, device="cuda")
+    plan, stage_values, attention, out, lse = binding.planned_forward_launchers(
+        d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"], d["key_valid"], d["positions"],
+        d["key_positions"], window=x.get("window"), workspace=ws)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        plan()
+        stage_values()
+        attention()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().double().numpy(), ref_out)
+        assert np.array_equal(lse.cpu().double().numpy(), ref_lse)
+
+
 def test_count_probe_small():
     """Mask inside the hot path: lse = ln(n_allowed) exactly decodes the oracle's counts."""
     for name in ("packed_window", "tailpad_G4_D128", "window_G4_D64"):

@@ -272,6 +272,37 @@ def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=N
     return out, lse
 
 
+def planned_forward_launchers(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
+                              key_positions=None, window=None, query_offset: int = 0, out=None, lse=None,
+                              workspace=None, stream=None):
+    """Marshals the arguments of the three steps of one forward once and returns
+    ``(plan, stage_values, attention, out, lse)``: zero-argument callables that
+    launch ``attn_plan``, ``attn_stage_values`` and ``attn_fwd_planned`` with
+    them, on ``stream``.  For loops that launch the same forward many times
+    (timing): each launch is then one C call.  The tensors must stay alive and
+    unchanged in shape while the callables are used.
+    """
+    args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
+                                        key_positions, window, query_offset, out, lse, workspace, stream)
+    (qp, kp, vp, pp, pdt, sp, vlp, kvp, posp, kposp, win, qoff, B, Sq, Sk, Hq, Hkv, D, E, op, lp, wsp, wsn,
+     st) = args
+    lib = load()
+    plan_args = (vlp, kvp, posp, kposp, qoff, B, Sq, Sk, wsp, wsn, st)
+    stage_args = (vp, vlp, kvp, qoff, B, Sq, Sk, Hkv, D, wsp, wsn, st)
+
+    def plan():
+        _check(lib.attn_plan(*plan_args), "attn_plan")
+
+    def stage_values():
+        _check(lib.attn_stage_values(*stage_args), "attn_stage_values")
+
+    def attention():
+        _check(lib.attn_fwd_planned(*args), "attn_fwd_planned")
+
+    plan.keep = stage_values.keep = attention.keep = keep   # the marshalled tensors live as long as these
+    return plan, stage_values, attention, out, lse
+
+
 def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_offset: int = 0,
               Sk: Optional[int] = None, workspace: Optional[torch.Tensor] = None, Hkv: int = 0, D: int = 0,
               stream=None) -> torch.Tensor:
@@ -412,6 +443,32 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ``eos_id``); ``fixed_block_size`` None/<=0: none; ``sliding_window`` <= 0: none;
     ``scale`` applies only without sink weights (None: head_dim^-0.5).
     """
+    args, out, lse, keep = _marshal_flex(q, k, v, sink_weights, tokens, eos_id, fixed_block_size, sliding_window,
+                                         scale, out, lse, workspace, stream)
+    _check(load().flex_attn_fwd(*args), "flex_attn_fwd")
+    del keep
+    return out, lse
+
+
+def flex_forward_launcher(q, k, v, sink_weights=None, tokens=None, eos_id: int = 0, fixed_block_size=None,
+                          sliding_window: int = 0, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Marshals the arguments of :func:`flex_attn_fwd` once and returns
+    ``(launch, out, lse)``: ``launch()`` calls the C entry point with them, on
+    ``stream`` (for loops that launch the same call many times).  The tensors
+    must stay alive and unchanged in shape while ``launch`` is used."""
+    args, out, lse, keep = _marshal_flex(q, k, v, sink_weights, tokens, eos_id, fixed_block_size, sliding_window,
+                                         scale, out, lse, workspace, stream)
+    lib = load()
+
+    def launch():
+        _check(lib.flex_attn_fwd(*args), "flex_attn_fwd")
+
+    launch.keep = keep
+    return launch, out, lse
+
+
+def _marshal_flex(q, k, v, sink_weights, tokens, eos_id, fixed_block_size, sliding_window, scale, out, lse,
+                  workspace, stream):
     dev = q.device
     q = _dev(q, "q", (torch.bfloat16,), None)
     k = _dev(k, "k", (torch.bfloat16,), dev)
@@ -433,10 +490,10 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(flex_attn_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
                                 device=dev)
-    rc = load().flex_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sink_weights), _ptr(tokens), int(eos_id),
-                              int(fixed_block_size or 0), int(sliding_window or 0),
-                              float(scale) if scale is not None else 0.0, B, Sq, Sk, Hq, Hkv, D,
-                              _ptr(out), _ptr(lse), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream, dev))
-    _check(rc, "flex_attn_fwd")
-    return out, lse
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(sink_weights), _ptr(tokens), int(eos_id),
+            int(fixed_block_size or 0), int(sliding_window or 0),
+            float(scale) if scale is not None else 0.0, B, Sq, Sk, Hq, Hkv, D,
+            _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    keep = (q, k, v, sink_weights, tokens, workspace)
+    return args, out, lse, keep
