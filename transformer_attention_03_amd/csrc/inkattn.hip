@@ -23,15 +23,18 @@
 //      32-token block).  Each 64-key K / V^T tile is staged once in LDS by DMA
 //      (buffer_load ... lds, XOR-swizzled rows) and serves every wave of the
 //      workgroup, i.e. every query head of the chunk (GQA).  The next live
-//      tile's DMA and this wave's bias for it are issued at the start of the
-//      current tile (one barrier per tile).  Per wave and tile:
+//      tile's DMA is issued at the start of the current tile, this wave's
+//      bias for it after the current tile's S^T (one barrier per tile).
+//      Tiles on which no wave of the workgroup can take bias run a loop body
+//      without the bias code.  Per wave and tile:
 //        S^T = K Q^T      bf16 MFMA 32x32x16 as two interleaved chains (one per
 //                         32-key half), keys on M and queries on N, so each
 //                         lane owns one query column: row reductions are
 //                         in-lane plus one exchange between the wave halves;
-//                         each chain starts from the relative bias (scaled by
-//                         sqrt(D)), gathered from the query's own profile row
-//                         as contiguous 4-entry runs one tile ahead, or from 0;
+//        + bias           the relative bias times sqrt(D), from the query's
+//                         own profile row, staged one tile ahead in a per-wave
+//                         LDS strip by DMA (whole row strips, 4-entry runs or
+//                         single entries, by how the tile meets [0, E));
 //        mask             only on tiles classed as masked;
 //        online softmax   running max / denominator per lane over the 64 keys,
 //                         started from the sink logit (the sink's weight
