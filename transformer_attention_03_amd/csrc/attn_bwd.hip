@@ -51,7 +51,8 @@ namespace {
 
 using namespace inkattn;
 
-constexpr int BW_WAVES = 4;          // waves per workgroup of both gradient kernels
+constexpr int BW_WAVES = 4;          // (query head, 32-query block) units per dQ workgroup
+constexpr int DQ_WAVES = 2 * BW_WAVES; // dQ waves: one per unit and 32-key half of each tile
 // bias class of a tile for one wave: no distance inside [0, E), all inside, mixed
 enum : int { BC_NONE = 0, BC_FULL = 1, BC_EDGE = 2 };
 constexpr int KV_WAVES = 8;          // waves per dK / dV workgroup (two per 32-key group)
@@ -270,15 +271,18 @@ __device__ __forceinline__ void store_grad(void* prow, int r, float x)
 }
 
 // ---------------------------------------------------------------------------
-// dQ and the profile gradients.  One workgroup of 4 waves per (batch row, K/V
-// head, head chunk, group of 32-query blocks), the forward's decomposition;
-// wave = (query head, 32-query block), lane = (query qi, wave half hh).
+// dQ and the profile gradients.  One workgroup of 8 waves per (batch row, K/V
+// head, head chunk, group of 32-query blocks), the forward's decomposition
+// into 4 units (query head, 32-query block).  Wave w takes unit w % 4 and the
+// 32-key half w / 4 of every key tile (two waves per SIMD); the two halves'
+// dQ partials are summed at the end.  Lane = (query qi, wave half hh).
 // ---------------------------------------------------------------------------
 template <int D, bool PB>
-__global__ __launch_bounds__(64 * BW_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * DQ_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p)
 {
-    constexpr int NW = BW_WAVES;
+    constexpr int NW = DQ_WAVES;
+    constexpr int NU = BW_WAVES;
     constexpr int NKK = D / 16;              // k-steps over D
     constexpr int NDB = D / 32;              // 32-row blocks of dQ^T
     constexpr int CH = D / 8;                // 16-byte chunks per row
@@ -286,17 +290,21 @@ void bwd_dq_kernel(BwdParams p)
     constexpr int K_OFF = 0, V_OFF = TBYTES, KT_OFF = 2 * TBYTES, CA_OFF = 3 * TBYTES;
     constexpr int STAGE = 3 * TBYTES + BN * 4;
     constexpr int NSCHED = 64 * NW;
-    constexpr int B_OFF = 2 * STAGE;         // per-wave bias strips (32 values per lane)
-    constexpr int SCHED_OFF = B_OFF + NW * 32 * 64 * 4;
+    constexpr int B_OFF = 2 * STAGE;         // per-wave bias strips (16 values per lane)
+    constexpr int BSW = 32 * 32 * 4;         // one wave's strip
+    constexpr int SCHED_OFF = B_OFF + NW * BSW;
+    static_assert(NU * (D / 32) * 16 * 64 * 4 <= 2 * STAGE, "the dQ partials fit the staging buffers");
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
-    constexpr int CPT = BN * CH / (64 * NW);  // 16-byte chunks per thread of one K (or V, K^T) tile
-    static_assert(CPT >= 1 && BN * CH % (64 * NW) == 0, "tile chunks must divide among threads");
+    constexpr int GPW = TBYTES / 1024 / NW;  // 1 KB DMA groups per wave of one K, V or K^T tile
+    constexpr int RPG = 1024 / (2 * D);      // K / V rows per DMA group
+    static_assert(GPW >= 1 && TBYTES % (1024 * NW) == 0, "tile DMA groups must divide among the waves");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int unit = wave % NU, kh = wave / NU;   // unit; key half (keys 32 kh .. 32 kh + 31 of a tile)
     const int qi = lane & 31, hh = lane >> 5;
 
     int idx = blockIdx.x;
@@ -305,8 +313,8 @@ void bwd_dq_kernel(BwdParams p)
     const int b = idx % p.B; idx /= p.B;
     const int qg = p.nQG - 1 - idx;
     const int g = hgi / p.nchunk;
-    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + wave % p.hpw;
-    const int qb = qg * p.tpw + wave / p.hpw;
+    const int h = g * p.G + (hgi - g * p.nchunk) * p.hpw + unit % p.hpw;
+    const int qb = qg * p.tpw + unit / p.hpw;
     const int qb_first = qg * p.tpw;
     const int qb_last = min(p.nQB - 1, qb_first + p.tpw - 1);
     const int i0 = qb * BM;
@@ -397,51 +405,59 @@ void bwd_dq_kernel(BwdParams p)
         uniform_rsrc((const char*)p.profiles + ((size_t)b * p.Hq + h) * pblock, pblock);
     const __amdgpu_buffer_rsrc_t drs = uniform_rsrc((char*)p.dprofiles + ((size_t)b * p.Hq + h) * pblock, pblock);
     const unsigned rowe = (unsigned)(qin ? i : 0) * (unsigned)p.E;   // this query's row, in entries
-    // per-thread parts of the K / V row offsets (chunk u = tid + 256 n: row u / CH, chunk u % CH)
-    unsigned kvoff[CPT];
-#pragma unroll
-    for (int n = 0; n < CPT; ++n) {
-        const int u = tid + 64 * NW * n;
-        kvoff[n] = (unsigned)(u / CH) * krow + 16u * (unsigned)(u % CH);
-    }
-    // Bias class of a tile for this wave: no distance of its 32 x 64 pairs in
-    // [0, E) (no bias, no profile gradient), all inside (whole 16-byte runs),
-    // or mixed (entry by entry).  Wave-uniform.
+    // Bias class of a tile for this wave: no distance of its 32 x 32 pairs
+    // (its key half) in [0, E) (no bias, no profile gradient), all inside
+    // (whole 16-byte runs), or mixed (entry by entry).  Wave-uniform.
     const int qlo_w = p.qoff + i0, qhi_w = p.qoff + min(p.Sq, i0 + BM) - 1;
     auto bias_class = [&](int j0t) -> int {
         if (qb >= p.nQB) return BC_NONE;
-        const int rmin = qlo_w - (j0t + BN - 1), rmax = qhi_w - j0t;
+        const int jh = j0t + 32 * kh;
+        const int rmin = qlo_w - (jh + 31), rmax = qhi_w - jh;
         if (rmax < 0 || rmin >= p.E) return BC_NONE;
         return (rmin >= 0 && rmax < p.E) ? BC_FULL : BC_EDGE;
     };
-    i32x4 sk[CPT], sv[CPT], skt[CPT];
-    i32x4 sca;
-    float breg[32];    // bias of the next tile: index 16 s + 4 jj + e is distance rb + e (below)
+    float breg[16];    // bias of the next tile's key half: index 4 jj + e is distance rb + e (below)
     int nbc = BC_NONE; // its class
-    auto stage_load = [&](int kt, auto with_bias) {
+    // K, V, K^T and the key start columns of tile kt go to stage buffer sb by
+    // buffer -> LDS DMA: lane l of 1 KB group a writes bytes 1024 a + 16 l of
+    // the tile and fetches the chunk that belongs there (K / V: row
+    // RPG a + l / CH, slot l % CH, i.e. chunk slot ^ row_swz(row); K^T: row
+    // 8 a + l / 8, slot l % 8, chunk slot ^ ((row / 2) % 8)).  Every wave also
+    // fetches the same 64 start columns, so that each wave's sequence of
+    // memory instructions is the same on every path.  The bias of the wave's
+    // key half goes to registers (stored to the strip at the end of the step).
+    auto stage_load = [&](int kt, int sb, auto with_bias) {
         constexpr bool WB = decltype(with_bias)::value;
         const int j0 = kt * BN;
-        const unsigned kb0 = (unsigned)j0 * krow;
+        char* const st = smem + sb * STAGE;
+        const unsigned ln = opaque((unsigned)lane);   // (offsets formed here, not held in registers)
 #pragma unroll
-        for (int n = 0; n < CPT; ++n) {
-            sk[n] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff[n] + kb0, 0, 0);
-            sv[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, kvoff[n] + kb0, 0, 0);
-            skt[n] = __builtin_amdgcn_raw_buffer_load_b128(kts, 16u * (unsigned)(tid + 64 * NW * n), kt * TBYTES, 0);
+        for (int u = 0; u < GPW; ++u) {
+            const int a = wave + NW * u;
+            const unsigned r = (unsigned)(RPG * a) + ln / CH;
+            // (whole offsets in the register operand: the range check, which
+            // turns rows past Sk into zeros, applies to it)
+            const unsigned kvo = ((unsigned)j0 + r) * krow + 16u * ((ln % CH) ^ (unsigned)row_swz<D>((int)r));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + K_OFF + 1024 * a), 16, kvo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + V_OFF + 1024 * a), 16, kvo, 0, 0, 0);
+            const unsigned d = (unsigned)(8 * a) + ln / 8;
+            const unsigned kto = (unsigned)(kt * TBYTES) + d * 128u + 16u * ((ln % 8) ^ ((d >> 1) & 7u));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kts, (lds_void*)(st + KT_OFF + 1024 * a), 16, kto, 0, 0, 0);
         }
-        sca = __builtin_amdgcn_raw_buffer_load_b128(kas, 16u * (unsigned)(tid & 15), j0 * 4, 0);
+        const unsigned cao = (unsigned)j0 * 4u + 4u * ln;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kas, (lds_void*)(st + CA_OFF), 4, cao, 0, 0, 0);
         if constexpr (!WB) {
             nbc = BC_NONE;
             return;
         }
         nbc = bias_class(j0);
         if (nbc == BC_NONE) return;
-        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3)
+        {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const int rb = gi - (j0 + 32 * s2 + 8 * jj + 4 * hh + 3);
-                float* w = breg + 16 * s2 + 4 * jj;
+                const int rb = gi - (j0 + 32 * kh + 8 * jj + 4 * hh + 3);
+                float* w = breg + 4 * jj;
                 const unsigned off = (rowe + (unsigned)rb) * (unsigned)ES;
                 if constexpr (PB) {
                     // (entry offsets kept opaque: they may wrap modulo 2^32 like
@@ -460,26 +476,15 @@ void bwd_dq_kernel(BwdParams p)
                     for (int e = 0; e < 4; ++e) w[e] = __int_as_float(x[e]);
                 }
             }
+        }
     };
-    char* const bstrip = smem + B_OFF + wave * (32 * 64 * 4);   // this wave's bias, lane-major
+    char* const bstrip = smem + B_OFF + wave * BSW;   // this wave's bias, lane-major
     auto stage_store = [&](int buf, auto with_bias) {
         constexpr bool WB = decltype(with_bias)::value;
-        char* st = smem + buf * STAGE;
-#pragma unroll
-        for (int n = 0; n < CPT; ++n) {
-            const int u = tid + 64 * NW * n;
-            const int r = u / CH, c = u % CH;
-            const int pr = r * (2 * D) + 16 * (c ^ row_swz<D>(r));
-            *(i32x4*)(st + K_OFF + pr) = sk[n];
-            *(i32x4*)(st + V_OFF + pr) = sv[n];
-            // K^T: row d = u / 8 of 64 bf16 (128 B), chunk u % 8
-            const int d = u >> 3, cc = u & 7;
-            *(i32x4*)(st + KT_OFF + d * 128 + 16 * (cc ^ ((d >> 1) & 7))) = skt[n];
-        }
-        if (tid < BN / 4) *(i32x4*)(st + CA_OFF + 16 * tid) = sca;
+        (void)buf;
         if (WB && nbc != BC_NONE) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int t = 0; t < 4; ++t)
                 *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
                     f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
         }
@@ -496,7 +501,7 @@ void bwd_dq_kernel(BwdParams p)
     int2 cur = next_entry(sch, kt_hi, classify);
     int2 nxt = make_int2(-1, 0);
     if (cur.x >= 0) {
-        stage_load(cur.x, T{});
+        stage_load(cur.x, 0, T{});
         stage_store(0, T{});
         nxt = next_entry(sch, kt_hi, classify);
     }
@@ -509,51 +514,45 @@ void bwd_dq_kernel(BwdParams p)
     const float nlse2 = -lse2;
     auto step = [&](auto with_bias) {
         constexpr bool WB = decltype(with_bias)::value;
-        if (nxt.x >= 0) stage_load(nxt.x, with_bias);
+        // (buffer buf ^ 1 was last read before the barrier that ended the
+        // previous iteration)
+        if (nxt.x >= 0) stage_load(nxt.x, buf ^ 1, with_bias);
         const int j0 = cur.x * BN;
         const int my_cls = (cur.y >> (2 * xw)) & 3;
         const int bc = WB ? bias_class(j0) : (int)BC_NONE;
         const char* st = smem + buf * STAGE;
 
-        // ---- S^T = K Q^T and dP^T = V dO^T, keys 32 s + ((lane & 31) ^ 3) on M
-        f32x16 acc[2], dacc[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            acc[s2] = f32x16{};
-            dacc[s2] = f32x16{};
-        }
+        // ---- S^T = K Q^T and dP^T = V dO^T for this wave's key half, keys
+        // 32 kh + ((lane & 31) ^ 3) on M
+        f32x16 acc = f32x16{}, dacc = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int r = 32 * s2 + (qi ^ 3);
-                const int pr = r * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(r));
-                const bf16x8 ak = *(const bf16x8*)(st + K_OFF + pr);
-                const bf16x8 av = *(const bf16x8*)(st + V_OFF + pr);
-                acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], acc[s2], 0, 0, 0);
-                dacc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[kk], dacc[s2], 0, 0, 0);
-            }
+            const int r = 32 * kh + (qi ^ 3);
+            const int pr = r * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(r));
+            const bf16x8 ak = *(const bf16x8*)(st + K_OFF + pr);
+            const bf16x8 av = *(const bf16x8*)(st + V_OFF + pr);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], acc, 0, 0, 0);
+            dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[kk], dacc, 0, 0, 0);
         }
 
-        // ---- P, dS, profile gradients.  Element (s, jj, e) is key
-        // j0 + 32 s + 8 jj + 4 hh + (e ^ 3), distance rb + e with
-        // rb = gi - (j0 + 32 s + 8 jj + 4 hh + 3).
+        // ---- P, dS, profile gradients.  Element (jj, e) is key
+        // j0 + 32 kh + 8 jj + 4 hh + (e ^ 3), distance rb + e with
+        // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).
         const int* ca = (const int*)(st + CA_OFF);
-        bf16x8 pd[4];
+        bf16x8 pd[2];
         auto body = [&](auto bct, auto mt) {
             constexpr int BCT = decltype(bct)::value;
             constexpr bool MASKED = decltype(mt)::value;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+            {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int kl = 32 * s2 + 8 * jj + 4 * hh;
+                    const int kl = 32 * kh + 8 * jj + 4 * hh;
                     const int rb = gi - (j0 + kl + 3);
                     f32x4 pre;   // bias * log2(e) - lse2 per entry
                     if constexpr (BCT == BC_NONE) {
                         pre = f32x4{nlse2, nlse2, nlse2, nlse2};
                     } else {
-                        const f32x4 bias = *(const f32x4*)(bstrip + (4 * s2 + jj) * 1024 + 16 * lane);
+                        const f32x4 bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             pre[e] = __builtin_fmaf(bias[e], LOG2E, nlse2);
@@ -566,13 +565,13 @@ void bwd_dq_kernel(BwdParams p)
                     f32x4 dz;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[s2][4 * jj + e], p.c_log2, pre[e]));
-                        const float x = pr * (dacc[s2][4 * jj + e] - dlt);
+                        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[4 * jj + e], p.c_log2, pre[e]));
+                        const float x = pr * (dacc[4 * jj + e] - dlt);
                         if constexpr (MASKED)   // (keys that are not real may hold any value)
                             dz[e] = key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim) ? x : 0.0f;
                         else
                             dz[e] = x;
-                        pd[2 * s2 + (jj >> 1)][4 * (jj & 1) + e] = (__bf16)dz[e];
+                        pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)dz[e];
                     }
                     // profile gradients: stores outside this query's row [0, E)
                     // get an offset past the buffer and are dropped
@@ -603,6 +602,7 @@ void bwd_dq_kernel(BwdParams p)
                         }
                     }
                 }
+            }
         };
         using NONE = std::integral_constant<int, BC_NONE>;
         using FULL = std::integral_constant<int, BC_FULL>;
@@ -620,18 +620,23 @@ void bwd_dq_kernel(BwdParams p)
             else body(EDGE{}, T{});
         }
 
-        // ---- dQ^T += K^T dS^T (K^T rows in the staged key order)
+        // ---- dQ^T += K^T dS^T over this wave's key half (16-key steps
+        // 2 kh, 2 kh + 1; K^T rows in the staged key order)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
+                const int c = 2 * kh + c2;
                 const int d = 32 * db + qi;
                 const bf16x8 a = *(const bf16x8*)(st + KT_OFF + d * 128 + 16 * ((2 * c + hh) ^ ((d >> 1) & 7)));
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[c], dqacc[db], 0, 0, 0);
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[c2], dqacc[db], 0, 0, 0);
             }
 
         // (this wave has read its bias strip: it takes the next tile's)
         if (nxt.x >= 0) stage_store(buf ^ 1, with_bias);
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA of the next tile has landed
+#endif
         __syncthreads();
         buf ^= 1;
         cur = nxt;
@@ -640,9 +645,28 @@ void bwd_dq_kernel(BwdParams p)
     while (cur.x >= 0 && cur.x < kt_split && nxt.x < kt_split) step(F{});
     while (cur.x >= 0) step(T{});
 
+    // ---- the two key halves' partials (the staging buffers are free: the
+    // last iteration ended at a barrier): half 1 hands its partial to half 0
+    // through LDS, then writes the profile-gradient zeros while half 0 writes dq
+    {
+        float* red = (float*)smem + (size_t)unit * NDB * 16 * 64 + lane;
+        if (kh == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) red[(db * 16 + t) * 64] = dqacc[db][t];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) dqacc[db][t] += red[(db * 16 + t) * 64];
+        }
+    }
     if (!qin) return;
     // ---- dq = scale * dQ^T
-    {
+    if (kh == 0) {
         float* dqp = p.dq + (((size_t)b * p.Sq + i) * p.Hq + h) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -655,6 +679,7 @@ void bwd_dq_kernel(BwdParams p)
             }
     }
 
+    if (kh == 0) return;
     // ---- zeros at the profile-gradient entries no visited tile wrote: the
     // distance r belongs to key column gi - r, so these are the columns
     // outside [0, Sk) and those in tiles the workgroup did not visit.
@@ -1148,7 +1173,7 @@ int launch_bwd(const BwdParams& p, hipStream_t st)
                            (long long)p.Hkv * D, (long long)D, p.kt);
     if (int rc = check_launch("bwd_stage_kernel")) return rc;
     const size_t ndq = (size_t)p.nQG * p.B * p.Hkv * p.nchunk;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, PB>), dim3((unsigned)ndq), dim3(64 * BW_WAVES), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, PB>), dim3((unsigned)ndq), dim3(64 * DQ_WAVES), 0, st, p);
     if (int rc = check_launch("bwd_dq_kernel")) return rc;
     const size_t nkv = (size_t)p.nKB * p.B * p.Hkv;
     if (nkv == 0) return INKATTN_OK;
