@@ -524,15 +524,32 @@ void bwd_dq_kernel(BwdParams p)
 
         // ---- S^T = K Q^T and dP^T = V dO^T for this wave's key half, keys
         // 32 kh + ((lane & 31) ^ 3) on M
+        // (the operands of k-step kk + 1 are read while k-step kk multiplies)
         f32x16 acc = f32x16{}, dacc = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
+        {
             const int r = 32 * kh + (qi ^ 3);
-            const int pr = r * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(r));
-            const bf16x8 ak = *(const bf16x8*)(st + K_OFF + pr);
-            const bf16x8 av = *(const bf16x8*)(st + V_OFF + pr);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[kk], acc, 0, 0, 0);
-            dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, doreg[kk], dacc, 0, 0, 0);
+            auto opnd = [&](int kk, int off) -> bf16x8 {
+                return *(const bf16x8*)(st + off + r * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(r)));
+            };
+            bf16x8 ak[2], av[2];
+            ak[0] = opnd(0, K_OFF);
+            av[0] = opnd(0, V_OFF);
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                if (kk + 1 < NKK) {
+                    ak[(kk + 1) & 1] = opnd(kk + 1, K_OFF);
+                    av[(kk + 1) & 1] = opnd(kk + 1, V_OFF);
+                }
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk & 1], qreg[kk], acc, 0, 0, 0);
+                dacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1], doreg[kk], dacc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // LDS reads
+#pragma unroll
+            for (int kk = 0; kk + 1 < NKK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // MFMA
         }
 
         // ---- P, dS, profile gradients.  Element (jj, e) is key
