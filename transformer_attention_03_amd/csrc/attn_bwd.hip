@@ -22,18 +22,21 @@
 //      global column (-1 if not real) and document start column.
 //   3. bwd_stage_kernel: K^T per 64-key tile in bf16, the keys in the order of
 //      the dS^T registers the dQ product meets them in.
-//   4. bwd_dq_kernel (query-parallel, one wave per (query head, 32 queries),
-//      keys on MFMA M as in the forward): per 64-key tile S^T = K Q^T and
-//      dP^T = V dO^T, then P and dS from the saved lse, dS written to the
-//      profile gradient row (a contiguous run per query), dQ^T += K^T dS^T.
-//      Every entry of a query's profile-gradient row is written by its wave:
-//      zeros where no tile it visits puts a value.
-//   5. bwd_dkdv_kernel (key-parallel, one wave per 32 keys, queries on MFMA
-//      M): per (32-query block, head of the group) S = Q K^T, dP = dO V^T,
-//      P, dS, then dV^T += dO^T P and dK^T += Q^T dS, the transposed operands
-//      read from the staged rows with transposing LDS reads.  The stages come
-//      by LDS DMA through a ring of three; S / dP of the next block run while
-//      P / dS of this one are computed.
+//   4. bwd_dq_kernel (query-parallel, two waves per (query head, 32
+//      queries), one per 32-key half of each tile, keys on MFMA M as in the
+//      forward): per 64-key tile S^T = K Q^T and dP^T = V dO^T, then P and dS
+//      from the saved lse, dS written to the profile gradient row (a
+//      contiguous run per query), dQ^T += K^T dS^T; the halves' partials are
+//      summed at the end.  Every entry of a query's profile-gradient row is
+//      written by one of its two waves: zeros where no tile they visit puts
+//      a value.
+//   5. bwd_dkdv_kernel (key-parallel, two waves per 32 keys, queries on MFMA
+//      M): per (32-query block, head of the group) the P wave forms S = Q K^T
+//      and P and accumulates dV^T += dO^T P; the dS wave forms dP = dO V^T,
+//      takes P through LDS one block later, forms dS and accumulates
+//      dK^T += Q^T dS.  The transposed operands are read from the staged rows
+//      with transposing LDS reads; the stages come by LDS DMA through a ring
+//      of four, two ahead.
 // Products are bf16 MFMA 32x32x16 with fp32 accumulation; P and dS are
 // rounded to bf16 for the products that consume them.
 #include <hip/hip_runtime.h>
