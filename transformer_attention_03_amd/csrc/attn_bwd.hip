@@ -743,7 +743,7 @@ void bwd_dkdv_kernel(BwdParams p)
     constexpr int NDB = D / 32;
     constexpr int RBYTES = BM * D * 2;       // one 32-row Q / dO tile
     // one stage: Q rows, dO rows, row statistics, query descriptors, and the
-    // P waves' bias strips; three stages in a ring, then the P exchange
+    // P waves' bias strips; four stages in a ring, then the P exchange
     constexpr int Q_OFF = 0, DO_OFF = RBYTES;
     constexpr int RS_OFF = 2 * RBYTES, QI_OFF = RS_OFF + BM * 8;
     constexpr int BS_OFF = QI_OFF + BM * 8;
