@@ -922,17 +922,27 @@ __global__ __launch_bounds__(D) void stage_values_kernel(const __bf16* __restric
     const int g = (t / nKT) % Hkv;
     const int b = t / (nKT * Hkv);
     const int sg = threadIdx.x / CH, dc = threadIdx.x % CH;
-    f16x8 rows[8];
+    // every row and its validity byte are loaded before any is used (one
+    // memory round trip, not one per row)
+    // (keys past Sk load key Sk - 1, branch-free, and are dropped below)
+    bf16x8 xr[8];
+    int ok[8];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
         // slot 8 sg + tt holds key 16 (sg / 2) + 8 (tt / 4) + 4 (sg % 2) + ((tt % 4) ^ 3)
         const int key = 16 * (sg >> 1) + 8 * (tt >> 2) + 4 * (sg & 1) + ((tt & 3) ^ 3);
-        const int j = kt * BN + key;
-        f16x8 y = f16x8{};
-        if (j < Sk && key_valid[(size_t)b * Sk + j]) {
-            const bf16x8 x = *(const bf16x8*)(v + b * v_bs + j * v_ts + g * v_hs + 8 * dc);
+        const int j = min(kt * BN + key, Sk - 1);
+        xr[tt] = *(const bf16x8*)(v + b * v_bs + j * v_ts + g * v_hs + 8 * dc);
+        ok[tt] = key_valid[(size_t)b * Sk + j];
+    }
+    f16x8 rows[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)x[e], -65504.0f), 65504.0f);
+    for (int tt = 0; tt < 8; ++tt) {
+        const int key = 16 * (sg >> 1) + 8 * (tt >> 2) + 4 * (sg & 1) + ((tt & 3) ^ 3);
+        f16x8 y = f16x8{};
+        if (ok[tt] && kt * BN + key < Sk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)xr[tt][e], -65504.0f), 65504.0f);
         }
         rows[tt] = y;
     }
@@ -1163,8 +1173,10 @@ __global__ __launch_bounds__(1024) void flex_positions_kernel(const int32_t* __r
                                                               uint8_t* __restrict__ ones, size_t nones)
 {
     constexpr int PER = 8;                       // tokens per thread and pass
-    __shared__ int scan[1024];
+    constexpr int NWV = 1024 / 64;               // waves
+    __shared__ int wmax[NWV];
     const int b = blockIdx.x, t = threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
     for (size_t u = (size_t)b * 1024 + t; u < nones; u += (size_t)gridDim.x * 1024) ones[u] = 1;
     if (!pos) return;
     const int32_t* tk = tokens ? tokens + (size_t)b * S : nullptr;
@@ -1179,18 +1191,25 @@ __global__ __launch_bounds__(1024) void flex_positions_kernel(const int32_t* __r
 #pragma unroll
         for (int e = 0; e < PER; ++e)
             if (is_eos[e]) last = lo + e + 1;
-        // running max over the threads' segments (Hillis-Steele), exclusive
-        scan[t] = last;
-        __syncthreads();
-        for (int d = 1; d < 1024; d <<= 1) {
-            const int other = t >= d ? scan[t - d] : 0;
-            __syncthreads();
-            scan[t] = max(scan[t], other);
-            __syncthreads();
+        // running max over the threads' segments: inclusive within the wave
+        // by shuffles, then over the waves before through LDS
+        int inc = last;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int other = __shfl_up(inc, d, 64);
+            if (lane >= d) inc = max(inc, other);
         }
-        int start = max(carry, t > 0 ? scan[t - 1] : 0);
-        const int pass_max = scan[1023];
-        __syncthreads();                         // scan[] is rewritten by the next pass
+        if (lane == 63) wmax[wv] = inc;
+        __syncthreads();
+        int before = 0, pass_max = 0;
+        for (int w = 0; w < NWV; ++w) {
+            const int x = wmax[w];
+            if (w < wv) before = max(before, x);
+            pass_max = max(pass_max, x);
+        }
+        const int prev = __shfl_up(inc, 1, 64);   // inclusive value of the lane before
+        int start = max(carry, max(before, lane > 0 ? prev : 0));
+        __syncthreads();                         // wmax[] is rewritten by the next pass
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
             const int u = lo + e;
@@ -1210,6 +1229,7 @@ int launch_stage(const __bf16* v, const uint8_t* key_valid, int B, int Sk, int H
                  long long v_ts, long long v_hs, _Float16* v16, hipStream_t st)
 {
     const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
+    if (tiles == 0) return INKATTN_OK;   // (the kernel reads key Sk - 1: Sk >= 1 from here on)
     if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
     if (D == 128)
         hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(128), 0, st, v, key_valid, Sk, Hkv,
