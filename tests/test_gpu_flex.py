@@ -153,3 +153,24 @@ def test_flex_full_size_sampled_rows():
     got_out = out.transpose(0, 2, 1, 3).reshape(w.B * w.S, w.Hq, w.D)[r]
     got_lse = lse.transpose(0, 2, 1).reshape(w.B * w.S, w.Hq)[r]
     assert_flex_close(got_out, got_lse, ref_out, ref_lse, w.name)
+
+
+def test_flex_positions_across_scan_passes():
+    """Block positions are scanned in passes of 8192 tokens (chunks of 1024):
+    a sequence longer than one pass, with fixed blocks too, checked at rows
+    around the chunk and pass edges and at the ends, documents crossing them."""
+    x = W.flex_custom(2, 9000, 4, 2, 64, mask="block_causal", doc_min=20, doc_max=900,
+                      fixed_block_size=700, seed=210)
+    S = 9000
+    must = []
+    for b in range(2):
+        for c in (0, 1023, 1024, 2047, 2048, 8191, 8192, 8193, S - 1):
+            must.append((b, c))
+    rows = W.sample_rows(2, S, 24, 1103, tuple(must))
+    announce(f"flex two scan passes: {rows.numel()} rows")
+    out, lse = run_flex(x)
+    ref_out, ref_lse, _ = ref_flex(x, rows=rows)
+    r = rows.numpy()
+    got_out = out.transpose(0, 2, 1, 3).reshape(2 * S, 4, 64)[r]
+    got_lse = lse.transpose(0, 2, 1).reshape(2 * S, 4)[r]
+    assert_flex_close(got_out, got_lse, ref_out, ref_lse, "two scan passes")

@@ -1174,52 +1174,50 @@ __global__ __launch_bounds__(1024) void flex_positions_kernel(const int32_t* __r
 {
     constexpr int PER = 8;                       // tokens per thread and pass
     constexpr int NWV = 1024 / 64;               // waves
-    __shared__ int wmax[NWV];
+    __shared__ int wmax[2][NWV];
     const int b = blockIdx.x, t = threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
     for (size_t u = (size_t)b * 1024 + t; u < nones; u += (size_t)gridDim.x * 1024) ones[u] = 1;
     if (!pos) return;
     const int32_t* tk = tokens ? tokens + (size_t)b * S : nullptr;
     int32_t* ps = pos + (size_t)b * S;
-    int carry = 0;                               // start column after the last eos of earlier passes
+    int carry = 0;                               // start column after the last eos so far
     for (int base = 0; base < S; base += 1024 * PER) {
-        const int lo = base + t * PER;
+        // token base + 1024 c + t of chunk c: all loads go out first (coalesced)
         int is_eos[PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) is_eos[e] = (tk && lo + e < S) ? (tk[lo + e] == eos) : 0;
-        int last = 0;
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-            if (is_eos[e]) last = lo + e + 1;
-        // running max over the threads' segments: inclusive within the wave
-        // by shuffles, then over the waves before through LDS
-        int inc = last;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int other = __shfl_up(inc, d, 64);
-            if (lane >= d) inc = max(inc, other);
+        for (int c = 0; c < PER; ++c) {
+            const int u = base + 1024 * c + t;
+            is_eos[c] = (tk && u < S) ? (tk[u] == eos) : 0;
         }
-        if (lane == 63) wmax[wv] = inc;
-        __syncthreads();
-        int before = 0, pass_max = 0;
-        for (int w = 0; w < NWV; ++w) {
-            const int x = wmax[w];
-            if (w < wv) before = max(before, x);
-            pass_max = max(pass_max, x);
-        }
-        const int prev = __shfl_up(inc, 1, 64);   // inclusive value of the lane before
-        int start = max(carry, max(before, lane > 0 ? prev : 0));
-        __syncthreads();                         // wmax[] is rewritten by the next pass
 #pragma unroll
-        for (int e = 0; e < PER; ++e) {
-            const int u = lo + e;
+        for (int c = 0; c < PER; ++c) {
+            const int u = base + 1024 * c + t;
+            // running max of (eos column + 1) over the chunk's tokens up to
+            // this one: inclusive within the wave by shuffles, then over the
+            // waves before through LDS (two slots: one barrier per chunk)
+            int inc = is_eos[c] ? u + 1 : 0;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int other = __shfl_up(inc, d, 64);
+                if (lane >= d) inc = max(inc, other);
+            }
+            if (lane == 63) wmax[c & 1][wv] = inc;
+            __syncthreads();
+            int before = carry, chunk_max = carry;
+            for (int w = 0; w < NWV; ++w) {
+                const int x = wmax[c & 1][w];
+                if (w < wv) before = max(before, x);
+                chunk_max = max(chunk_max, x);
+            }
+            const int prev = __shfl_up(inc, 1, 64);   // inclusive value of the lane before
+            const int start = max(before, lane > 0 ? prev : 0);   // after the last eos before u
             if (u < S) {
                 const int st = fixed > 0 ? max(start, (u / fixed) * fixed) : start;
                 ps[u] = u - st;
             }
-            if (is_eos[e]) start = u + 1;
+            carry = chunk_max;
         }
-        carry = max(carry, pass_max);
     }
 }
 
