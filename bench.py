@@ -34,7 +34,15 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / fp16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 DEFAULT_WORKLOAD = "full_causal_8k"
-KERNEL_SRC = os.path.join(ROOT, "transformer_attention_03_amd", "csrc", "inkattn.hip")
+# the forward kernel's sources: its traffic record holds their combined sha256
+KERNEL_SRCS = [os.path.join(ROOT, "transformer_attention_03_amd", "csrc", f) for f in ("inkattn.hip", "common.h")]
+
+
+def kernel_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def allowed_counts(x) -> np.ndarray:
@@ -126,8 +134,7 @@ def traffic_from_profiles(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return rec.get("hbm_bytes_per_launch")
 
