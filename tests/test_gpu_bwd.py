@@ -108,6 +108,11 @@ SMALL = {
     "extent_beyond_S": dict(B=1, S=150, Hq=4, Hkv=2, D=64, E=400, structure="packed", doc_min=10, doc_max=90,
                             seed=307),
     "G2_D64_window": dict(B=1, S=333, Hq=4, Hkv=2, D=64, E=64, window=100, structure="single", seed=308),
+    # 16 heads per K/V head: four head chunks per group in the dQ grid; G = 3:
+    # one head per dQ unit, four query blocks per workgroup
+    "G16_chunks": dict(B=1, S=180, Hq=16, Hkv=1, D=128, E=70, structure="single", seed=309),
+    "G3_D64": dict(B=2, S=150, Hq=6, Hkv=2, D=64, E=40, window=60, structure="tail_pad", max_tail_pad=30,
+                   seed=310),
 }
 
 
