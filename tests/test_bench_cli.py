@@ -26,13 +26,21 @@ def _bench_module():
 
 
 def test_traffic_records_follow_the_kernel_sources(tmp_path):
-    """The committed HBM-traffic records are used only while the forward
-    kernel's sources are the ones they were measured on."""
+    """A committed HBM-traffic record is used only while the forward kernel's
+    sources are the ones it was measured on (a synthetic record here)."""
+    import json
     bench = _bench_module()
-    for wl in ("full_causal_8k", "local", "long", "flex_block_causal"):
-        t = bench.traffic_from_profiles(wl)
-        assert t is not None and t > 0, f"{wl}: record missing or stale"
-    changed = tmp_path / "common.h"
-    changed.write_bytes(open(bench.KERNEL_SRCS[1], "rb").read() + b"\n// changed\n")
-    bench.KERNEL_SRCS = [bench.KERNEL_SRCS[0], str(changed)]
-    assert bench.traffic_from_profiles("full_causal_8k") is None
+    srcs = []
+    for name, text in (("inkattn.hip", b"// kernel\n"), ("common.h", b"// shared\n")):
+        f = tmp_path / name
+        f.write_bytes(text)
+        srcs.append(str(f))
+    bench.KERNEL_SRCS = srcs
+    bench.ROOT = str(tmp_path)
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernel_source_sha256": bench.kernel_source_sha256(), "hbm_bytes_per_launch": 12345}
+    (tmp_path / "profiles" / "traffic_attn_fwd_kernel_wl.json").write_text(json.dumps(rec))
+    assert bench.traffic_from_profiles("wl") == 12345
+    assert bench.traffic_from_profiles("other") is None          # no record
+    (tmp_path / "common.h").write_bytes(b"// shared, changed\n")
+    assert bench.traffic_from_profiles("wl") is None              # either source changed
