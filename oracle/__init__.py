@@ -48,36 +48,40 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    lib.attn_oracle_fwd.restype = ctypes.c_int
+    lib.attn_oracle_fwd.argtypes = [
+        P, P, P, P, ctypes.c_int, P, P, P, P, P,
+        ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int,
+        P, ctypes.c_int64, P, P, P, ctypes.c_int]
+    lib.flex_oracle_fwd.restype = ctypes.c_int
+    lib.flex_oracle_fwd.argtypes = [
+        P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        P, ctypes.c_int64, P, P, P, ctypes.c_int]
+    lib.attn_oracle_bwd.restype = ctypes.c_int
+    lib.attn_oracle_bwd.argtypes = [
+        P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+    lib.attn_oracle_max_threads.restype = ctypes.c_int
+    lib.attn_oracle_mask.restype = ctypes.c_int
+    lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
+                                     ctypes.c_int]
+    return lib
+
+
 def _load():
     global _lib
     with _lock:
         if _lib is None:
             build()
-            lib = ctypes.CDLL(_LIB)
-            P = ctypes.c_void_p
-            lib.attn_oracle_fwd.restype = ctypes.c_int
-            lib.attn_oracle_fwd.argtypes = [
-                P, P, P, P, ctypes.c_int, P, P, P, P, P,
-                ctypes.c_int64, ctypes.c_int64,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int,
-                P, ctypes.c_int64, P, P, P, ctypes.c_int]
-            lib.flex_oracle_fwd.restype = ctypes.c_int
-            lib.flex_oracle_fwd.argtypes = [
-                P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                P, ctypes.c_int64, P, P, P, ctypes.c_int]
-            lib.attn_oracle_bwd.restype = ctypes.c_int
-            lib.attn_oracle_bwd.argtypes = [
-                P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
-            lib.attn_oracle_max_threads.restype = ctypes.c_int
-            lib.attn_oracle_mask.restype = ctypes.c_int
-            lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
-                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
-                                             ctypes.c_int]
-            _lib = lib
+            _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
 
 

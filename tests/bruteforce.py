@@ -74,3 +74,21 @@ def forward(q, k, v, profiles, sink, valid, positions, window=None):
             out[b, :, h, :] = o
             lse[b, :, h] = l
     return out, lse
+
+
+def mask(valid, positions, window=None):
+    """Whole visibility matrix ``[B, S, S]`` (bool) of queries and keys that are the
+    same tokens: both real, key not after the query, same document by reset scan,
+    column distance below the window."""
+    valid = valid.cpu().numpy().astype(bool)
+    pos = positions.cpu().numpy().astype(np.int64)
+    B, S = valid.shape
+    doc = doc_ids_by_reset_scan(pos)
+    ii, jj = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    out = np.zeros((B, S, S), dtype=bool)
+    for b in range(B):
+        m = (jj <= ii) & valid[b][:, None] & valid[b][None, :] & (doc[b][:, None] == doc[b][None, :])
+        if window is not None and window > 0:
+            m &= (ii - jj) < window
+        out[b] = m
+    return out
