@@ -42,9 +42,13 @@
  *    (Sk*Hkv*D*2 bytes) and one (batch row, head) block of profiles (Sq*E
  *    entries) below 4 GiB each.
  *  - Preconditions not checked (they would need a device read): positions and
- *    key_positions hold values in [0, 2^30); bf16 values of v lie within
- *    +-65504 (v is converted exactly to fp16 for the PV product); inputs at
- *    tokens that are not valid hold finite values.
+ *    key_positions hold values in [0, 2^30); inputs at tokens that are not
+ *    valid hold finite values.
+ *  - Values of v: the probabilities multiply v in fp16 (exact for bf16 values
+ *    within +-65504).  A value at a real key outside that range, or not
+ *    finite, cannot be represented: the forward then writes NaN at (at least)
+ *    every output element it would enter, never a clamped result, and
+ *    attn_check_values reports INKATTN_ERR_RANGE for the workspace.
  */
 #ifndef INKATTN_H
 #define INKATTN_H
@@ -67,7 +71,8 @@ enum inkattn_status {
     INKATTN_ERR_UNSUPPORTED = 3, /* head_dim / dtype outside what is built     */
     INKATTN_ERR_ALIGN = 4,       /* a pointer is not aligned as required       */
     INKATTN_ERR_WORKSPACE = 5,   /* workspace missing or too small             */
-    INKATTN_ERR_LAUNCH = 6       /* a HIP launch reported an error             */
+    INKATTN_ERR_LAUNCH = 6,      /* a HIP launch reported an error             */
+    INKATTN_ERR_RANGE = 7        /* a value outside the supported range        */
 };
 
 /*
@@ -76,7 +81,9 @@ enum inkattn_status {
  * query block and per 64-key tile, then one int32 document start column per
  * key, padded to whole 64-key tiles; each part rounded up to 256 bytes),
  * followed by an fp16 copy of the values in whole 64-key tiles,
- * B*Hkv*ceil(Sk/64)*64*D*2 bytes.  Never fails; returns 0 for non-positive B.
+ * B*Hkv*ceil(Sk/64)*64*D*2 bytes, and one flag byte per staged tile (rounded
+ * up to 256 bytes; see attn_check_values).  Never fails; returns 0 for
+ * non-positive B.
  */
 size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D);
 
@@ -187,12 +194,14 @@ int attn_plan(const uint8_t* valid, const uint8_t* key_valid,
  * the attention kernel stages from, in `workspace` after the summaries: per
  * (batch row, K/V head, 64-key tile) the tile's values transposed, D rows of
  * 64 keys, the keys of each row in the order the kernel's PV product consumes
- * them (a layout private to this library).  Each value is saturated to
- * +-65504; values of keys whose key_valid is 0, and of the padding past Sk,
- * are written as 0.  The probabilities multiply the values in fp16 MFMA (fp16
- * keeps 11 significant bits where bf16 keeps 8; a bf16 value inside the fp16
- * range converts exactly).  key_valid defaults as in attn_fwd.  One call per
- * layer (the values differ per layer).
+ * them (a layout private to this library).  Values of keys whose key_valid
+ * is 0, and of the padding past Sk, are written as 0.  The probabilities
+ * multiply the values in fp16 MFMA (fp16 keeps 11 significant bits where bf16
+ * keeps 8; a bf16 value inside the fp16 range converts exactly).  A real value
+ * outside +-65504 or not finite is written as NaN and sets its tile's flag
+ * byte (every tile's byte is rewritten on every call; attn_check_values reads
+ * them).  key_valid defaults as in attn_fwd.  One call per layer (the values
+ * differ per layer).
  */
 int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_valid, int64_t query_offset,
                       int B, int Sq, int Sk, int Hkv, int D, void* workspace, size_t workspace_bytes,
@@ -224,6 +233,33 @@ int attn_debug_counts(const uint8_t* valid, const uint8_t* key_valid,
                       const int32_t* positions, const int32_t* key_positions,
                       int64_t window, int64_t query_offset, int B, int Sq, int Sk,
                       int32_t* n_allowed, void* stream);
+
+/*
+ * attn_debug_mask -- the whole visibility matrix mask[B, Sq, Sk] (uint8, 1 =
+ * key j allowed for query i), from the same device predicate attn_fwd
+ * applies on masked tiles (the masks are rebuilt from each forward's token
+ * validity and positions: page "nemo_automodel.components.models.inkling2.
+ * flex_attention", class description).  Meant for small shapes: B*Sq*Sk must
+ * not exceed 2^32 (INKATTN_ERR_SHAPE otherwise).  Same argument meanings as
+ * attn_fwd; `mask` is a caller-owned device buffer of B*Sq*Sk bytes.
+ */
+int attn_debug_mask(const uint8_t* valid, const uint8_t* key_valid,
+                    const int32_t* positions, const int32_t* key_positions,
+                    int64_t window, int64_t query_offset, int B, int Sq, int Sk,
+                    uint8_t* mask, void* stream);
+
+/*
+ * attn_check_values -- reads back the flag bytes the last value staging
+ * (attn_fwd, attn_stage_values or flex_attn_fwd) wrote into `workspace` for
+ * these sizes, after waiting for `stream` (this call synchronises the
+ * stream).  Returns INKATTN_OK when every real value of v fitted fp16, or
+ * INKATTN_ERR_RANGE naming the first (batch row, K/V head, key tile) that
+ * held a value outside +-65504 or not finite; the forward's output is then
+ * NaN where that value enters it.  For flex_attn_fwd's workspace pass its
+ * (B, Sq, Sk, Hkv, D): the flags sit at the same place.
+ */
+int attn_check_values(const void* workspace, size_t workspace_bytes, int B, int Sq, int Sk, int Hkv, int D,
+                      void* stream);
 
 /*
  * attn_debug_tiles -- the class attn_fwd gives each (query block, key tile):

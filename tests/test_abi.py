@@ -41,10 +41,13 @@ def test_status_strings_and_sizes():
     assert binding.attn_query_block() == 32 and binding.attn_key_tile() == 64
     # tile summaries (16 B per query block / key tile) + key start columns (4 B per key),
     # each rounded up to 256 B, then the fp16 values
-    assert binding.attn_fwd_workspace_size(1, 128, 128, 2, 64) == 256 + 512 + 128 * 2 * 64 * 2
+    # and one flag byte per staged value tile (rounded up to 256 B)
+    assert binding.attn_fwd_workspace_size(1, 128, 128, 2, 64) == 256 + 512 + 128 * 2 * 64 * 2 + 256
     # values are staged in whole 64-key tiles: 65 keys take two
-    assert binding.attn_fwd_workspace_size(2, 33, 65, 1, 128) == 256 + 1024 + 2 * 128 * 128 * 2
-    assert binding.attn_fwd_workspace_size(40, 64, 64, 1, 64) == 2048 + 40 * 64 * 4 + 40 * 64 * 64 * 2
+    assert binding.attn_fwd_workspace_size(2, 33, 65, 1, 128) == 256 + 1024 + 2 * 128 * 128 * 2 + 256
+    assert binding.attn_fwd_workspace_size(40, 64, 64, 1, 64) == 2048 + 40 * 64 * 4 + 40 * 64 * 64 * 2 + 256
+    assert binding.attn_fwd_workspace_size(1, 64, 64 * 300, 1, 64) == (4864 + 64 * 300 * 4 + 64 * 300 * 64 * 2
+                                                                       + 512)
     assert binding.attn_fwd_workspace_size(0, 10, 10, 1, 64) == 0
 
 
@@ -69,7 +72,8 @@ def call(**over):
     (dict(Sq=1 << 30, Sk=1 << 30), 2), (dict(qoff=-1, key_valid=A), 2),
     (dict(D=96), 3), (dict(D=256), 3), (dict(pdt=7), 3),
     (dict(q=A + 8), 4), (dict(out=A + 4), 4), (dict(profiles=A + 2), 4), (dict(positions=A + 2), 4),
-    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(wsb=256 + 256 + 64 * 2 * 128 * 2 - 1), 5), (dict(ws=A + 8), 4),
+    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(wsb=256 + 256 + 64 * 2 * 128 * 2), 5), (dict(ws=A + 8), 4),
+    (dict(wsb=256 + 256 + 64 * 2 * 128 * 2 + 255), 5),
     (dict(Sq=1 << 20, Sk=1 << 20, Hkv=16, Hq=16, key_valid=A), 2),   # one k/v row of 4 GiB
 ])
 def test_host_validation_rejects_before_launch(over, status):
@@ -169,3 +173,65 @@ def test_bwd_workspace_size():
     assert binding.attn_bwd_workspace_size(0, 64, 64, 4, 2, 128) == 0
     # bf16 profile gradients need only 2-byte alignment: the workspace check is what stops this call
     assert bwd_call(pdt=1, profiles=A + 2, dprof=A + 2, wsb=8) == 5
+
+
+def test_late_size_checks_run_before_any_launch():
+    """A call whose tile count overflows the pre-pass grid is rejected by its checks alone: the
+    status is the shape error, not a launch error (this container has no GPU, so an attempted
+    launch would fail with INKATTN_ERR_LAUNCH)."""
+    big = dict(B=4096, Sq=1, Sk=(1 << 25) - 64, Hq=1, Hkv=1, D=64, wsb=1 << 62)
+    assert flex_call(**big) == 2
+    assert "too many tiles" in binding.attn_last_error()
+    assert call(E=1, key_valid=A, **big) == 2
+    assert "too many tiles" in binding.attn_last_error()
+
+
+def debug_mask_call(**over):
+    a = dict(valid=A, key_valid=None, positions=None, key_positions=None, window=0, qoff=0, B=1, Sq=64, Sk=64,
+             mask=A, stream=None)
+    a.update(over)
+    return binding.load().attn_debug_mask(P(a["valid"]), P(a["key_valid"]), P(a["positions"]),
+                                          P(a["key_positions"]), a["window"], a["qoff"], a["B"], a["Sq"],
+                                          a["Sk"], P(a["mask"]), P(a["stream"]))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mask=None), 1), (dict(valid=None), 1), (dict(Sk=10), 1), (dict(B=-1), 2),
+    (dict(B=2, Sq=1 << 16, Sk=1 << 16, key_valid=A), 2), (dict(positions=A + 1), 4),
+])
+def test_debug_mask_validation(over, status):
+    assert debug_mask_call(**over) == status
+    assert binding.attn_last_error() != ""
+
+
+def test_debug_mask_empty_is_ok():
+    assert debug_mask_call(B=0) == 0 and debug_mask_call(Sq=0, Sk=0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1 << 20, 1, 64, 64, 2, 128), 5), ((A, 16, 1, 64, 64, 2, 128), 5), ((A, 1 << 20, 1, 64, 64, 2, 96), 3),
+    ((A + 8, 1 << 20, 1, 64, 64, 2, 128), 4), ((A, 1 << 20, -1, 64, 64, 2, 128), 2),
+])
+def test_check_values_validation(args, status):
+    ws, wsb, B, Sq, Sk, Hkv, D = args
+    assert binding.load().attn_check_values(P(ws), wsb, B, Sq, Sk, Hkv, D, None) == status
+    assert binding.attn_last_error() != ""
+
+
+def test_check_values_without_tiles_is_ok():
+    assert binding.load().attn_check_values(None, 0, 0, 64, 64, 2, 128, None) == 0
+    assert binding.load().attn_check_values(None, 0, 1, 64, 0, 2, 128, None) == 0
+    assert binding.attn_status_string(7) == "a value outside the supported range"
+
+
+def test_int64_positions_and_tokens_are_range_checked_before_narrowing():
+    import torch
+    ok = binding._narrow_int64(torch.tensor([0, 5, (1 << 30) - 1]), "positions", 0, binding.POS_LIMIT)
+    assert ok.dtype == torch.int32 and ok.tolist() == [0, 5, (1 << 30) - 1]
+    for bad in ([0, 1 << 30], [-1, 3], [1 << 40]):
+        with pytest.raises(ValueError, match="positions"):
+            binding._narrow_int64(torch.tensor(bad), "positions", 0, binding.POS_LIMIT)
+    with pytest.raises(ValueError, match="tokens"):
+        binding._narrow_int64(torch.tensor([1 << 31]), "tokens", -(1 << 31), 1 << 31)
+    assert binding._narrow_int64(torch.tensor([-(1 << 31), 7]), "tokens", -(1 << 31), 1 << 31).tolist() == [
+        -(1 << 31), 7]

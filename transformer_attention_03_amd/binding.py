@@ -8,6 +8,8 @@ library is missing, or a tensor is not on a GPU, the call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 import threading
 from typing import Optional, Tuple
@@ -20,11 +22,13 @@ LIB_PATH = os.path.join(_PKG, "libinkattn.so")
 INKATTN_F32 = 0
 INKATTN_BF16 = 1
 STATUS = {0: "INKATTN_OK", 1: "INKATTN_ERR_NULL", 2: "INKATTN_ERR_SHAPE", 3: "INKATTN_ERR_UNSUPPORTED",
-          4: "INKATTN_ERR_ALIGN", 5: "INKATTN_ERR_WORKSPACE", 6: "INKATTN_ERR_LAUNCH"}
+          4: "INKATTN_ERR_ALIGN", 5: "INKATTN_ERR_WORKSPACE", 6: "INKATTN_ERR_LAUNCH", 7: "INKATTN_ERR_RANGE"}
+INKATTN_ERR_RANGE = 7
 
 # Every symbol include/inkattn.h declares.
 EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
-           "attn_debug_counts", "attn_debug_tiles", "flex_attn_workspace_size", "flex_attn_fwd",
+           "attn_debug_counts", "attn_debug_mask", "attn_debug_tiles", "attn_check_values",
+           "flex_attn_workspace_size", "flex_attn_fwd",
            "attn_bwd_workspace_size", "attn_bwd",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
@@ -60,6 +64,10 @@ def load() -> ctypes.CDLL:
             lib.attn_plan.argtypes = [P, P, P, P, I64, I, I, I, P, SZ, P]
             lib.attn_debug_counts.restype = I
             lib.attn_debug_counts.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P]
+            lib.attn_debug_mask.restype = I
+            lib.attn_debug_mask.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P]
+            lib.attn_check_values.restype = I
+            lib.attn_check_values.argtypes = [P, SZ, I, I, I, I, I, P]
             lib.attn_debug_tiles.restype = I
             lib.attn_debug_tiles.argtypes = [P, P, P, P, I64, I64, I, I, I, P, P, SZ, P]
             lib.flex_attn_workspace_size.restype = SZ
@@ -113,16 +121,56 @@ def _mask_tensor(t, name, device):
     return None if t is None else (t.view(torch.uint8) if t.dtype == torch.bool else t)
 
 
+POS_LIMIT = 1 << 30   # positions lie in [0, 2^30) (include/inkattn.h)
+
+
+def _narrow_int64(t: torch.Tensor, name: str, lo: int, hi: int) -> torch.Tensor:
+    """int32 copy of an int64 tensor after checking lo <= t < hi (one device read)."""
+    if t.numel():
+        mn, mx = torch.aminmax(t)
+        mn, mx = int(mn), int(mx)
+        if mn < lo or mx >= hi:
+            raise ValueError(f"{name}: values must lie in [{lo}, {hi}) to narrow to int32 (got {mn}..{mx})")
+    return t.to(torch.int32)
+
+
 def _pos_tensor(t, name, device):
     t = _dev(t, name, (torch.int32, torch.int64), device)
     if t is not None and t.dtype == torch.int64:
-        t = t.to(torch.int32)   # logical positions are below 2^30 by contract
+        t = _narrow_int64(t, name, 0, POS_LIMIT)
     return t
 
 
+def _token_tensor(t, name, device):
+    t = _dev(t, name, (torch.int32, torch.int64), device)
+    if t is not None and t.dtype == torch.int64:
+        t = _narrow_int64(t, name, -(1 << 31), 1 << 31)
+    return t
+
+
+def _resolve_stream(stream, device):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _on_call_stream(fn):
+    """Run ``fn`` with torch's current stream set to the call's ``stream`` argument (when
+    one is given), so that the temporaries the binding allocates (default workspace,
+    outputs, int32 copies of int64 positions) belong to the stream the library's kernels
+    are enqueued on, and the copies are ordered before those kernels."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _stream(stream, device) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_resolve_stream(stream, device).cuda_stream)
 
 
 def attn_fwd_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
@@ -173,6 +221,7 @@ def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_posit
     return args, out, lse, keep
 
 
+@_on_call_stream
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.Tensor,
              sink: torch.Tensor, valid: torch.Tensor, key_valid: Optional[torch.Tensor] = None,
              positions: Optional[torch.Tensor] = None, key_positions: Optional[torch.Tensor] = None,
@@ -197,6 +246,7 @@ def attn_bwd_workspace_size(B: int, Sq: int, Sk: int, Hq: int, Hkv: int, D: int)
     return int(load().attn_bwd_workspace_size(B, Sq, Sk, Hq, Hkv, D))
 
 
+@_on_call_stream
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.Tensor,
              sink: torch.Tensor, valid: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
              dout: torch.Tensor, dlse: Optional[torch.Tensor] = None,
@@ -259,6 +309,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.
     return dq, dk, dv, dprof, dsink
 
 
+@_on_call_stream
 def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=None, key_positions=None,
                      window=None, query_offset: int = 0, out=None, lse=None, workspace=None, stream=None):
     """The attention kernel alone, on a workspace filled by :func:`attn_plan` (same masks) and
@@ -272,6 +323,7 @@ def attn_fwd_planned(q, k, v, profiles, sink, valid, key_valid=None, positions=N
     return out, lse
 
 
+@_on_call_stream
 def planned_forward_launchers(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
                               key_positions=None, window=None, query_offset: int = 0, out=None, lse=None,
                               workspace=None, stream=None):
@@ -303,6 +355,7 @@ def planned_forward_launchers(q, k, v, profiles, sink, valid, key_valid=None, po
     return plan, stage_values, attention, out, lse
 
 
+@_on_call_stream
 def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_offset: int = 0,
               Sk: Optional[int] = None, workspace: Optional[torch.Tensor] = None, Hkv: int = 0, D: int = 0,
               stream=None) -> torch.Tensor:
@@ -324,6 +377,7 @@ def attn_plan(valid, key_valid=None, positions=None, key_positions=None, query_o
     return workspace
 
 
+@_on_call_stream
 def attn_stage_values(v, valid, key_valid=None, query_offset: int = 0, Sq: Optional[int] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """fp16 copy of the values into ``workspace`` (after the summaries) for :func:`attn_fwd_planned`."""
@@ -344,6 +398,7 @@ def attn_stage_values(v, valid, key_valid=None, query_offset: int = 0, Sq: Optio
     return workspace
 
 
+@_on_call_stream
 def attn_debug_counts(valid, key_valid=None, positions=None, key_positions=None, window=None,
                       query_offset: int = 0, Sk: Optional[int] = None, stream=None) -> torch.Tensor:
     """Allowed keys per query row, int32 [B, Sq], from the kernels' mask predicate."""
@@ -363,6 +418,38 @@ def attn_debug_counts(valid, key_valid=None, positions=None, key_positions=None,
     return n
 
 
+@_on_call_stream
+def attn_debug_mask(valid, key_valid=None, positions=None, key_positions=None, window=None,
+                    query_offset: int = 0, Sk: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Whole visibility matrix uint8 [B, Sq, Sk] (1: key allowed) from the kernels' mask predicate
+    (small shapes: at most 2^32 entries)."""
+    dev = valid.device
+    valid_u8 = _mask_tensor(valid, "valid", dev)
+    kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
+    pos = _pos_tensor(positions, "positions", dev)
+    kpos = _pos_tensor(key_positions, "key_positions", dev)
+    B, Sq = valid_u8.shape
+    if Sk is None:
+        Sk = kvalid_u8.shape[1] if kvalid_u8 is not None else Sq
+    m = torch.empty((B, Sq, Sk), dtype=torch.uint8, device=dev)
+    rc = load().attn_debug_mask(_ptr(valid_u8), _ptr(kvalid_u8), _ptr(pos), _ptr(kpos),
+                                0 if window is None else int(window), int(query_offset), B, Sq, Sk,
+                                _ptr(m), _stream(stream, dev))
+    _check(rc, "attn_debug_mask")
+    return m
+
+
+@_on_call_stream
+def attn_check_values(workspace: torch.Tensor, B: int, Sq: int, Sk: int, Hkv: int, D: int, stream=None) -> int:
+    """Status of the last value staging into ``workspace`` (waits for ``stream``): 0 when every
+    real value of v fitted fp16, else INKATTN_ERR_RANGE (the output is NaN where such a value
+    enters it).  Returns the status; the detail is in :func:`attn_last_error`."""
+    dev = workspace.device
+    return int(load().attn_check_values(_ptr(workspace), workspace.numel() * workspace.element_size(), int(B),
+                                        int(Sq), int(Sk), int(Hkv), int(D), _stream(stream, dev)))
+
+
+@_on_call_stream
 def attn_debug_tiles(valid, key_valid=None, positions=None, key_positions=None, window=None,
                      query_offset: int = 0, Sk: Optional[int] = None, stream=None) -> torch.Tensor:
     """Tile classes uint8 [B, ceil(Sq/32), ceil(Sk/64)]: 0 skip, 1 masked, 2 full."""
@@ -429,6 +516,7 @@ def flex_attn_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
     return int(load().flex_attn_workspace_size(B, Sq, Sk, Hkv, D))
 
 
+@_on_call_stream
 def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   sink_weights: Optional[torch.Tensor] = None, tokens: Optional[torch.Tensor] = None,
                   eos_id: int = 0, fixed_block_size: Optional[int] = None, sliding_window: int = 0,
@@ -450,6 +538,7 @@ def flex_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+@_on_call_stream
 def flex_forward_launcher(q, k, v, sink_weights=None, tokens=None, eos_id: int = 0, fixed_block_size=None,
                           sliding_window: int = 0, scale=None, out=None, lse=None, workspace=None, stream=None):
     """Marshals the arguments of :func:`flex_attn_fwd` once and returns
@@ -474,7 +563,7 @@ def _marshal_flex(q, k, v, sink_weights, tokens, eos_id, fixed_block_size, slidi
     k = _dev(k, "k", (torch.bfloat16,), dev)
     v = _dev(v, "v", (torch.bfloat16,), dev)
     sink_weights = _dev(sink_weights, "sink_weights", (torch.float32,), dev)
-    tokens = _pos_tensor(tokens, "tokens", dev)
+    tokens = _token_tensor(tokens, "tokens", dev)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k and v must be 4-d")
     B, Hq, Sq, D = q.shape

@@ -156,6 +156,12 @@ size_t round256(size_t x);
 size_t tile_summary_bytes(int B, int Sq, int Sk);
 size_t summaries_bytes(int B, int Sq, int Sk);
 size_t values_bytes(int B, int Sk, int Hkv, int D);
+// per (batch row, K/V head, key tile) one byte: the staging found a value fp16 cannot hold
+size_t value_flags_bytes(int B, int Sk, int Hkv);
+// whole forward workspace: summaries, fp16 values, value flags
+size_t fwd_workspace_bytes(int B, int Sq, int Sk, int Hkv, int D);
+// tile and grid counts every launch of a forward needs must fit its index types
+int check_tile_counts(int B, int Sq, int Sk, int Hq, int Hkv);
 
 struct MaskArgs {
     const uint8_t* key_valid;

@@ -55,6 +55,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <type_traits>
 
@@ -410,8 +411,9 @@ void attn_fwd_kernel(FwdParams p)
     };
 
     // ---- K / V staging by LDS DMA.  The K resource covers rows 0..Sk-1 of
-    // this (batch row, K/V head), rows past Sk read as zero; the V^T resource
-    // covers the staged tiles of this (batch row, K/V head).
+    // this (batch row, K/V head), rows past Sk read as zero (their offsets
+    // lie past the resource's size); the V^T resource covers the staged tiles
+    // of this (batch row, K/V head).
     const int krow = (int)p.k_ts * 2;                   // bytes between consecutive keys
     const unsigned nrec = p.Sk > 0 ? (unsigned)((size_t)(p.Sk - 1) * krow + D * 2) : 0u;
     const __amdgpu_buffer_rsrc_t krsrc = uniform_rsrc(p.k + b * p.k_bs + g * p.k_hs, nrec);
@@ -433,9 +435,11 @@ void attn_fwd_kernel(FwdParams p)
             // (the offsets are named values: an expression written into the
             // builtin's argument list keeps the host pass from emitting the
             // kernel's launch stub)
-            const int soff = (j0 + a * L::RPI) * krow;
+            // the whole byte offset travels in the offset register, which the
+            // buffer range check covers: rows past Sk read as zero
+            const int voff = kvoff + (j0 + a * L::RPI) * krow;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                krsrc, (lds_void*)(smem + K_OFF + bufsel * KBYTES + a * L::KGP), 16, kvoff, soff, 0, 0);
+                krsrc, (lds_void*)(smem + K_OFF + bufsel * KBYTES + a * L::KGP), 16, voff, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < NVG / NW; ++u) {
@@ -899,22 +903,23 @@ void attn_fwd_kernel(FwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Value staging: v (bf16) -> fp16, saturated to the fp16 range, zero at keys
-// that are not real, so that a masked key's weight 0 never meets a value that
-// fp16 cannot hold.  One thread per 8 elements.
-// ---------------------------------------------------------------------------
-// One workgroup of D threads per (batch row, K/V head, 64-key tile): v (bf16)
-// -> V^T (fp16, saturated to +-65504, 0 at keys that are not real or lie past
-// Sk), the keys of each row in vt_slot order.  Thread (slot group sg, dim
-// chunk dc) loads the 8 keys of output slots 8 sg .. 8 sg + 7 at dims
+// Value staging.  One workgroup of D threads per (batch row, K/V head, 64-key
+// tile): v (bf16) -> V^T (fp16), the keys of each row in vt_slot order, 0 at
+// keys that are not real or lie past Sk (a masked key's weight 0 never meets
+// a value fp16 cannot hold).  A real value outside +-65504 (or not finite) has
+// no fp16 form: it is written as NaN, so that the rows that use it come out
+// NaN instead of silently wrong, and the tile's byte in `bad` is set (0
+// otherwise; every tile writes its byte on every call).  Thread (slot group
+// sg, dim chunk dc) loads the 8 keys of output slots 8 sg .. 8 sg + 7 at dims
 // 8 dc .. 8 dc + 7, transposes the 8 x 8 block in registers and writes 8 rows
 // of 16 bytes.
+// ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void stage_values_kernel(const __bf16* __restrict__ v,
                                                          const uint8_t* __restrict__ key_valid,
                                                          int Sk, int Hkv, int nKT, long long v_bs,
                                                          long long v_ts, long long v_hs,
-                                                         _Float16* __restrict__ vt)
+                                                         _Float16* __restrict__ vt, uint8_t* __restrict__ bad)
 {
     constexpr int CH = D / 8;                 // 16-byte chunks per key row
     const int t = blockIdx.x;                 // ((b * Hkv + g) * nKT + kt)
@@ -936,16 +941,24 @@ __global__ __launch_bounds__(D) void stage_values_kernel(const __bf16* __restric
         ok[tt] = key_valid[(size_t)b * Sk + j];
     }
     f16x8 rows[8];
+    int out_of_range = 0;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
         const int key = 16 * (sg >> 1) + 8 * (tt >> 2) + 4 * (sg & 1) + ((tt & 3) ^ 3);
         f16x8 y = f16x8{};
         if (ok[tt] && kt * BN + key < Sk) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (_Float16)fminf(fmaxf((float)xr[tt][e], -65504.0f), 65504.0f);
+            for (int e = 0; e < 8; ++e) {
+                const float f = (float)xr[tt][e];
+                const bool fits = fabsf(f) <= 65504.0f;   // false for NaN and infinities too
+                out_of_range |= !fits;
+                y[e] = fits ? (_Float16)f : (_Float16)__builtin_nanf("");
+            }
         }
         rows[tt] = y;
     }
+    out_of_range = __syncthreads_or(out_of_range);
+    if (threadIdx.x == 0) bad[t] = (uint8_t)(out_of_range != 0);
     _Float16* dst = vt + (size_t)t * D * BN;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -985,6 +998,26 @@ __global__ void debug_counts_kernel(const uint8_t* __restrict__ valid, const uin
         __syncthreads();
     }
     if (threadIdx.x == 0) n_allowed[qrow] = red[0];
+}
+
+// One thread per (batch row, query, key): the same predicate as the attention
+// kernel's masked tiles, written as one byte.
+__global__ void debug_mask_kernel(const uint8_t* __restrict__ valid, const uint8_t* __restrict__ key_valid,
+                                  const int32_t* __restrict__ positions, const int32_t* __restrict__ key_positions,
+                                  int window, int qoff, int Sq, int Sk, size_t n, uint8_t* __restrict__ mask)
+{
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int j = (int)(idx % Sk);
+    const size_t qrow = idx / Sk;               // b * Sq + i
+    const int b = (int)(qrow / Sq), i = (int)(qrow % Sq);
+    const int gi = qoff + i;
+    const bool qreal = valid[qrow] != 0;
+    const int a_q = qreal ? (positions ? gi - positions[qrow] : 0) : 0;
+    const size_t o = (size_t)b * Sk + j;
+    const int c = key_valid[o] ? (key_positions ? j - key_positions[o] : 0) : INT_MIN;
+    const unsigned wlim = window > 0 ? (unsigned)window : 0x80000000u;
+    mask[idx] = key_visible(qreal ? gi : -1, a_q, j, c, wlim) ? 1 : 0;
 }
 
 __global__ void debug_tiles_kernel(const TileSummary* __restrict__ qsum, const TileSummary* __restrict__ ksum,
@@ -1048,6 +1081,22 @@ size_t summaries_bytes(int B, int Sq, int Sk)
 size_t values_bytes(int B, int Sk, int Hkv, int D)
 {
     return (size_t)B * Hkv * ceil_div(Sk, BN) * BN * D * sizeof(_Float16);
+}
+
+size_t value_flags_bytes(int B, int Sk, int Hkv) { return round256((size_t)B * Hkv * ceil_div(Sk, BN)); }
+
+size_t fwd_workspace_bytes(int B, int Sq, int Sk, int Hkv, int D)
+{
+    return summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D) + value_flags_bytes(B, Sk, Hkv);
+}
+
+int check_tile_counts(int B, int Sq, int Sk, int Hq, int Hkv)
+{
+    const long long nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
+    if ((long long)B * (nQB + nKT) >= (1LL << 31)) return fail(INKATTN_ERR_SHAPE, "too many tiles");
+    if ((long long)B * Hkv * nKT >= (1LL << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
+    if ((long long)B * Hq * nQB >= (1LL << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
+    return INKATTN_OK;
 }
 
 // Defaults of the optional arguments and the checks shared by every entry point.
@@ -1222,19 +1271,21 @@ __global__ __launch_bounds__(1024) void flex_positions_kernel(const int32_t* __r
 }
 
 // Launches the fp16 value staging for v with element strides (batch row,
-// key, head).
-int launch_stage(const __bf16* v, const uint8_t* key_valid, int B, int Sk, int Hkv, int D, long long v_bs,
-                 long long v_ts, long long v_hs, _Float16* v16, hipStream_t st)
+// key, head) into the workspace (values, then one flag byte per staged tile).
+int launch_stage(const __bf16* v, const uint8_t* key_valid, int B, int Sq, int Sk, int Hkv, int D, long long v_bs,
+                 long long v_ts, long long v_hs, void* workspace, hipStream_t st)
 {
     const size_t tiles = (size_t)B * Hkv * ceil_div(Sk, BN);
     if (tiles == 0) return INKATTN_OK;   // (the kernel reads key Sk - 1: Sk >= 1 from here on)
     if (tiles >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "v too large");
+    _Float16* v16 = (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk));
+    uint8_t* bad = (uint8_t*)v16 + values_bytes(B, Sk, Hkv, D);
     if (D == 128)
         hipLaunchKernelGGL(stage_values_kernel<128>, dim3((unsigned)tiles), dim3(128), 0, st, v, key_valid, Sk, Hkv,
-                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
+                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16, bad);
     else
         hipLaunchKernelGGL(stage_values_kernel<64>, dim3((unsigned)tiles), dim3(64), 0, st, v, key_valid, Sk, Hkv,
-                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16);
+                           ceil_div(Sk, BN), v_bs, v_ts, v_hs, v16, bad);
     return check_launch("stage_values_kernel");
 }
 
@@ -1303,7 +1354,7 @@ extern "C" {
 size_t attn_fwd_workspace_size(int B, int Sq, int Sk, int Hkv, int D)
 {
     if (B <= 0 || Sq < 0 || Sk < 0 || Hkv < 0 || D < 0) return 0;
-    return summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D);
+    return fwd_workspace_bytes(B, Sq, Sk, Hkv, D);
 }
 
 int attn_query_block(void) { return BM; }
@@ -1340,6 +1391,7 @@ int flex_attn_fwd(const void* q, const void* k, const void* v, const float* sink
         return fail(INKATTN_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
     if ((sink_weights && !aligned(sink_weights, 4)) || (lse && !aligned(lse, 4)) || (tokens && !aligned(tokens, 4)))
         return fail(INKATTN_ERR_ALIGN, "sink_weights / lse / tokens misaligned");
+    if (int rc = check_tile_counts(B, Sq, Sk, Hq, Hkv)) return rc;
     if (int rc = check_workspace(workspace, workspace_bytes, flex_attn_workspace_size(B, Sq, Sk, Hkv, D))) return rc;
 
     hipStream_t st = (hipStream_t)stream;
@@ -1348,17 +1400,16 @@ int flex_attn_fwd(const void* q, const void* k, const void* v, const float* sink
     int32_t* pos = blocks ? (int32_t*)(ws + attn_ws) : nullptr;
     uint8_t* ones = (uint8_t*)(ws + attn_ws + round256((size_t)B * Sq * 4));
     const size_t nones = (size_t)B * std::max(Sq, Sk);
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(ones, ones, pos, pos, 0, B, Sq, Sk, &ma)) return rc;
+    // every check has run: from here on only launches
     hipLaunchKernelGGL(flex_positions_kernel, dim3((unsigned)B), dim3(1024), 0, st, tokens, (int)eos_id,
                        (int)fixed_block_size, Sq, pos, ones, nones);
     if (int rc = check_launch("flex_positions_kernel")) return rc;
-
-    MaskArgs ma;
-    if (int rc = resolve_mask_args(ones, ones, pos, pos, 0, B, Sq, Sk, &ma)) return rc;
     if (int rc = launch_summaries(ones, pos, ma.key_valid, ma.key_positions, 0, B, Sq, Sk, workspace, st)) return rc;
     if (Sk > 0) {
         const long long v_hs = (long long)Sk * D;
-        if (int rc = launch_stage((const __bf16*)v, ones, B, Sk, Hkv, D, Hkv * v_hs, D, v_hs,
-                                  (_Float16*)(ws + summaries_bytes(B, Sq, Sk)), st))
+        if (int rc = launch_stage((const __bf16*)v, ones, B, Sq, Sk, Hkv, D, Hkv * v_hs, D, v_hs, workspace, st))
             return rc;
     }
     // scale: applied only without sink weights (the default head_dim^-0.5 otherwise)
@@ -1381,6 +1432,7 @@ const char* attn_status_string(int status)
     case INKATTN_ERR_ALIGN: return "pointer misaligned";
     case INKATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case INKATTN_ERR_LAUNCH: return "HIP launch failed";
+    case INKATTN_ERR_RANGE: return "a value outside the supported range";
     default: return "unknown status";
     }
 }
@@ -1414,11 +1466,10 @@ int attn_stage_values(const void* v, const uint8_t* valid, const uint8_t* key_va
     if ((size_t)B * Sk == 0) return INKATTN_OK;
     if (!v) return fail(INKATTN_ERR_NULL, "v is NULL");
     if (!aligned(v, 16)) return fail(INKATTN_ERR_ALIGN, "v must be 16-byte aligned");
-    if (int rc = check_workspace(workspace, workspace_bytes,
-                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
-        return rc;
-    return launch_stage((const __bf16*)v, ma.key_valid, B, Sk, Hkv, D, (long long)Sk * Hkv * D, (long long)Hkv * D, D,
-                        (_Float16*)((char*)workspace + summaries_bytes(B, Sq, Sk)), (hipStream_t)stream);
+    if (int rc = check_tile_counts(B, Sq, Sk, Hkv, Hkv)) return rc;
+    if (int rc = check_workspace(workspace, workspace_bytes, fwd_workspace_bytes(B, Sq, Sk, Hkv, D))) return rc;
+    return launch_stage((const __bf16*)v, ma.key_valid, B, Sq, Sk, Hkv, D, (long long)Sk * Hkv * D, (long long)Hkv * D,
+                        D, workspace, (hipStream_t)stream);
 }
 
 int attn_fwd_planned(const void* q, const void* k, const void* v,
@@ -1440,9 +1491,8 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
     if ((size_t)B * Sq == 0) return INKATTN_OK;   // nothing to write
     if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
         return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
-    if (int rc = check_workspace(workspace, workspace_bytes,
-                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
-        return rc;
+    if (int rc = check_tile_counts(B, Sq, Sk, Hq, Hkv)) return rc;
+    if (int rc = check_workspace(workspace, workspace_bytes, fwd_workspace_bytes(B, Sq, Sk, Hkv, D))) return rc;
 
     const long long sq_h = (long long)Hq * D, sk_h = (long long)Hkv * D;
     return run_forward(q, k, workspace, profiles, profiles_dtype, sink, valid, ma, positions, (int)window,
@@ -1471,9 +1521,8 @@ int attn_fwd(const void* q, const void* k, const void* v,
     if ((size_t)B * Sq == 0) return INKATTN_OK;
     if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
         return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
-    if (int rc = check_workspace(workspace, workspace_bytes,
-                                 summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D)))
-        return rc;
+    if (int rc = check_tile_counts(B, Sq, Sk, Hq, Hkv)) return rc;
+    if (int rc = check_workspace(workspace, workspace_bytes, fwd_workspace_bytes(B, Sq, Sk, Hkv, D))) return rc;
     if (int rc = attn_plan(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, workspace,
                            workspace_bytes, stream))
         return rc;
@@ -1503,6 +1552,61 @@ int attn_debug_counts(const uint8_t* valid, const uint8_t* key_valid,
                        ma.key_valid, positions, ma.key_positions, (int)window, (int)query_offset, B, Sq, Sk,
                        n_allowed);
     return check_launch("debug_counts_kernel");
+}
+
+int attn_debug_mask(const uint8_t* valid, const uint8_t* key_valid,
+                    const int32_t* positions, const int32_t* key_positions,
+                    int64_t window, int64_t query_offset, int B, int Sq, int Sk,
+                    uint8_t* mask, void* stream)
+{
+    g_last_error[0] = '\0';
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
+        return rc;
+    if (window >= (int64_t(1) << 31) || window < 0) window = 0;
+    const size_t n = (size_t)B * Sq * Sk;
+    if (n == 0) return INKATTN_OK;
+    if (n > (size_t(1) << 32)) return fail(INKATTN_ERR_SHAPE, "mask of %zu entries is above the 2^32 limit", n);
+    if (!mask) return fail(INKATTN_ERR_NULL, "mask is NULL");
+    hipLaunchKernelGGL(debug_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       valid, ma.key_valid, positions, ma.key_positions, (int)window, (int)query_offset, Sq, Sk, n,
+                       mask);
+    return check_launch("debug_mask_kernel");
+}
+
+int attn_check_values(const void* workspace, size_t workspace_bytes, int B, int Sq, int Sk, int Hkv, int D,
+                      void* stream)
+{
+    g_last_error[0] = '\0';
+    if (B < 0 || Sq < 0 || Sk < 0 || Hkv < 1) return fail(INKATTN_ERR_SHAPE, "bad sizes");
+    if (D != 64 && D != 128) return fail(INKATTN_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", D);
+    if (Sq >= (1 << 30) || Sk >= (1 << 30)) return fail(INKATTN_ERR_SHAPE, "Sq / Sk must be below 2^30");
+    const size_t nflags = (size_t)B * Hkv * ceil_div(Sk, BN);
+    if (nflags == 0) return INKATTN_OK;
+    if (int rc = check_workspace((void*)workspace, workspace_bytes, fwd_workspace_bytes(B, Sq, Sk, Hkv, D)))
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const uint8_t* flags = (const uint8_t*)workspace + summaries_bytes(B, Sq, Sk) + values_bytes(B, Sk, Hkv, D);
+    uint8_t* host = (uint8_t*)malloc(nflags);
+    if (!host) return fail(INKATTN_ERR_SHAPE, "no host memory for %zu flags", nflags);
+    hipError_t e = hipMemcpyAsync(host, flags, nflags, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        free(host);
+        return fail(INKATTN_ERR_LAUNCH, "reading the value flags: %s", hipGetErrorString(e));
+    }
+    size_t first = nflags;
+    for (size_t t = 0; t < nflags && first == nflags; ++t)
+        if (host[t]) first = t;
+    free(host);
+    if (first < nflags) {
+        const size_t nKT = (size_t)ceil_div(Sk, BN);
+        return fail(INKATTN_ERR_RANGE,
+                    "v holds a value outside +-65504 (or not finite) at a real key: batch row %zu, K/V head %zu, "
+                    "keys %zu..%zu",
+                    first / ((size_t)Hkv * nKT), (first / nKT) % Hkv, (first % nKT) * BN, (first % nKT) * BN + BN - 1);
+    }
+    return INKATTN_OK;
 }
 
 int attn_debug_tiles(const uint8_t* valid, const uint8_t* key_valid,
