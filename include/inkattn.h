@@ -29,7 +29,8 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer to C-contiguous memory owned by
  *    the caller; the library allocates nothing and keeps no global mutable
- *    state, so calls are reentrant.  Inputs are never written.
+ *    state, so calls are reentrant (the one exception is attn_fwd_noalloc,
+ *    whose per-GPU scratch is shared by its calls).  Inputs are never written.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  A successful return means the work was enqueued.
  *  - Every argument check runs on the host before any launch; on failure
@@ -223,6 +224,33 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
                      int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
                      float* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device
+ * memory: code under stream capture, tight serving loops, harnesses that
+ * forbid allocation.  The same forward (the same kernels, the same results
+ * bit for bit), with no workspace argument: its workspace is a scratch array
+ * of INKATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU
+ * it runs on, from the first call there until the process ends.  The call
+ * allocates nothing; the caller still passes every input and `out` / `lse`.
+ * Sizes whose workspace (attn_fwd_workspace_size) exceeds the scratch are
+ * rejected with INKATTN_ERR_WORKSPACE before any launch.  The scratch of the
+ * current device is used (`stream` must belong to it).  Every call on a GPU
+ * shares that GPU's scratch and leaves its contents behind: calls that
+ * overlap on one GPU (on different streams or from different host threads)
+ * race and must be serialised by the caller; calls in order on one stream are
+ * safe.  (The value flags of attn_check_values stay in the scratch, which no
+ * entry point reads back: a caller that wants that check calls attn_fwd with
+ * a workspace of its own.)
+ */
+#define INKATTN_NOALLOC_SCRATCH_BYTES (72u << 20)
+int attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                     const void* profiles, int profiles_dtype,
+                     const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                     float* out, float* lse, void* stream);
 
 /*
  * attn_debug_counts -- number of allowed keys per query row, n_allowed[B, Sq]

@@ -235,3 +235,15 @@ def test_int64_positions_and_tokens_are_range_checked_before_narrowing():
         binding._narrow_int64(torch.tensor([1 << 31]), "tokens", -(1 << 31), 1 << 31)
     assert binding._narrow_int64(torch.tensor([-(1 << 31), 7]), "tokens", -(1 << 31), 1 << 31).tolist() == [
         -(1 << 31), 7]
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch_before_touching_the_device():
+    lib = binding.load()
+    # B=1, Sq=Sk=40000, Hkv=8, D=128: the fp16 value copy alone is 82 MB, above the 72 MiB scratch
+    rc = lib.attn_fwd_noalloc(P(A), P(A), P(A), P(A), 0, P(A), P(A), None, None, None, 0, 0,
+                              1, 40000, 40000, 8, 8, 128, 1, P(A), P(A), None)
+    assert rc == 5
+    assert "no-allocation scratch" in binding.attn_last_error()
+    assert binding.attn_fwd_workspace_size(1, 40000, 40000, 8, 128) > binding.NOALLOC_SCRATCH_BYTES
+    # the long-context workload (B=1, S=32768, Hkv=8, D=128) fits
+    assert binding.attn_fwd_workspace_size(1, 32768, 32768, 8, 128) <= binding.NOALLOC_SCRATCH_BYTES

@@ -28,7 +28,7 @@ INKATTN_ERR_RANGE = 7
 # Every symbol include/inkattn.h declares.
 EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
            "attn_debug_counts", "attn_debug_mask", "attn_debug_tiles", "attn_check_values",
-           "flex_attn_workspace_size", "flex_attn_fwd",
+           "flex_attn_workspace_size", "flex_attn_fwd", "attn_fwd_noalloc",
            "attn_bwd_workspace_size", "attn_bwd",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
             lib.attn_fwd.restype = I
             lib.attn_fwd.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
                                      I, I, I, I, I, I, I, P, P, P, SZ, P]
+            lib.attn_fwd_noalloc.restype = I
+            lib.attn_fwd_noalloc.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
+                                             I, I, I, I, I, I, I, P, P, P]
             lib.attn_fwd_planned.restype = I
             lib.attn_fwd_planned.argtypes = list(lib.attn_fwd.argtypes)
             lib.attn_plan.restype = I
@@ -178,7 +181,7 @@ def attn_fwd_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
 
 
 def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_positions, window,
-                 query_offset, out, lse, workspace, stream):
+                 query_offset, out, lse, workspace, stream, with_workspace: bool = True):
     dev = q.device
     q = _dev(q, "q", (torch.bfloat16,), None)
     k = _dev(k, "k", (torch.bfloat16,), dev)
@@ -208,14 +211,14 @@ def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_posit
         lse = torch.empty((B, Sq, Hq), dtype=torch.float32, device=dev)
     else:
         lse = _dev(lse, "lse", (torch.float32,), dev)
-    if workspace is None:
+    if workspace is None and with_workspace:
         workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
                                 device=dev)
     pdt = INKATTN_BF16 if profiles.dtype == torch.bfloat16 else INKATTN_F32
+    ws_args = (_ptr(workspace), workspace.numel() * workspace.element_size()) if with_workspace else ()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(profiles), pdt, _ptr(sink), _ptr(valid_u8),
             _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), 0 if window is None else int(window),
-            int(query_offset), B, Sq, Sk, Hq, Hkv, D, E, _ptr(out), _ptr(lse),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+            int(query_offset), B, Sq, Sk, Hq, Hkv, D, E, _ptr(out), _ptr(lse), *ws_args, _stream(stream, dev))
     # keep converted tensors alive until the call is enqueued
     keep = (q, k, v, profiles, sink, valid_u8, kvalid_u8, pos, kpos, workspace)
     return args, out, lse, keep
@@ -238,6 +241,27 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.
     args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
                                         key_positions, window, query_offset, out, lse, workspace, stream)
     _check(load().attn_fwd(*args), "attn_fwd")
+    del keep
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 72 << 20   # INKATTN_NOALLOC_SCRATCH_BYTES (include/inkattn.h)
+
+
+@_on_call_stream
+def attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.Tensor,
+                     sink: torch.Tensor, valid: torch.Tensor, key_valid: Optional[torch.Tensor] = None,
+                     positions: Optional[torch.Tensor] = None, key_positions: Optional[torch.Tensor] = None,
+                     window: Optional[int] = None, query_offset: int = 0,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """:func:`attn_fwd` through the entry point that allocates nothing (its workspace is the
+    library's per-GPU scratch of NOALLOC_SCRATCH_BYTES).  A caller that may not allocate passes
+    ``out``, ``lse`` and int32 positions; calls that overlap on one GPU race (see the header)."""
+    args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
+                                        key_positions, window, query_offset, out, lse, None, stream,
+                                        with_workspace=False)
+    _check(load().attn_fwd_noalloc(*args), "attn_fwd_noalloc")
     del keep
     return out, lse
 

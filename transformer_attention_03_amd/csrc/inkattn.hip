@@ -57,6 +57,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1045,6 +1046,41 @@ __global__ void debug_tiles_kernel(const TileSummary* __restrict__ qsum, const T
 
 }  // namespace
 
+// Workspace of attn_fwd_noalloc: one copy per GPU, at that GPU's own address,
+// held from the first use on the GPU until the process ends.  Host code never
+// passes this name to a kernel or a copy (on the host it only stands for the
+// symbol); it uses the device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[INKATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};   // device address of `scratch`, per device
+
+// Device address of the current device's scratch (looked up once per device,
+// with that device current).
+int scratch_address(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(INKATTN_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(INKATTN_ERR_LAUNCH, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(INKATTN_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return INKATTN_OK;
+}
+
+}  // namespace
+
 namespace inkattn __attribute__((visibility("hidden"))) {
 
 thread_local char g_last_error[512] = "";
@@ -1532,6 +1568,39 @@ int attn_fwd(const void* q, const void* k, const void* v,
     return attn_fwd_planned(q, k, v, profiles, profiles_dtype, sink, valid, key_valid, positions, key_positions,
                             window, query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, lse, workspace, workspace_bytes,
                             stream);
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                     const void* profiles, int profiles_dtype,
+                     const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                     float* out, float* lse, void* stream)
+{
+    g_last_error[0] = '\0';
+    if (int rc = check_fwd_args(q, k, v, profiles, profiles_dtype, sink, B, Sq, Sk, Hq, Hkv, D, E, out, lse))
+        return rc;
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
+        return rc;
+    if ((size_t)B * Sq == 0) return INKATTN_OK;
+    if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
+    if (int rc = check_tile_counts(B, Sq, Sk, Hq, Hkv)) return rc;
+    const size_t need = fwd_workspace_bytes(B, Sq, Sk, Hkv, D);
+    if (need > (size_t)INKATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(INKATTN_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of workspace, above the %zu bytes of the no-allocation scratch "
+                    "(use attn_fwd with a workspace of attn_fwd_workspace_size bytes)",
+                    need, (size_t)INKATTN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (int rc = scratch_address(&ws)) return rc;
+    // every part of the workspace is rewritten by each forward before it is
+    // read (summaries, key start columns, values, flags): nothing to clear
+    return attn_fwd(q, k, v, profiles, profiles_dtype, sink, valid, key_valid, positions, key_positions, window,
+                    query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, lse, ws, (size_t)INKATTN_NOALLOC_SCRATCH_BYTES,
+                    stream);
 }
 
 int attn_debug_counts(const uint8_t* valid, const uint8_t* key_valid,
