@@ -236,20 +236,6 @@ template <> struct TileLayout<64> {
 };
 
 
-enum : int { BIAS_NONE = 0, BIAS_FAST = 1, BIAS_EDGE = 2 };
-
-// Relative-bias class of a 32-key sub-tile starting at key js for the query
-// columns qlo..qhi: no distance below E (no bias), every distance inside
-// [0, E) (one contiguous 4-element run per lane and 4 keys), or mixed.
-__device__ __forceinline__ int bias_class(int qlo, int qhi, int js, int E)
-{
-    if (E <= 0) return BIAS_NONE;   // no relative term
-    const int rmin = qlo - (js + 31), rmax = qhi - js;
-    if (rmin >= E) return BIAS_NONE;
-    if (rmin >= 0 && rmax < E) return BIAS_FAST;
-    return BIAS_EDGE;
-}
-
 template <int D, bool PROF_BF16, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p)
@@ -476,177 +462,113 @@ void attn_fwd_kernel(FwdParams p)
 
     // ---- relative bias.  Element (jj, e) of half s of a tile's S^T
     // accumulator is key j0 + 32 s + 8 jj + 4 hh + (e ^ 3), i.e. distance
-    // R - 8 jj - 4 hh - (e ^ 3) with R = gi - (j0 + 32 s).  All loads go through
-    // a buffer resource over this (batch row, head)'s [Sq, E] block, and reads
-    // outside the block return 0.
+    // R - 32 s - 8 jj - 4 hh - (e ^ 3) with R = gi - j0.  All loads go through
+    // a buffer resource over this (batch row, head)'s [Sq, E] block; the
+    // hardware range-checks each offset register as an unsigned value, so
+    // offsets past the block, or before it (wrapped), read as 0.
     constexpr int PE = PROF_BF16 ? 2 : 4;               // bytes per profile entry
     const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(
         (const char*)p.profiles + ((size_t)b * p.Hq + h) * p.Sq * p.E * PE, (size_t)p.Sq * p.E * PE);
-    // Byte offset of distance gi - 4 hh - 30 in this lane's row, in wrapping
-    // 32-bit arithmetic (it may lie before the row: every entry read below is
-    // at most 30 entries after it).  The buffer hardware range-checks the
-    // offset register as an unsigned value, so every register offset handed to
-    // it is the exact offset of an entry (never a base to be completed by the
-    // constant operand), and offsets before the block wrap out of range.
-    // (derived from the lane id where it is used, not held in registers)
-    auto prow_off_now = [&]() -> unsigned {
-        const unsigned ln = opaque((unsigned)lane);
-        const unsigned ii = (unsigned)i0 + (ln & 31u);
-        return (ii * (unsigned)p.E + ii + (unsigned)p.qoff - 4u * (ln >> 5) - 30u) * PE;
-    };
     constexpr float INV_SCALE = D == 128 ? 11.313708498984761f : 8.0f;   // sqrt(D)
-    constexpr int BIAS_DMA = 16;   // code bit: the tile's strip was copied row by row
 
-    // fp32 profiles: every bias value reaches the accumulators through this
-    // wave's 8 KB LDS strip, filled by DMA (buffer_load ... lds) one tile ahead.
-    // Layouts, by the tile's bias code:
-    //  - BIAS_DMA (both halves fast): 32 rows x 64 distances, copied row by
-    //    row: lane (row r, slot c) of instruction u, r = 4 u + lane / 16,
-    //    fetches 16-byte chunk c ^ (r % 16) of row r's strip (distances
-    //    R_r - 63 .. R_r), which makes the column-wise reads conflict free;
-    //  - otherwise half s uses bytes 4096 s .. + 4095: a fast half (every
-    //    distance in [0, E)) as 4 runs of 4 entries, run jj of lane l at
-    //    1024 jj + 16 l; an edge half entry by entry, entry 4 jj + e of lane l
-    //    at 256 (4 jj + e) + 4 l, zeroed outside [0, E) on reading.
-    // bf16 profiles: every non-empty half is loaded entry by entry as an
-    // edge half; a 2-byte DMA lands zero-extended in the lane's dword, i.e.
-    // as the upper half of the fp32 value.
+    // Every bias value reaches the accumulators through this wave's 8 KB LDS
+    // strip, filled by DMA one tile ahead, in one layout: row r (query
+    // i0 + r) at bytes 256 r holds the distances R_r - 63 .. R_r of the tile
+    // (R_r = its R), 4 bytes per distance, the 16-byte chunk c (distances
+    // R_r - 63 + 4 c .. + 3) at slot c ^ (r % 16), which makes the reads of
+    // the S^T layout conflict free.  Distances below 0 read whatever the
+    // profile row before holds (finite; those keys are masked: they lie after
+    // the query); distances >= E are zeroed on reading (BC_FAR).  Two ways in:
+    //  - BC_ROWS (fp32): 16-byte runs, 4 rows per instruction, 8 instructions;
+    //    only when the tile's lowest offset (row 0, distance R_0 - 63) lies
+    //    inside the block, so that no run straddles its start;
+    //  - BC_ENTRIES (bf16, and fp32 near the block's start): one instruction
+    //    per row, each lane one entry at its exact offset (64 contiguous
+    //    entries per instruction); a bf16 entry lands zero-extended in the
+    //    low half of its dword.
+    enum : int { BC_NONE = 0, BC_ROWS = 1, BC_ENTRIES = 2, BC_FAR = 4 };
     char* bstrip = smem + B_OFF + wave * BSTRIP;
 
-    // loads of a fast half: vo = exact offset of its lowest distance (run jj = 3)
-    auto fetch_fast_half = [&](unsigned vo, int s) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int soff = (24 - 8 * jj) * PE;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bstrip + 4096 * s + 1024 * jj), 16, vo,
-                                                     soff, 0, 0);
-        }
-    };
-    // loads of an edge half (keys js .. js + 31), entry by entry
-    auto fetch_edge_half = [&](int js, int s) {
-        const unsigned vo = prow_off_now() - (unsigned)js * PE;
-        lds_char* const bs = opaque_lds((lds_char*)bstrip);   // (recomputed per tile, not held in registers)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // the exact entry offset, opaque: loads of neighbouring entries
-                // must not merge into one wider load whose first entry may lie
-                // before the block (which would read the whole load as 0)
-                const unsigned off = opaque(vo + (30 - 8 * jj - (e ^ 3)) * PE);
-                if constexpr (PROF_BF16) {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        prsrc, (lds_void*)(bs + 4096 * s + 256 * (4 * jj + e)), 2, off, 0, 0, 0);
-                } else {
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        prsrc, (lds_void*)(bs + 4096 * s + 256 * (4 * jj + e)), 4, off, 0, 0, 0);
-                }
-            }
-        }
-    };
-    // Issues the bias loads of this wave's part of tile d; returns the tile's
-    // code: the classes of its two 32-key halves (bits 0-1, 2-3), plus BIAS_DMA.
+    // Issues the bias loads of this wave's part of tile d; returns its code.
     auto load_bias = [&](const TileDesc& d) -> int {
-        if (d.kt > kt_hi || d.my_cls == TILE_SKIP) return BIAS_NONE | (BIAS_NONE << 2);
+        if (p.E <= 0 || d.kt > kt_hi || d.my_cls == TILE_SKIP) return BC_NONE;
         const int j0n = d.kt * BN;
-        int c0 = bias_class(qlo, qhi, j0n, p.E);
-        int c1 = bias_class(qlo, qhi, j0n + 32, p.E);
-        if constexpr (PROF_BF16) {
-            if (c0 == BIAS_FAST) c0 = BIAS_EDGE;
-            if (c1 == BIAS_FAST) c1 = BIAS_EDGE;
-        }
-        {
-            if (c0 == BIAS_NONE && c1 == BIAS_NONE) return 0;
-            __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // earlier reads of the strip are done
-            if (!PROF_BF16 && c0 == BIAS_FAST && c1 == BIAS_FAST) {
-                // row i0 + r, distance qlo + r - j0n - 63 + 4 c': the strip of row r
-                const unsigned tile_off = (unsigned)((i0 * p.E + qlo - j0n - 63) * 4);
-                // chunk (lane % 16) ^ (r % 16) of row r = 4 u + brow: (r % 16) = 4 (u % 4) | brow
-                const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
-                const unsigned bl = (ln >> 4) * (unsigned)(p.E + 1) * 4u;
-                const unsigned rstep = opaque_s((unsigned)(p.E + 1) * 16u);   // bytes between rows 4 apart, + 16
-                const unsigned xb = 16u * ((ln & 15u) ^ (ln >> 4));
-                lds_char* const bs = opaque_lds((lds_char*)bstrip);
+        if (qlo - (j0n + BN - 1) >= p.E) return BC_NONE;        // every distance >= E
+        const int far = (qhi - j0n >= p.E) ? BC_FAR : 0;
+        const int min_off = i0 * p.E + qlo - j0n - (BN - 1);    // entry of row 0, distance R_0 - 63
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // earlier reads of the strip are done
+        lds_char* const bs = opaque_lds((lds_char*)bstrip);
+        const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
+        if (!PROF_BF16 && min_off >= 0) {
+            // row r = 4 u + lane / 16 takes chunk (lane % 16) ^ (r % 16) = ((lane % 16) ^ (lane / 16)) ^ 4 (u % 4)
+            const unsigned bl = (ln >> 4) * (unsigned)(p.E + 1) * 4u;
+            const unsigned rstep = opaque_s((unsigned)(p.E + 1) * 16u);   // bytes between rows 4 apart, + 16
+            const unsigned xb = 16u * ((ln & 15u) ^ (ln >> 4));
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const unsigned voff = opaque(tile_off + (unsigned)u * rstep + bl +
-                                                 (xb ^ (64u * (unsigned)(u & 3))));
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 1024 * u), 16, voff, 0,
-                                                             0, 0);
-                }
-                return c0 | (c1 << 2) | BIAS_DMA;
+            for (int u = 0; u < 8; ++u) {
+                const unsigned voff = opaque((unsigned)min_off * 4u + (unsigned)u * rstep + bl +
+                                             (xb ^ (64u * (unsigned)(u & 3))));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 1024 * u), 16, voff, 0, 0, 0);
             }
-            const unsigned po = prow_off_now();
-            const unsigned vo0 = opaque(po + (3 - j0n) * PE);
-            const unsigned vo1 = opaque(po + (3 - j0n - 32) * PE);
-            if (c0 == BIAS_FAST) fetch_fast_half(vo0, 0);
-            else if (c0 != BIAS_NONE) fetch_edge_half(j0n, 0);
-            if (c1 == BIAS_FAST) fetch_fast_half(vo1, 1);
-            else if (c1 != BIAS_NONE) fetch_edge_half(j0n + 32, 1);
-            return c0 | (c1 << 2);
+            return BC_ROWS | far;
         }
+        // row r: lane L fetches distance R_r - 63 + (L ^ 4 (r % 16)), the entry its slot holds
+        const unsigned rstep = opaque_s((unsigned)(p.E + 1));
+#pragma unroll
+        for (int r = 0; r < BM; ++r) {
+            const unsigned off = opaque(((unsigned)min_off + (unsigned)r * rstep + (ln ^ (4u * (unsigned)(r & 15)))) *
+                                        (unsigned)PE);
+            if constexpr (PROF_BF16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 256 * r), 2, off, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 256 * r), 4, off, 0, 0, 0);
+        }
+        return BC_ENTRIES | far;
     };
     // Vector-memory instructions load_bias issued for a code.
-    auto bias_loads = [&](int code) -> int {
-        if (code & BIAS_DMA) return 8;
-        auto per_half = [](int c) { return c == BIAS_NONE ? 0 : (c == BIAS_FAST && !PROF_BF16) ? 4 : 16; };
-        return per_half(code & 3) + per_half((code >> 2) & 3);
-    };
-    // a + the entry (jj, e) of the half starting at key js times sqrt(D), or a
-    // outside [0, E).
-    // (rb = gi - 4 hh - js, opaque: the distances are recomputed per tile
-    // rather than held in registers)
-    auto add_edge = [&](unsigned rb, int jj, int e, float raw, float a) -> float {
-        const unsigned r = rb - (unsigned)(8 * jj + (e ^ 3));
-        return __builtin_fmaf(r < (unsigned)p.E ? raw : 0.0f, INV_SCALE, a);
-    };
-    // Adds tile j0t's bias (code as load_bias returned it) to the accumulators.
-    // Its loads were issued before this wave's DMA of the next K / V tile,
-    // which may stay outstanding (N_KV_DMA instructions).
+    auto bias_loads = [&](int code) -> int { return (code & BC_ROWS) ? 8 : (code & BC_ENTRIES) ? BM : 0; };
+    // Adds tile j0t's bias (code as load_bias returned it) times sqrt(D) to the
+    // accumulators.  Its loads were issued before this wave's DMA of the next
+    // K / V tile, which may stay outstanding (N_KV_DMA instructions).
     auto bias_add_tile = [&](int code, int j0t, f32x16* a) {
-        if ((code & 15) == 0) return;
+        if (code == BC_NONE) return;
         wait_vm_keep(N_KV_DMA);
-        if (!PROF_BF16 && (code & BIAS_DMA)) {
-            // chunk k = 15 - 8 s - 2 jj - hh (distances R - 32 s - 8 jj - 4 hh - 3 ..) of
-            // row qi sits at chunk slot k ^ (qi % 16) = (15 ^ hh ^ (qi % 16)) ^ (8 s + 2 jj)
-            const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
-            const unsigned rb = (ln & 31u) * 256u + 16u * (15u ^ (ln >> 5) ^ (ln & 15u));
+        // chunk k = 15 - 8 s - 2 jj - hh of row qi (distances R - 32 s - 8 jj - 4 hh - 3 ..)
+        // sits at slot k ^ (qi % 16) = (15 ^ hh ^ (qi % 16)) ^ (8 s + 2 jj)
+        const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
+        const unsigned rb = (ln & 31u) * 256u + 16u * (15u ^ (ln >> 5) ^ (ln & 15u));
+        f32x4 w[2][4];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                w[s2][jj] = *(const f32x4*)(bstrip + (rb ^ (unsigned)(16 * (8 * s2 + 2 * jj))));
+                if constexpr (PROF_BF16) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)   // the entry is the upper half of the fp32 value
+                        w[s2][jj][e] = __uint_as_float(__float_as_uint(w[s2][jj][e]) << 16);
+                }
+            }
+        if (code & BC_FAR) {
+            // distances outside [0, E) take no bias
+            const unsigned rd = opaque((unsigned)(gi - 4 * hh - j0t));
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 w = *(const f32x4*)(bstrip + (rb ^ (unsigned)(16 * (8 * s2 + 2 * jj))));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
-                }
-            return;
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int c = (code >> (2 * s2)) & 3;
-            if (!PROF_BF16 && c == BIAS_FAST) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 w = *(const f32x4*)(bstrip + 4096 * s2 + 1024 * jj + 16 * opaque((unsigned)lane));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
-                }
-            } else if (c != BIAS_NONE) {
-                const unsigned rb = opaque((unsigned)(gi - 4 * hh - j0t - 32 * s2));
-                const char* ep = bstrip + 4096 * s2 + 4 * opaque((unsigned)lane);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const unsigned u = *(const unsigned*)(ep + 256 * (4 * jj + e));
-                        // bf16: the entry is the upper half of the fp32 value
-                        const float raw = __uint_as_float(PROF_BF16 ? u << 16 : u);
-                        a[s2][4 * jj + e] = add_edge(rb, jj, e, raw, a[s2][4 * jj + e]);
+                        const unsigned r = rd - (unsigned)(32 * s2 + 8 * jj + (e ^ 3));
+                        w[s2][jj][e] = r < (unsigned)p.E ? w[s2][jj][e] : 0.0f;
                     }
-            }
         }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a[s2][4 * jj + e] = __builtin_fmaf(w[s2][jj][e], INV_SCALE, a[s2][4 * jj + e]);
     };
 
     // Software pipeline, per 64-key tile t: the DMA of the next live tile is
