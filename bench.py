@@ -63,12 +63,12 @@ def allowed_counts(x) -> np.ndarray:
     return np.where(valid > 0, n, 0)
 
 
-def used_profile_entries(x) -> int:
+def used_profile_entries(x, E=None) -> int:
     """Profile elements the method reads: allowed pairs with distance below E (per head)."""
     valid = x["valid"].numpy().astype(np.int64)
     pos = x["positions"].numpy().astype(np.int64)
     B, S = valid.shape
-    E = x["profiles"].shape[-1]
+    E = x["profiles"].shape[-1] if E is None else E
     W = x["window"] if x["window"] else S
     cols = np.arange(S)
     lo = np.maximum(np.maximum(cols - pos, cols - W + 1), cols - E + 1)
@@ -203,6 +203,8 @@ def main():
 
     if args.workload in W.FLEX_WORKLOADS:
         return bench_flex(args)
+    if args.workload in W.RELPROJ_WORKLOADS:
+        return bench_relproj(args)
     if args.workload not in W.WORKLOADS:
         sys.exit(f"unknown workload {args.workload!r}; choose from {sorted(W.WORKLOADS) + sorted(W.FLEX_WORKLOADS)}")
     w = W.WORKLOADS[args.workload]
@@ -518,6 +520,95 @@ def bench_flex(args):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = flex_cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def relproj_algorithmic_work(y):
+    """Attention flops as for the profile workloads (4 D per unmasked pair); bytes with the
+    relative features (d_rel bf16 per real row and head) and the table in place of the profile
+    entries.  The producer's own flops (2 d_rel per profile entry used) are reported apart."""
+    w = y["workload"]
+    cnt = allowed_counts(y)
+    pairs = int(cnt.sum()) * w.Hq
+    flops = 4.0 * w.D * pairs
+    valid_rows = int(y["valid"].sum())
+    used = used_profile_entries(y, E=y["E"])
+    nbytes = (valid_rows * w.Hq * w.D * 2 + valid_rows * w.Hkv * w.D * 2 * 2
+              + valid_rows * w.Hq * y["d_rel"] * 2 + y["table"].numel() * 2
+              + valid_rows * w.Hq * 4 + w.B * w.S * w.Hq * (w.D + 1) * 4 + w.B * w.S * (1 + 4))
+    return cnt, pairs, flops, nbytes, 2.0 * y["d_rel"] * used * w.Hq
+
+
+def bench_relproj(args):
+    """The forward with its profile rows formed in the kernel (attn_fwd_relproj): one step = one
+    call (pre-pass, value copy, attention kernel forming the rows from relative features)."""
+    import torch
+    from transformer_attention_03_amd import binding
+    from transformer_attention_03_amd import workloads as W
+
+    y = W.generate_relproj(args.workload)
+    w = y["workload"]
+    cnt, pairs, flops, nbytes, prod_flops = relproj_algorithmic_work(y)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = {k: y[k].to(dev) for k in ("q", "k", "v", "rfeat", "table", "sink", "valid", "positions")}
+    out = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.S, w.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, binding.attn_fwd_workspace_size(w.B, w.S, w.S, w.Hkv, w.D)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.attn_fwd_relproj(d["q"], d["k"], d["v"], d["rfeat"], d["table"], d["sink"], d["valid"],
+                                 positions=d["positions"], window=w.window, out=out, lse=lse, workspace=ws,
+                                 stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    if not torch.isfinite(out).all():
+        sys.exit("non-finite output")
+    gbs = nbytes / (call_ms * 1e-3) / 1e9
+    tf = flops / (call_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fwd attention TFLOP/s (unmasked pairs) + % MFMA peak, 1 GPU; tokens/s",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} E={w.E} "
+                               f"window={w.window} profile rows formed in-kernel from d_rel={y['d_rel']} "
+                               f"relative features and a table of {y['table'].shape[0]} slice(s)",
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
+                   "qk_mfma": "bf16", "pv_mfma": "fp16", "profile_mfma": "bf16", "accumulate": "fp32"},
+        "tokens_per_s": int(y["valid"].sum()) / (ms_step * 1e-3),
+        "unmasked_pairs": pairs,
+        "producer_tflops": prod_flops / (call_ms * 1e-3) / 1e12,
+        "hbm_gbs_algorithmic": gbs,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_fwd_relproj call (pre-pass, value copy, attn_fwd_kernel forming profile rows)",
+                     "kernel_ms": call_ms, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_frac_with_producer": (flops + prod_flops) / (call_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS},
+    }
     print(json.dumps(line), flush=True)
 
 

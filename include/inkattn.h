@@ -226,6 +226,38 @@ int attn_fwd_planned(const void* q, const void* k, const void* v,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_relproj -- attn_fwd with the profile rows formed in the kernel
+ * from relative features instead of read from a profiles tensor, so that no
+ * [B, Hq, Sq, E] tensor exists.  The page
+ * "nemo_automodel.components.models.inkling2.attention" (v0.4, class
+ * Inkling2Attention) names the pieces -- the fused projection qkvr that also
+ * yields relative features, their width d_rel, relative_table and
+ * rel_extent -- and the page "nemo_automodel.components.models.inkling2.
+ * flex_attention" (forward parameter profiles) calls the profiles relative
+ * logits of shape [batch, heads, sequence, relative_extent]; neither prints a
+ * formula.  The reading built here:
+ *
+ *   profiles[b,h,i,r] = sum_c rfeat[b,i,h,c] * table[t,r,c]   (0 <= r < E)
+ *
+ * with t = h for a table of one slice per head (table_heads == Hq) and t = 0
+ * for a shared one (table_heads == 1); bf16 products accumulated in fp32 and
+ * used unrounded (the fp32 boundary).  Everything else as attn_fwd.
+ *
+ *   rfeat   [B, Sq, Hq, d_rel] bf16, 16-byte aligned
+ *   table   [table_heads, E, d_rel] bf16, 16-byte aligned
+ *   d_rel   16 or 32 (INKATTN_ERR_UNSUPPORTED otherwise)
+ *   workspace as for attn_fwd (attn_fwd_workspace_size bytes)
+ */
+int attn_fwd_relproj(const void* q, const void* k, const void* v,
+                     const void* rfeat, const void* table, int table_heads, int d_rel,
+                     const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                     float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_fwd_noalloc -- attn_fwd for callers that cannot allocate device
  * memory: code under stream capture, tight serving loops, harnesses that
  * forbid allocation.  The same forward (the same kernels, the same results

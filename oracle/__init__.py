@@ -68,6 +68,9 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
         P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+    lib.attn_oracle_relproj_profiles.restype = ctypes.c_int
+    lib.attn_oracle_relproj_profiles.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, P]
     lib.attn_oracle_max_threads.restype = ctypes.c_int
     lib.attn_oracle_mask.restype = ctypes.c_int
     lib.attn_oracle_mask.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int64,
@@ -169,10 +172,14 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
     E = int(profiles.shape[-1])
     if profiles_bf16 is None:
         profiles_bf16 = isinstance(profiles, torch.Tensor) and profiles.dtype == torch.bfloat16
+    # fp64 profiles (relproj_profiles) are read as they are
+    prof64 = (isinstance(profiles, np.ndarray) and profiles.dtype == np.float64) or \
+        (isinstance(profiles, torch.Tensor) and profiles.dtype == torch.float64)
     qn = _as_np(q, np.uint16)
     kn = _as_np(k, np.uint16)
     vn = _as_np(v, np.uint16)
-    pn = _as_np(profiles, np.uint16 if profiles_bf16 else np.float32)
+    pn = _as_np(profiles, np.float64 if prof64 else np.uint16 if profiles_bf16 else np.float32)
+    pdt = 2 if prof64 else int(bool(profiles_bf16))
     sn = _as_np(sink, np.float32)
     valid_n, kvalid_n, pos_n, kpos_n = _mask_inputs(valid, key_valid, positions, key_positions,
                                                     query_offset, B, Sq, Sk)
@@ -194,7 +201,7 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
     cnt = np.empty((n,), dtype=np.int32)
     w = 0 if window is None else int(window)
     rc = _load().attn_oracle_fwd(
-        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), int(bool(profiles_bf16)), _ptr(sn),
+        _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), pdt, _ptr(sn),
         _ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n), w, int(query_offset),
         B, Sq, Sk, Hq, Hkv, D, E,
         None if rows_n is None else _ptr(rows_n), n, _ptr(out), _ptr(lse), _ptr(cnt),
@@ -284,6 +291,24 @@ def flex_fwd(q, k, v, sink_weights=None, tokens=None, eos_id: int = 0, fixed_blo
         return (out.reshape(B, Sq, Hq, D).transpose(0, 2, 1, 3).copy(), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy(),
                 cnt.reshape(B, Sq))
     return out, lse, cnt
+
+
+def relproj_profiles(rfeat, table, E: Optional[int] = None):
+    """Relative logits from relative features, fp64 ``[B, Hq, Sq, E]`` (reading stated in
+    ``attn_oracle.c``): ``profiles[b,h,i,r] = sum_c rfeat[b,i,h,c] * table[t,r,c]``.
+
+    ``rfeat [B,Sq,Hq,d_rel]`` bf16; ``table [T,E,d_rel]`` bf16 with T = 1 (shared) or Hq."""
+    B, Sq, Hq, d_rel = (int(x) for x in rfeat.shape)
+    T, Et, dt = (int(x) for x in table.shape)
+    if dt != d_rel or T not in (1, Hq):
+        raise ValueError(f"table {tuple(table.shape)} does not match rfeat {tuple(rfeat.shape)}")
+    E = Et if E is None else int(E)
+    rn = _as_np(rfeat, np.uint16)
+    tn = _as_np(table, np.uint16)
+    out = np.empty((B, Hq, Sq, E), dtype=np.float64)
+    if _load().attn_oracle_relproj_profiles(_ptr(rn), _ptr(tn), T, B, Sq, Hq, d_rel, E, _ptr(out)) != 0:
+        raise RuntimeError("attn_oracle_relproj_profiles failed")
+    return out
 
 
 def timed_fwd(inputs: dict, rows, n_threads: int = 0):

@@ -64,10 +64,13 @@ static double bf16_to_double(uint16_t bits)
     return (double)f;
 }
 
-static double profile_at(const void* profiles, int profiles_is_bf16, size_t idx)
+/* profiles_dtype: 0 fp32, 1 bf16, 2 fp64 (profiles formed by attn_oracle_relproj_profiles) */
+static double profile_at(const void* profiles, int profiles_dtype, size_t idx)
 {
-    if (profiles_is_bf16)
+    if (profiles_dtype == 1)
         return bf16_to_double(((const uint16_t*)profiles)[idx]);
+    if (profiles_dtype == 2)
+        return ((const double*)profiles)[idx];
     return (double)((const float*)profiles)[idx];
 }
 
@@ -96,7 +99,7 @@ static int allowed(const uint8_t* valid, const uint8_t* key_valid,
  * when rows == NULL (then n_rows must be B*Sq).  Outputs are compact over the
  * listed rows: out[n_rows, Hq, D], lse[n_rows, Hq], n_allowed[n_rows].
  *
- * q, k, v: bf16 bit patterns.  profiles: fp32 or bf16 (profiles_is_bf16).
+ * q, k, v: bf16 bit patterns.  profiles: fp32, bf16 or fp64 (profiles_is_bf16 = 0, 1, 2).
  * Every pointer is a host pointer; nothing is allocated beyond one logit buffer
  * of Sk doubles per thread.  Returns 0, or -1 on bad arguments / no memory.
  */
@@ -432,6 +435,47 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             }
         }
     free(z); free(o); free(ok);
+    return 0;
+}
+
+/*
+ * Relative logits from relative features (reading of the page
+ * "nemo_automodel.components.models.inkling2.attention", v0.4: class
+ * Inkling2Attention, attributes qkvr (the fused projection that also yields
+ * relative features), d_rel (their width), relative_table and rel_extent;
+ * and of the page "nemo_automodel.components.models.inkling2.flex_attention",
+ * forward parameter profiles: relative logits of shape [batch, heads,
+ * sequence, relative_extent] that keep the projection's rounding boundary).
+ * The pages give no formula; the reading taken:
+ *
+ *   profiles[b,h,i,r] = sum_c rfeat[b,i,h,c] * table[t,r,c],  0 <= r < E,
+ *
+ * rfeat [B,Sq,Hq,d_rel] and table [T,E,d_rel] bf16 bit patterns, t = h when the
+ * table has one slice per head (T = Hq), t = 0 when it is shared (T = 1).
+ * Every product of two bf16 values is exact in double; the d_rel products
+ * are summed in plain sequential order in double and the result is written
+ * unrounded: profiles [B,Hq,Sq,E] fp64.  Returns 0, or -1 on bad arguments.
+ */
+int attn_oracle_relproj_profiles(const uint16_t* rfeat, const uint16_t* table, int table_heads,
+                                 int B, int Sq, int Hq, int d_rel, int E, double* profiles)
+{
+    if (!rfeat || !table || !profiles || B < 0 || Sq < 0 || Hq <= 0 || d_rel <= 0 || E <= 0) return -1;
+    if (table_heads != 1 && table_heads != Hq) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t bhi = 0; bhi < (int64_t)B * Hq * Sq; ++bhi) {
+        int i = (int)(bhi % Sq);
+        int h = (int)((bhi / Sq) % Hq);
+        int b = (int)(bhi / ((int64_t)Sq * Hq));
+        const uint16_t* f = rfeat + (((size_t)b * Sq + i) * Hq + h) * (size_t)d_rel;
+        const uint16_t* t = table + (size_t)(table_heads == 1 ? 0 : h) * E * (size_t)d_rel;
+        double* out = profiles + (size_t)bhi * E;
+        for (int r = 0; r < E; ++r) {
+            double sum = 0.0;
+            for (int c = 0; c < d_rel; ++c)
+                sum += bf16_to_double(f[c]) * bf16_to_double(t[(size_t)r * d_rel + c]);
+            out[r] = sum;
+        }
+    }
     return 0;
 }
 

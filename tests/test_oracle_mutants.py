@@ -18,6 +18,7 @@ import pytest
 import oracle
 from tests import test_oracle_mask_pins as MP
 from tests import test_oracle_pins as OP
+from tests import test_relproj_oracle_pins as RP
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
@@ -69,6 +70,16 @@ MUTANTS = {
     "bias added beyond the extent as the last entry": (
         "int attn_oracle_fwd(", "if (r >= 0 && r < E)", "if (r >= 0 && (r = r < E ? r : E - 1) >= 0)",
         [functools.partial(OP.test_bruteforce_agrees, OP.CASES[0])]),
+    "relative table read transposed": (
+        "int attn_oracle_relproj_profiles(", "t[(size_t)r * d_rel + c]", "t[(size_t)c * E + r]",
+        [RP.test_one_hot_table_reproduces_features]),
+    "per-head table slice ignored": (
+        "int attn_oracle_relproj_profiles(", "(table_heads == 1 ? 0 : h)", "(table_heads == 1 ? 0 : 0)",
+        [RP.test_per_head_table_scales_by_head]),
+    "features of head 0 for every head": (
+        "int attn_oracle_relproj_profiles(", "(((size_t)b * Sq + i) * Hq + h) * (size_t)d_rel",
+        "(((size_t)b * Sq + i) * Hq + 0) * (size_t)d_rel",
+        [RP.test_one_hot_table_reproduces_features]),
 }
 
 

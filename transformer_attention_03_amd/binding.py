@@ -28,7 +28,7 @@ INKATTN_ERR_RANGE = 7
 # Every symbol include/inkattn.h declares.
 EXPORTS = ("attn_fwd_workspace_size", "attn_fwd", "attn_plan", "attn_stage_values", "attn_fwd_planned",
            "attn_debug_counts", "attn_debug_mask", "attn_debug_tiles", "attn_check_values",
-           "flex_attn_workspace_size", "flex_attn_fwd", "attn_fwd_noalloc",
+           "flex_attn_workspace_size", "flex_attn_fwd", "attn_fwd_noalloc", "attn_fwd_relproj",
            "attn_bwd_workspace_size", "attn_bwd",
            "attn_status_string", "attn_last_error", "attn_query_block", "attn_key_tile")
 
@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
             lib.attn_fwd.restype = I
             lib.attn_fwd.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
                                      I, I, I, I, I, I, I, P, P, P, SZ, P]
+            lib.attn_fwd_relproj.restype = I
+            lib.attn_fwd_relproj.argtypes = [P, P, P, P, P, I, I, P, P, P, P, P, I64, I64,
+                                             I, I, I, I, I, I, I, P, P, P, SZ, P]
             lib.attn_fwd_noalloc.restype = I
             lib.attn_fwd_noalloc.argtypes = [P, P, P, P, I, P, P, P, P, P, I64, I64,
                                              I, I, I, I, I, I, I, P, P, P]
@@ -181,22 +184,27 @@ def attn_fwd_workspace_size(B: int, Sq: int, Sk: int, Hkv: int, D: int) -> int:
 
 
 def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_positions, window,
-                 query_offset, out, lse, workspace, stream, with_workspace: bool = True):
+                 query_offset, out, lse, workspace, stream, with_workspace: bool = True,
+                 extent: Optional[int] = None):
+    """Pointer arguments of the forward entry points; ``profiles`` may be None when ``extent``
+    gives E (the in-kernel profile rows of attn_fwd_relproj)."""
     dev = q.device
     q = _dev(q, "q", (torch.bfloat16,), None)
     k = _dev(k, "k", (torch.bfloat16,), dev)
     v = _dev(v, "v", (torch.bfloat16,), dev)
+    if profiles is None and extent is None:
+        raise ValueError("profiles is required")
     profiles = _dev(profiles, "profiles", (torch.float32, torch.bfloat16), dev)
     sink = _dev(sink, "sink", (torch.float32,), dev)
     valid_u8 = _mask_tensor(valid, "valid", dev)
     kvalid_u8 = _mask_tensor(key_valid, "key_valid", dev)
     pos = _pos_tensor(positions, "positions", dev)
     kpos = _pos_tensor(key_positions, "key_positions", dev)
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or profiles.dim() != 4:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or (profiles is not None and profiles.dim() != 4):
         raise ValueError("q, k, v and profiles must be 4-d")
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
-    E = profiles.shape[3]
+    E = profiles.shape[3] if profiles is not None else int(extent)
     expect = {"k": (k, (B, Sk, Hkv, D)), "v": (v, (B, Sk, Hkv, D)), "profiles": (profiles, (B, Hq, Sq, E)),
               "sink": (sink, (B, Sq, Hq)), "valid": (valid_u8, (B, Sq)), "key_valid": (kvalid_u8, (B, Sk)),
               "positions": (pos, (B, Sq)), "key_positions": (kpos, (B, Sk))}
@@ -214,7 +222,7 @@ def _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions, key_posit
     if workspace is None and with_workspace:
         workspace = torch.empty(max(attn_fwd_workspace_size(B, Sq, Sk, Hkv, D), 16), dtype=torch.uint8,
                                 device=dev)
-    pdt = INKATTN_BF16 if profiles.dtype == torch.bfloat16 else INKATTN_F32
+    pdt = INKATTN_BF16 if profiles is not None and profiles.dtype == torch.bfloat16 else INKATTN_F32
     ws_args = (_ptr(workspace), workspace.numel() * workspace.element_size()) if with_workspace else ()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(profiles), pdt, _ptr(sink), _ptr(valid_u8),
             _ptr(kvalid_u8), _ptr(pos), _ptr(kpos), 0 if window is None else int(window),
@@ -241,6 +249,37 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, profiles: torch.
     args, out, lse, keep = _marshal_fwd(q, k, v, profiles, sink, valid, key_valid, positions,
                                         key_positions, window, query_offset, out, lse, workspace, stream)
     _check(load().attn_fwd(*args), "attn_fwd")
+    del keep
+    return out, lse
+
+
+@_on_call_stream
+def attn_fwd_relproj(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rfeat: torch.Tensor,
+                     table: torch.Tensor, sink: torch.Tensor, valid: torch.Tensor,
+                     key_valid: Optional[torch.Tensor] = None, positions: Optional[torch.Tensor] = None,
+                     key_positions: Optional[torch.Tensor] = None, window: Optional[int] = None,
+                     query_offset: int = 0, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward with the profile rows formed in the kernel from relative features:
+    ``profiles[b,h,i,r] = sum_c rfeat[b,i,h,c] * table[t,r,c]`` (t = h, or 0 for a shared table).
+
+    rfeat [B,Sq,Hq,d_rel] bf16 (d_rel 16 or 32); table [T,E,d_rel] bf16 with T = 1 or Hq; other
+    arguments as :func:`attn_fwd`.  Returns ``(out, lse)``."""
+    dev = q.device
+    rfeat = _dev(rfeat, "rfeat", (torch.bfloat16,), dev)
+    table = _dev(table, "table", (torch.bfloat16,), dev)
+    if rfeat.dim() != 4 or table.dim() != 3:
+        raise ValueError("rfeat must be 4-d and table 3-d")
+    T, E, d_rel = table.shape
+    B, Sq, Hq, _ = q.shape
+    if tuple(rfeat.shape) != (B, Sq, Hq, d_rel):
+        raise ValueError(f"rfeat: shape {tuple(rfeat.shape)} != {(B, Sq, Hq, d_rel)}")
+    args, out, lse, keep = _marshal_fwd(q, k, v, None, sink, valid, key_valid, positions, key_positions, window,
+                                        query_offset, out, lse, workspace, stream, extent=E)
+    qp, kp, vp, _profiles, _pdt, *rest = args
+    _check(load().attn_fwd_relproj(qp, kp, vp, _ptr(rfeat), _ptr(table), int(T), int(d_rel), *rest),
+           "attn_fwd_relproj")
     del keep
     return out, lse
 

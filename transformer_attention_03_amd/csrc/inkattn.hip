@@ -146,6 +146,10 @@ struct FwdParams {
     const TileSummary* qsum;       // [B, nQB]
     const TileSummary* ksum;       // [B, nKT]
     const int* kanchor;            // [B, Sk] key start column j - key_positions[j], INT_MIN if not real
+    const __bf16* rfeat;           // relative features [.., d_rel] (profiles formed in-kernel), or NULL
+    const __bf16* table;           // relative table rows [E, d_rel] of this launch's heads
+    long long r_bs, r_ts, r_hs;    // element strides (batch row, token, head) of rfeat
+    long long t_hs;                // elements between the table slices of two heads (0: one shared slice)
     void* out;                     // fp32, or bf16 when out_bf16
     float* lse;                    // may be NULL (not written)
     // element strides (batch row, token, head) of q, k, out, lse and sink
@@ -236,7 +240,10 @@ template <> struct TileLayout<64> {
 };
 
 
-template <int D, bool PROF_BF16, int NW>
+// REL > 0: the profile rows are not read but formed in-kernel from REL
+// relative features per (token, head) and the relative table (see the bias
+// section); REL == 0: the profiles tensor is read.
+template <int D, bool PROF_BF16, int NW, int REL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdParams p)
 {
@@ -255,8 +262,12 @@ void attn_fwd_kernel(FwdParams p)
     // product of a tile runs during the next tile, while the tile after that
     // is being fetched)
     constexpr int K_OFF = 0, V_OFF = 2 * KBYTES, CA_OFF = 2 * KBYTES + 3 * VBYTES;
-    // fp32 bias strips staged by DMA: per wave 32 rows x 64 distances (8 KB)
-    constexpr int BSTRIP = BM * BN * 4;
+    // fp32 bias strips: per wave 32 rows x 64 distances (8 KB), staged by
+    // DMA; formed in-kernel (REL > 0) they take rows of 272 bytes (64
+    // distances + 16 bytes of padding, which spreads the rows over the banks)
+    static_assert(REL == 0 || REL == 16 || REL == 32, "relative feature widths 16 and 32 are built");
+    constexpr int SROW = REL ? 272 : BN * 4;
+    constexpr int BSTRIP = BM * SROW;
     constexpr int B_OFF = CA_OFF + 2 * BN * 4;
     // tile schedule: one entry per live key tile of a round of NSCHED tiles,
     // plus a count per wave
@@ -309,6 +320,17 @@ void attn_fwd_kernel(FwdParams p)
         const __bf16* qp = p.q + b * p.q_bs + (long long)i * p.q_ts + h * p.q_hs + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) qreg[kk] = qin ? *(const bf16x8*)(qp + 16 * kk) : bf16x8{};
+    }
+    // relative features (REL > 0), the B operand of the profile product:
+    // lane holds rfeat[i, h, 16*kk + 8*hh + 0..7]
+    constexpr int NRK = REL ? REL / 16 : 1;
+    bf16x8 rreg[NRK];
+#pragma unroll
+    for (int kk = 0; kk < NRK; ++kk) rreg[kk] = bf16x8{};
+    if constexpr (REL > 0) {
+        const __bf16* rp = p.rfeat + b * p.r_bs + (long long)i * p.r_ts + h * p.r_hs + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < NRK; ++kk) rreg[kk] = qin ? *(const bf16x8*)(rp + 16 * kk) : bf16x8{};
     }
 
     // Online-softmax state (log2 units).  The sink's weight e^{s - m} counts
@@ -571,6 +593,83 @@ void attn_fwd_kernel(FwdParams p)
                     a[s2][4 * jj + e] = __builtin_fmaf(w[s2][jj][e], INV_SCALE, a[s2][4 * jj + e]);
     };
 
+    // ---- profile rows formed in-kernel (REL > 0).  profiles[b, h, i, r] =
+    // sum_c rfeat[b, i, h, c] * table[r, c] (the table slice of head h).  For
+    // a tile with keys j0 .. j0 + 63 the wave needs distances rho0 .. rho0 + 94,
+    // rho0 = qlo - j0 - 63: P[rho', n] = table[rho0 + rho'] . rfeat[i0 + n] is
+    // three 32 x 32 MFMA blocks (table rows on M, queries on N), and row n of
+    // the strip holds P[n .. n + 63, n] (distance rho0 + n + e at entry e).
+    // Table rows outside [0, E) read as 0 (range check), so distances outside
+    // [0, E) take bias 0 with no further test.
+    const __amdgpu_buffer_rsrc_t trsrc = uniform_rsrc(p.table + (REL ? h * p.t_hs : 0),
+                                                      REL ? (size_t)p.E * REL * 2 : 0);
+    typedef int i32x4_t __attribute__((ext_vector_type(4)));
+    // Does this wave take bias on tile d (some distance below E)?
+    auto rel_needed = [&](const TileDesc& d) -> bool {
+        return REL > 0 && p.E > 0 && d.kt >= 0 && d.kt <= kt_hi && d.my_cls != TILE_SKIP &&
+               qlo - (d.kt * BN + BN - 1) < p.E;
+    };
+    // A operands: lane (row m = lane % 32, half hh) of block s, k-step kk holds
+    // table[rho0 + 32 s + m, 16 kk + 8 hh + 0..7]
+    auto load_table = [&](int j0t, bf16x8 (&ta)[3][NRK]) {
+        const unsigned ln = opaque((unsigned)lane);
+        const unsigned row = (unsigned)(qlo - j0t - (BN - 1)) + (ln & 31u);
+        const unsigned base = (row * (unsigned)REL + 8u * (ln >> 5)) * 2u;
+#pragma unroll
+        for (int s3 = 0; s3 < 3; ++s3)
+#pragma unroll
+            for (int kk = 0; kk < NRK; ++kk) {
+                // (the whole offset travels in the range-checked register)
+                const unsigned off = opaque(base + (unsigned)(32 * s3 * REL + 16 * kk) * 2u);
+                const i32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(trsrc, (int)off, 0, 0);
+                ta[s3][kk] = __builtin_bit_cast(bf16x8, x);
+            }
+    };
+    // P of the tile into this wave's strip (row n at SROW n; no swizzle).
+    // Lane (n, hh) holds P[32 s + 8 jj + 4 hh + e, n] of block s.  Block 1
+    // (rows 32 .. 63) always lies in the band n .. n + 63; of blocks 0 and 2,
+    // exactly one value of each pair (x, x + 64) does: x >= n takes block 0
+    // (entry x - n), else block 2 (entry x + 64 - n).
+    auto form_strip = [&](const bf16x8 (&ta)[3][NRK]) {
+        f32x16 pc[3];
+#pragma unroll
+        for (int s3 = 0; s3 < 3; ++s3) {
+            pc[s3] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NRK; ++kk)
+                pc[s3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[s3][kk], rreg[kk], pc[s3], 0, 0, 0);
+        }
+        const unsigned ln = opaque((unsigned)lane);
+        const unsigned n = ln & 31u, h4 = 4u * (ln >> 5);
+        float* const row = (float*)(bstrip + (SROW - 4) * n + 4 * h4);   // entry x - n of row n at + 4 x
+        const int nn = (int)n - (int)h4;                                  // x >= n  <=>  8 jj + e >= nn
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int xl = 8 * jj + e;                                // x = xl + 4 hh
+                row[32 + xl] = pc[1][4 * jj + e];
+                const bool lo = xl >= nn;
+                const float v = lo ? pc[0][4 * jj + e] : pc[2][4 * jj + e];
+                row[xl + (lo ? 0 : 64)] = v;
+            }
+    };
+    // Adds the strip (formed for this tile) times sqrt(D) to the accumulators.
+    auto bias_add_formed = [&](f32x16* a) {
+        // chunk k = 15 - 8 s - 2 jj - hh of row qi at SROW qi + 16 k
+        const unsigned ln = opaque((unsigned)lane);
+        const char* rb = bstrip + (ln & 31u) * (unsigned)SROW + 16u * (15u - (ln >> 5));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 w = *(const f32x4*)(rb - 16 * (8 * s2 + 2 * jj));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a[s2][4 * jj + e] = __builtin_fmaf(w[e], INV_SCALE, a[s2][4 * jj + e]);
+            }
+    };
+
     // Software pipeline, per 64-key tile t: the DMA of the next live tile is
     // issued first; S^T = K Q^T of both 32-key halves runs as two interleaved
     // MFMA chains; tile t's bias (loaded during tile t - 1) is added and the
@@ -607,6 +706,14 @@ void attn_fwd_kernel(FwdParams p)
         // (after the last tile the current one is fetched again into the free
         // buffers, which nothing reads, so that every iteration issues the same
         // memory instructions)
+        // (REL > 0: the table operands of this tile go out before the DMA of
+        // the next one, so that waiting for them leaves that DMA in flight)
+        bf16x8 tab[3][NRK];
+        bool formed = false;
+        if constexpr (WB && REL > 0) {
+            formed = rel_needed(cur);
+            if (formed) load_table(j0, tab);
+        }
         asm volatile("" ::: "memory");
         issue_tile(nxt.kt <= kt_hi ? nxt : cur, kbuf ^ 1, vnext);
         asm volatile("" ::: "memory");
@@ -653,7 +760,15 @@ void attn_fwd_kernel(FwdParams p)
         // ---- + bias * sqrt(D) (nothing on tiles this wave skips); the bias
         // registers / strip then take the next tile's
         int ncode = 0;   // bias code of the next tile
-        if constexpr (WB) {
+        if constexpr (WB && REL > 0) {
+            if (formed) {
+                wait_vm_keep(N_KV_DMA);
+                form_strip(tab);
+                __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // this wave's strip writes are done
+                bias_add_formed(acc);
+                __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // and read, before the next tile rewrites it
+            }
+        } else if constexpr (WB) {
             bias_add_tile(bcode, j0, acc);
             asm volatile("" ::: "memory");
             ncode = load_bias(nxt);
@@ -778,7 +893,7 @@ void attn_fwd_kernel(FwdParams p)
         };
     while (cur.kt <= kt_hi && cur.kt < kt_split) step(std::false_type{});
     // the first tile that may carry bias: its loads overlap its own QK^T
-    if (cur.kt <= kt_hi) bcode = load_bias(cur);
+    if (REL == 0 && cur.kt <= kt_hi) bcode = load_bias(cur);
     while (cur.kt <= kt_hi) step(std::true_type{});
     // ---- the last tile's O^T += V^T P^T
     {
@@ -1163,11 +1278,11 @@ Shape choose_shape(int G)
     return s;
 }
 
-template <int D, bool PB>
+template <int D, bool PB, int REL>
 void launch_fwd(const Shape& sh, dim3 grid, hipStream_t st, const FwdParams& p)
 {
     (void)sh;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, PB, NWAVES>), grid, dim3(64 * NWAVES), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, PB, NWAVES, REL>), grid, dim3(64 * NWAVES), 0, st, p);
 }
 
 // Positions for the generic flex forward, one workgroup per batch row: a
@@ -1251,12 +1366,20 @@ struct Strides {
     long long bs, ts, hs;   // elements between batch rows, tokens, heads
 };
 
+// In-kernel profile rows (attn_fwd_relproj): relative features and table.
+struct RelArgs {
+    const void* rfeat = nullptr;
+    const void* table = nullptr;
+    int d_rel = 0;                 // 0: profiles are read
+    long long r_bs = 0, r_ts = 0, r_hs = 0, t_hs = 0;
+};
+
 // Launches the attention kernel over a planned and staged workspace.
 int run_forward(const void* q, const void* k, void* workspace, const void* profiles, int profiles_dtype,
                 const float* sink, const uint8_t* valid, const MaskArgs& ma, const int32_t* positions, int window,
                 int query_offset, int B, int Sq, int Sk, int Hq, int Hkv, int D, int E, void* out, int out_bf16,
                 float* lse, Strides qs, Strides ks, Strides os, Strides ls, Strides ss, float c_log2,
-                hipStream_t st)
+                hipStream_t st, const RelArgs& rel = RelArgs{})
 {
     const int nQB = ceil_div(Sq, BM), nKT = ceil_div(Sk, BN);
     const Shape sh = choose_shape(Hq / Hkv);
@@ -1295,12 +1418,22 @@ int run_forward(const void* q, const void* k, void* workspace, const void* profi
     if (nblocks >= (size_t(1) << 31)) return fail(INKATTN_ERR_SHAPE, "grid too large");
     const dim3 grid((unsigned)nblocks);
     const bool pb = profiles_dtype == INKATTN_BF16;
-    if (D == 128) {
-        if (pb) launch_fwd<128, true>(sh, grid, st, p);
-        else launch_fwd<128, false>(sh, grid, st, p);
+    p.rfeat = (const __bf16*)rel.rfeat;
+    p.table = (const __bf16*)rel.table;
+    p.r_bs = rel.r_bs; p.r_ts = rel.r_ts; p.r_hs = rel.r_hs;
+    p.t_hs = rel.t_hs;
+    if (rel.d_rel == 16) {
+        if (D == 128) launch_fwd<128, false, 16>(sh, grid, st, p);
+        else launch_fwd<64, false, 16>(sh, grid, st, p);
+    } else if (rel.d_rel == 32) {
+        if (D == 128) launch_fwd<128, false, 32>(sh, grid, st, p);
+        else launch_fwd<64, false, 32>(sh, grid, st, p);
+    } else if (D == 128) {
+        if (pb) launch_fwd<128, true, 0>(sh, grid, st, p);
+        else launch_fwd<128, false, 0>(sh, grid, st, p);
     } else {
-        if (pb) launch_fwd<64, true>(sh, grid, st, p);
-        else launch_fwd<64, false>(sh, grid, st, p);
+        if (pb) launch_fwd<64, true, 0>(sh, grid, st, p);
+        else launch_fwd<64, false, 0>(sh, grid, st, p);
     }
     return check_launch("attn_fwd_kernel");
 }
@@ -1490,6 +1623,57 @@ int attn_fwd(const void* q, const void* k, const void* v,
     return attn_fwd_planned(q, k, v, profiles, profiles_dtype, sink, valid, key_valid, positions, key_positions,
                             window, query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, lse, workspace, workspace_bytes,
                             stream);
+}
+
+int attn_fwd_relproj(const void* q, const void* k, const void* v,
+                     const void* rfeat, const void* table, int table_heads, int d_rel,
+                     const float* sink, const uint8_t* valid, const uint8_t* key_valid,
+                     const int32_t* positions, const int32_t* key_positions,
+                     int64_t window, int64_t query_offset,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
+                     float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_last_error[0] = '\0';
+    if (d_rel != 16 && d_rel != 32)
+        return fail(INKATTN_ERR_UNSUPPORTED, "relative feature width %d not built (16, 32)", d_rel);
+    if (Hq >= 1 && table_heads != 1 && table_heads != Hq)
+        return fail(INKATTN_ERR_SHAPE, "table_heads=%d must be 1 (shared) or Hq=%d", table_heads, Hq);
+    // the profile checks of attn_fwd stand for the feature tensor (same rows, E entries per row)
+    if (int rc = check_fwd_args(q, k, v, rfeat, INKATTN_BF16, sink, B, Sq, Sk, Hq, Hkv, D, E, out, lse)) return rc;
+    if ((size_t)E * d_rel * 2 >= (size_t(1) << 32)) return fail(INKATTN_ERR_SHAPE, "table slice above 4 GiB");
+    MaskArgs ma;
+    if (int rc = resolve_mask_args(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, &ma))
+        return rc;
+    if ((size_t)B * Sq == 0) return INKATTN_OK;
+    if (!table) return fail(INKATTN_ERR_NULL, "table is NULL");
+    if (!aligned(rfeat, 16) || !aligned(table, 16))
+        return fail(INKATTN_ERR_ALIGN, "rfeat and table must be 16-byte aligned");
+    if ((size_t)Sk * Hkv * D * 2 >= (size_t(1) << 32))
+        return fail(INKATTN_ERR_SHAPE, "one batch row of k / v must stay below 4 GiB");
+    if (window >= (int64_t(1) << 31) || window < 0) window = 0;
+    if (int rc = check_tile_counts(B, Sq, Sk, Hq, Hkv)) return rc;
+    if (int rc = check_workspace(workspace, workspace_bytes, fwd_workspace_bytes(B, Sq, Sk, Hkv, D))) return rc;
+    if (int rc = attn_plan(valid, key_valid, positions, key_positions, query_offset, B, Sq, Sk, workspace,
+                           workspace_bytes, stream))
+        return rc;
+    if (int rc = attn_stage_values(v, valid, key_valid, query_offset, B, Sq, Sk, Hkv, D, workspace,
+                                   workspace_bytes, stream))
+        return rc;
+    RelArgs rel;
+    rel.rfeat = rfeat;
+    rel.table = table;
+    rel.d_rel = d_rel;
+    rel.r_bs = (long long)Sq * Hq * d_rel;
+    rel.r_ts = (long long)Hq * d_rel;
+    rel.r_hs = d_rel;
+    rel.t_hs = table_heads == 1 ? 0 : (long long)E * d_rel;
+    const long long sq_h = (long long)Hq * D, sk_h = (long long)Hkv * D;
+    return run_forward(q, k, workspace, nullptr, INKATTN_F32, sink, valid, ma, positions, (int)window,
+                       (int)query_offset, B, Sq, Sk, Hq, Hkv, D, E, out, 0, lse,
+                       Strides{Sq * sq_h, sq_h, D}, Strides{Sk * sk_h, sk_h, D}, Strides{Sq * sq_h, sq_h, D},
+                       Strides{(long long)Sq * Hq, Hq, 1}, Strides{(long long)Sq * Hq, Hq, 1},
+                       (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634), (hipStream_t)stream, rel);
 }
 
 int attn_fwd_noalloc(const void* q, const void* k, const void* v,

@@ -241,3 +241,45 @@ def flex_custom(B: int, S: int, Hq: int, Hkv: int, D: int, mask: str = "causal",
                 **kw) -> dict:
     """Inputs for an ad-hoc generic flex shape with the same value recipe."""
     return generate_flex(FlexWorkload("custom", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, mask=mask, seed=seed, **kw))
+
+
+# ----------------------------------------------------------------------------
+# Relative features instead of profiles (the in-kernel profile rows of
+# attn_fwd_relproj): per (token, query head) d_rel features rfeat
+# [B,S,Hq,d_rel] and a relative table [T,E,d_rel] (T = 1 shared, or Hq), both
+# bf16.  rfeat ~ N(0, 1) and table ~ N(0, 0.5 / sqrt(d_rel)), so that the
+# profile entries they form have the standard deviation 0.5 of the profiles
+# of the workloads above.  Drawn after the workload's own tensors, from the
+# same generator.
+# ----------------------------------------------------------------------------
+RELPROJ_WORKLOADS = {
+    # the local (sliding-window) layer with its profiles formed in-kernel
+    "local_relproj": (WORKLOADS["local"], 32, 1),
+}
+
+
+def add_relative_features(x: dict, d_rel: int, table_heads: int, seed: int) -> dict:
+    """Adds ``rfeat`` and ``table`` (and ``d_rel``) to the inputs ``x`` of a workload; the
+    profiles tensor is dropped (the kernel forms its rows)."""
+    w = x["workload"]
+    gen = torch.Generator().manual_seed(seed)
+    B, S, Hq = x["q"].shape[0], x["q"].shape[1], x["q"].shape[2]
+    E = x["profiles"].shape[-1]
+    T = 1 if table_heads == 1 else Hq
+    y = dict(x)
+    y["rfeat"] = _randn((B, S, Hq, d_rel), 1.0, gen, torch.bfloat16)
+    y["table"] = _randn((T, E, d_rel), 0.5 / d_rel ** 0.5, gen, torch.bfloat16)
+    y["d_rel"] = d_rel
+    y["E"] = E
+    y["profiles"] = None
+    del w
+    return y
+
+
+def generate_relproj(name: str) -> dict:
+    """Inputs of a named relative-feature workload (deterministic)."""
+    w, d_rel, table_heads = RELPROJ_WORKLOADS[name]
+    x = generate(w)
+    y = add_relative_features(x, d_rel, table_heads, seed=w.seed + 500)
+    y["relproj_name"] = name
+    return y
