@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / fp16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 DEFAULT_WORKLOAD = "full_causal_8k"
+MALL_FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB MALL
 # the forward kernel's sources: its traffic record holds their combined sha256
 KERNEL_SRCS = [os.path.join(ROOT, "transformer_attention_03_amd", "csrc", f) for f in ("inkattn.hip", "common.h")]
 
@@ -176,6 +177,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mall-flush", action="store_true",
+                    help="do not flush the 256 MB MALL between timed steps (then ms_per_step is wall clock)")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -235,27 +238,38 @@ def main():
         d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"], positions=d["positions"],
         window=w.window, out=out, lse=lse, workspace=ws, stream=stream)
 
-    def step(ev0=None, ev1=None):
+    # The 256 MB MALL (last-level cache) would otherwise keep inputs of one step
+    # for the next: a 512 MiB write before every step, outside the step's events.
+    flush = None if args.no_mall_flush else torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def step(evs=None):
+        if flush is not None:
+            flush.fill_(1)
+        if evs is not None:
+            evs[0].record(stream)
         plan()
         stage_values()
-        if ev0 is not None:
-            ev0.record(stream)
+        if evs is not None:
+            evs[1].record(stream)
         attention()
-        if ev1 is not None:
-            ev1.record(stream)
+        if evs is not None:
+            evs[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
+    for e in evs:
+        step(e)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    # with the flush, a step's time is its own events' span (the flush is not the step's work)
+    ms_step = step_ms if flush is not None else wall_ms
+    kern_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     if not torch.isfinite(out).all():
         sys.exit("non-finite output")
 
@@ -278,6 +292,10 @@ def main():
                                f"window={w.window} profiles={str(w.profiles_dtype).replace('torch.', '')}",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
                    "qk_mfma": "bf16", "pv_mfma": "fp16", "accumulate": "fp32"},
+        "timing": ("per-step HIP events (pre-pass, value copy, attention kernel); the MALL is flushed by a "
+                   f"{MALL_FLUSH_BYTES >> 20} MiB write before each step, outside the events; wall clock over the "
+                   f"{args.steps} steps, flushes included: {wall_ms:.4f} ms/step") if flush is not None else
+                  "wall clock over the timed steps, no cache flush between them",
         "tokens_per_s": valid_tokens / (ms_step * 1e-3),
         "mfma_frac_step": flops / (ms_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
         "unmasked_pairs": pairs,
@@ -563,19 +581,22 @@ def bench_relproj(args):
                                  positions=d["positions"], window=w.window, out=out, lse=lse, workspace=ws,
                                  stream=stream)
 
+    flush = None if args.no_mall_flush else torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e0, e1 in evs:
+        if flush is not None:
+            flush.fill_(1)
         e0.record(stream)
         step()
         e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
     call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms_step = call_ms if flush is not None else (t1 - t0) * 1e3 / args.steps
     if not torch.isfinite(out).all():
         sys.exit("non-finite output")
     gbs = nbytes / (call_ms * 1e-3) / 1e9
