@@ -59,6 +59,12 @@ SMALL = {
     "S1": lambda: W.custom(B=3, S=1, Hq=4, Hkv=2, D=128, E=5, seed=111),
     "wide_sink": lambda: W.custom(B=1, S=200, Hq=8, Hkv=2, D=128, E=64, seed=112, sink_std=8.0,
                                   profile_std=3.0),
+    # strip runs that reach past the end of a (batch row, head) profile block: the last row
+    # (E 100), and with E below a run's entry count several rows before it (E 5, bf16 E 3)
+    "E100_block_end": lambda: W.custom(B=1, S=333, Hq=4, Hkv=2, D=128, E=100, seed=115),
+    "E5_rows_near_end": lambda: W.custom(B=1, S=100, Hq=4, Hkv=2, D=64, E=5, seed=116),
+    "bf16_E3_rows_near_end": lambda: W.custom(B=1, S=129, Hq=4, Hkv=1, D=128, E=3, seed=117,
+                                              profiles_dtype=torch.bfloat16),
 }
 
 
@@ -152,6 +158,34 @@ def test_index_probe_decodes_key(E, D, pdt, S, structure):
     expect = (np.arange(S)[:, None] - rstar.numpy().T)
     assert np.array_equal(dec, expect)
     assert np.array_equal(np.rint(out[0, :, :, 2]), np.repeat((np.arange(Hq) // (Hq // Hkv))[None, :], S, 0))
+
+
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("E,S", [(128, 400), (100, 333)])
+def test_index_probe_at_the_extent_edge(E, S, pdt):
+    """The peak at distances E-1 .. E-3 (by head) for every row that reaches them, the last row
+    of each (batch row, head) profile block included: the entries next to the block's end and
+    to the next row's, where a 16-byte run of the strip reaches past the row."""
+    B, Hq, Hkv, D = 1, 6, 2, 128
+    x = W.custom(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, E=E, seed=130, profiles_dtype=pdt)
+    x["q"].zero_()
+    x["k"].zero_()
+    x["sink"].fill_(-math.inf)
+    n_i = torch.arange(S)[None, :] + 1
+    h_idx = torch.arange(Hq)[:, None]
+    rstar = torch.clamp(torch.minimum(n_i, torch.tensor(E)) - 1 - (h_idx % 3), min=0)
+    prof = torch.full((B, Hq, S, E), -30000.0)
+    prof[0].scatter_(2, rstar[..., None], 40.0)
+    x["profiles"] = prof.to(pdt)
+    v = torch.zeros(B, S, Hkv, D)
+    j = torch.arange(S, dtype=torch.float32)
+    v[0, :, :, 0] = (j % 256)[:, None]
+    v[0, :, :, 1] = (j // 256)[:, None]
+    x["v"] = v.to(torch.bfloat16)
+    announce(f"index probe at the extent edge: E={E} S={S} profiles={pdt}")
+    out, _ = run_hip(x)
+    dec = np.rint(out[0, :, :, 0]) + 256 * np.rint(out[0, :, :, 1])
+    assert np.array_equal(dec, np.arange(S)[:, None] - rstar.numpy().T)
 
 
 def test_garbage_at_invalid_tokens():

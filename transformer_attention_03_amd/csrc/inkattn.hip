@@ -179,13 +179,14 @@ __device__ __forceinline__ void wait_all_and_barrier()
 }
 
 // As wait_all_and_barrier, but the last n_after vector-memory loads of the
-// wave (n_after in {0, 4, 8, 16, 20, 32}) may still be in flight.  s_waitcnt
+// wave (n_after in {0, 4, 5, 8, 16, 20, 32}) may still be in flight.  s_waitcnt
 // operand: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8.
 __device__ __forceinline__ void wait_dma_and_barrier(int n_after)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     switch (n_after) {
     case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0075); break;
     case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
     case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
     case 20: __builtin_amdgcn_s_waitcnt(0x4074); break;
@@ -504,10 +505,14 @@ void attn_fwd_kernel(FwdParams p)
     //  - BC_ROWS (fp32): 16-byte runs, 4 rows per instruction, 8 instructions;
     //    only when the tile's lowest offset (row 0, distance R_0 - 63) lies
     //    inside the block, so that no run straddles its start;
-    //  - BC_ENTRIES (bf16, and fp32 near the block's start): one instruction
-    //    per row, each lane one entry at its exact offset (64 contiguous
-    //    entries per instruction); a bf16 entry lands zero-extended in the
-    //    low half of its dword.
+    //  - BC_ENTRIES (fp32 near the block's start): one instruction per row,
+    //    each lane one entry at its exact offset (64 contiguous entries per
+    //    instruction).
+    // bf16 profiles keep 2 bytes per entry: row r at 144 r holds a window of
+    // 72 entries starting at the 4-byte boundary at or before the row's first
+    // needed entry (clamped at the block start), as 9 dword-aligned 16-byte
+    // runs, 5 instructions per tile (BC_ROWS); the reads shift each entry
+    // group out of three dwords.
     enum : int { BC_NONE = 0, BC_ROWS = 1, BC_ENTRIES = 2, BC_FAR = 4 };
     char* bstrip = smem + B_OFF + wave * BSTRIP;
 
@@ -521,7 +526,25 @@ void attn_fwd_kernel(FwdParams p)
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // earlier reads of the strip are done
         lds_char* const bs = opaque_lds((lds_char*)bstrip);
         const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
-        if (!PROF_BF16 && min_off >= 0) {
+        if constexpr (PROF_BF16) {
+            // bf16: row r's window of 72 entries from a0 = max(s0 & ~1, 0) (s0 = min_off + r (E + 1),
+            // its first needed entry), 9 dword-aligned 16-byte runs at 144 r + 16 c of the strip;
+            // instruction u, lane L takes run g = 64 u + L (r = g / 9, c = g % 9), 288 runs in 5
+            // instructions, the 32 lanes past them reading nothing (offsets out of range)
+            const unsigned e1 = opaque_s((unsigned)(p.E + 1));
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const unsigned g = 64u * (unsigned)u + ln;
+                const unsigned r = (g * 57u) >> 9;                  // g / 9 for g < 320
+                const unsigned c = g - 9u * r;
+                const int s0 = min_off + (int)(r * e1);
+                const unsigned a0 = (unsigned)max(s0 & ~1, 0);
+                const unsigned off = opaque(g < 288u ? (a0 + 8u * c) * 2u : 0xFFFFFFF0u);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prsrc, (lds_void*)(bs + 1024 * u), 16, off, 0, 0, 0);
+            }
+            return BC_ROWS | far;
+        }
+        if (min_off >= 0) {
             // row r = 4 u + lane / 16 takes chunk (lane % 16) ^ (r % 16) = ((lane % 16) ^ (lane / 16)) ^ 4 (u % 4)
             const unsigned bl = (ln >> 4) * (unsigned)(p.E + 1) * 4u;
             const unsigned rstep = opaque_s((unsigned)(p.E + 1) * 16u);   // bytes between rows 4 apart, + 16
@@ -548,29 +571,83 @@ void attn_fwd_kernel(FwdParams p)
         return BC_ENTRIES | far;
     };
     // Vector-memory instructions load_bias issued for a code.
-    auto bias_loads = [&](int code) -> int { return (code & BC_ROWS) ? 8 : (code & BC_ENTRIES) ? BM : 0; };
+    auto bias_loads = [&](int code) -> int {
+        return (code & BC_ROWS) ? (PROF_BF16 ? 5 : 8) : (code & BC_ENTRIES) ? BM : 0;
+    };
     // Adds tile j0t's bias (code as load_bias returned it) times sqrt(D) to the
     // accumulators.  Its loads were issued before this wave's DMA of the next
     // K / V tile, which may stay outstanding (N_KV_DMA instructions).
     auto bias_add_tile = [&](int code, int j0t, f32x16* a) {
         if (code == BC_NONE) return;
         wait_vm_keep(N_KV_DMA);
-        // chunk k = 15 - 8 s - 2 jj - hh of row qi (distances R - 32 s - 8 jj - 4 hh - 3 ..)
-        // sits at slot k ^ (qi % 16) = (15 ^ hh ^ (qi % 16)) ^ (8 s + 2 jj)
         const unsigned ln = opaque((unsigned)lane);   // offsets derived per tile, not held in registers
-        const unsigned rb = (ln & 31u) * 256u + 16u * (15u ^ (ln >> 5) ^ (ln & 15u));
         f32x4 w[2][4];
+        if constexpr (PROF_BF16) {
+            // row qi's window starts delta entries before its first needed entry s0 (delta 0 or 1,
+            // negative where the window was clamped at the block start: the entries before it are
+            // those of keys after the query, masked); chunk k's 4 entries start at window entry
+            // delta + 4 k, i.e. byte 2 (delta & 1) of dword (delta >> 1) + 2 k, and are shifted
+            // out of three dwords (bf16 -> fp32: the entry is the upper half)
+            const int s0 = i0 * p.E + qlo - j0t - (BN - 1) + (int)(ln & 31u) * (p.E + 1);
+            const int delta = s0 - max(s0 & ~1, 0);
+            const unsigned sel = 2u * ((unsigned)delta & 1u);
+            const unsigned* const rw =
+                (const unsigned*)(bstrip + (ln & 31u) * 144u) + (delta >> 1) + 2 * (15 - (int)(ln >> 5));
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                w[s2][jj] = *(const f32x4*)(bstrip + (rb ^ (unsigned)(16 * (8 * s2 + 2 * jj))));
-                if constexpr (PROF_BF16) {
+                for (int jj = 0; jj < 4; ++jj) {
+                    const unsigned* const d = rw - 2 * (8 * s2 + 2 * jj);
+                    const unsigned d0 = d[0], d1 = d[1], d2 = d[2];
+                    const unsigned x0 = __builtin_amdgcn_alignbyte(d1, d0, sel);
+                    const unsigned x1 = __builtin_amdgcn_alignbyte(d2, d1, sel);
+                    w[s2][jj][0] = __uint_as_float(x0 << 16);
+                    w[s2][jj][1] = __uint_as_float(x0 & 0xFFFF0000u);
+                    w[s2][jj][2] = __uint_as_float(x1 << 16);
+                    w[s2][jj][3] = __uint_as_float(x1 & 0xFFFF0000u);
+                }
+        } else {
+            // chunk k = 15 - 8 s - 2 jj - hh of row qi (distances R - 32 s - 8 jj - 4 hh - 3 ..)
+            // sits at slot k ^ (qi % 16) = (15 ^ hh ^ (qi % 16)) ^ (8 s + 2 jj)
+            const unsigned rb = (ln & 31u) * 256u + 16u * (15u ^ (ln >> 5) ^ (ln & 15u));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)   // the entry is the upper half of the fp32 value
-                        w[s2][jj][e] = __uint_as_float(__float_as_uint(w[s2][jj][e]) << 16);
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    w[s2][jj] = *(const f32x4*)(bstrip + (rb ^ (unsigned)(16 * (8 * s2 + 2 * jj))));
+        }
+        if (code & BC_ROWS) {
+            // A 16-byte run that reaches past the end of the (batch row, head) block reads as zeros
+            // in full, entries inside the block included.  A row whose runs may reach that far
+            // (its first needed entry s0 plus the run span passes Sq E) reads its entries one by
+            // one at their exact offsets instead; the span grows with the row, so the wave's last
+            // row decides whether any row does.
+            constexpr int SPAN = PROF_BF16 ? 72 : BN;
+            const int last = min(i0 + BM, p.Sq) - 1;
+            const int lim = p.Sq * p.E;
+            if (last * p.E + (qlo + last - i0) - j0t - (BN - 1) + SPAN > lim) {
+                const int s0r = i * p.E + gi - j0t - (BN - 1);
+                if (i < p.Sq && s0r + SPAN > lim) {
+                    const unsigned rd = (unsigned)(gi - 4 * hh - j0t);
+                    const unsigned rowoff = (unsigned)i * (unsigned)p.E;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const unsigned r = rd - (unsigned)(32 * s2 + 8 * jj + (e ^ 3));
+                                const unsigned off = opaque(r < (unsigned)p.E ? (rowoff + r) * PE : 0xFFFFFFF0u);
+                                if constexpr (PROF_BF16)
+                                    w[s2][jj][e] = __uint_as_float(
+                                        (unsigned)__builtin_amdgcn_raw_buffer_load_b16(prsrc, (int)off, 0, 0) << 16);
+                                else
+                                    w[s2][jj][e] = __uint_as_float(
+                                        __builtin_amdgcn_raw_buffer_load_b32(prsrc, (int)off, 0, 0));
+                            }
                 }
             }
+        }
         if (code & BC_FAR) {
             // distances outside [0, E) take no bias
             const unsigned rd = opaque((unsigned)(gi - 4 * hh - j0t));
