@@ -123,9 +123,8 @@ int attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Bytes of device workspace attn_bwd needs: the pre-pass summaries as for
  * attn_fwd, then per query 8 bytes and per (query, head) row 8 bytes of row
- * statistics, a bf16 copy of dout (B*Sq*Hq*D*2) and K^T in whole 64-key tiles
- * (B*Hkv*ceil(Sk/64)*64*D*2); each part rounded up to 256 bytes.  Never
- * fails; returns 0 for non-positive B.
+ * statistics and a bf16 copy of dout (B*Sq*Hq*D*2); each part rounded up to
+ * 256 bytes.  Never fails; returns 0 for non-positive B.
  */
 size_t attn_bwd_workspace_size(int B, int Sq, int Sk, int Hq, int Hkv, int D);
 

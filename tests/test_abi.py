@@ -158,7 +158,7 @@ def bwd_call(**over):
     (dict(dsink=None), 1), (dict(lse=None), 1), (dict(valid=None), 1), (dict(Sk=100), 1),
     (dict(Hq=6, Hkv=4), 2), (dict(E=0), 2), (dict(Sq=-1), 2), (dict(D=96), 3), (dict(pdt=5), 3),
     (dict(dout=A + 8), 4), (dict(dk=A + 4), 4), (dict(dprof=A + 2), 4), (dict(dsink=A + 2), 4),
-    (dict(ws=None), 5), (dict(wsb=101375), 5),
+    (dict(ws=None), 5), (dict(wsb=68607), 5),
 ])
 def test_bwd_host_validation(over, status):
     assert bwd_call(**over) == status
@@ -166,10 +166,9 @@ def test_bwd_host_validation(over, status):
 
 
 def test_bwd_workspace_size():
-    # summaries 256 + 256; per query 8 B; per row 8 B; bf16 dout; K^T in 64-key tiles; each
-    # rounded up to 256 B
-    assert binding.attn_bwd_workspace_size(1, 64, 64, 4, 2, 128) == 512 + 512 + 2048 + 65536 + 32768
-    assert bwd_call(wsb=101376, ws=None) == 5
+    # summaries 256 + 256; per query 8 B; per row 8 B; bf16 dout; each rounded up to 256 B
+    assert binding.attn_bwd_workspace_size(1, 64, 64, 4, 2, 128) == 512 + 512 + 2048 + 65536
+    assert bwd_call(wsb=68608, ws=None) == 5
     assert binding.attn_bwd_workspace_size(0, 64, 64, 4, 2, 128) == 0
     # bf16 profile gradients need only 2-byte alignment: the workspace check is what stops this call
     assert bwd_call(pdt=1, profiles=A + 2, dprof=A + 2, wsb=8) == 5

@@ -20,17 +20,17 @@
 //   2. bwd_prep_kernel: per row Delta - dlse, dsink and lse * log2(e); dout
 //      rounded to bf16 rows (0 on rows that are not real); per query its
 //      global column (-1 if not real) and document start column.
-//   3. bwd_stage_kernel: K^T per 64-key tile in bf16, the keys in the order of
-//      the dS^T registers the dQ product meets them in.
-//   4. bwd_dq_kernel (query-parallel, two waves per (query head, 32
+//   3. bwd_dq_kernel (query-parallel, two waves per (query head, 32
 //      queries), one per 32-key half of each tile, keys on MFMA M as in the
 //      forward): per 64-key tile S^T = K Q^T and dP^T = V dO^T, then P and dS
 //      from the saved lse, dS written to the profile gradient row (a
-//      contiguous run per query), dQ^T += K^T dS^T; the halves' partials are
-//      summed at the end.  Every entry of a query's profile-gradient row is
+//      contiguous run per query), dQ^T += K^T dS^T with K^T read from the
+//      staged K rows by transposing LDS reads; the halves' partials are
+//      summed at the end.  Each wave's bias runs arrive by LDS DMA two tiles
+//      ahead (two strips per wave).  Every entry of a query's profile-gradient row is
 //      written by one of its two waves: zeros where no tile they visit puts
 //      a value.
-//   5. bwd_dkdv_kernel (key-parallel, two waves per 32 keys, queries on MFMA
+//   4. bwd_dkdv_kernel (key-parallel, two waves per 32 keys, queries on MFMA
 //      M): per (32-query block, head of the group) the P wave forms S = Q K^T
 //      and P and accumulates dV^T += dO^T P; the dS wave forms dP = dO V^T,
 //      takes P through LDS one block later, forms dS and accumulates
@@ -80,7 +80,6 @@ struct BwdParams {
     int2* qinfo;                   // [B, Sq] {global column or -1, document start column}
     float2* rowstat;               // [B, Hq, Sq] {lse * log2(e) (0 when lse = -inf), Delta - dlse}
     __bf16* dob;                   // [B, Sq, Hq, D] bf16 dout, 0 on rows that are not real
-    __bf16* kt;                    // [B, Hkv, nKT, D, 64] K^T tiles
     float* dq;                     // [B, Sq, Hq, D]
     float* dk;                     // [B, Sk, Hkv, D]
     float* dv;                     // [B, Sk, Hkv, D]
@@ -94,17 +93,6 @@ struct BwdParams {
     float scale;                   // head_dim^-0.5
     float c_log2;                  // scale * log2(e)
 };
-
-// Element order of the staged transposed tiles.  Slot 8 hh + t of each
-// 16-token step holds token 8 (t / 4) + 4 hh + ((t % 4) ^ X): X = 3 for the
-// key tiles (the dQ kernel's S^T rows run through the keys in groups of four
-// reversed, as in the forward), X = 0 for the query tiles (the dK / dV
-// kernel's S rows are the queries in order).
-__device__ __forceinline__ int stage_token(int slot, int X)
-{
-    const int sg = slot >> 3, t = slot & 7;
-    return 16 * (sg >> 1) + 8 * (t >> 2) + 4 * (sg & 1) + ((t & 3) ^ X);
-}
 
 // XOR swizzle of the 16-byte chunks of a staged row of D bf16 (row pitch
 // 2 D bytes).  D = 128: the two 2-bit fields of r mod 16 are swapped, so that
@@ -156,55 +144,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Transposed bf16 tiles: one workgroup of (T / 8) (D / 8) threads per (batch
-// row, head, T-token tile).  Thread (slot group sg, dim chunk dc) loads the 8
-// tokens of slots 8 sg .. 8 sg + 7 at dims 8 dc .. 8 dc + 7 (fp32 sources are
-// rounded to bf16, nearest even), transposes the 8 x 8 block in registers and
-// writes 8 rows of 16 bytes.  Tokens that are not real, and the padding past
-// S, are written as 0.
-// ---------------------------------------------------------------------------
-template <int D, int T, int X, bool F32>
-__global__ __launch_bounds__((T / 8) * (D / 8)) void bwd_stage_kernel(const void* __restrict__ src,
-                                                                     const uint8_t* __restrict__ real, int S,
-                                                                     int H, int nT, long long bs, long long ts,
-                                                                     long long hs, __bf16* __restrict__ dst)
+// Waits until at most n vector-memory instructions of the wave are
+// outstanding (n in {0, 4, 8, 16, 20, 32}: the counts an iteration of the dQ
+// kernel can leave in flight), then meets the workgroup.  s_waitcnt operand:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0).
+__device__ __forceinline__ void wait_vm_and_barrier(int n)
 {
-    constexpr int CH = D / 8;
-    const int tile = blockIdx.x;              // (b H + h) nT + tt
-    const int tt = tile % nT;
-    const int h = (tile / nT) % H;
-    const int b = tile / (nT * H);
-    const int sg = threadIdx.x / CH, dc = threadIdx.x % CH;
-    bf16x8 rows[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int j = tt * T + stage_token(8 * sg + u, X);
-        bf16x8 y = bf16x8{};
-        if (j < S && real[(size_t)b * S + j]) {
-            const long long off = b * bs + j * ts + h * hs + 8 * dc;
-            if constexpr (F32) {
-                const f32x4 lo = *(const f32x4*)((const float*)src + off);
-                const f32x4 hi = *(const f32x4*)((const float*)src + off + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    y[e] = (__bf16)lo[e];
-                    y[4 + e] = (__bf16)hi[e];
-                }
-            } else {
-                y = *(const bf16x8*)((const __bf16*)src + off);
-            }
-        }
-        rows[u] = y;
+#if defined(__HIP_DEVICE_COMPILE__)
+    switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4074); break;
+    case 32: __builtin_amdgcn_s_waitcnt(0x8070); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0070); break;
     }
-    __bf16* d = dst + (size_t)tile * D * T;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bf16x8 o;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = rows[u][e];
-        *(bf16x8*)(d + (8 * dc + e) * T + 8 * sg) = o;
-    }
+#endif
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Per-workgroup list of live tiles, built in rounds of NSCHED candidates (one
@@ -289,16 +245,19 @@ void bwd_dq_kernel(BwdParams p)
     constexpr int NKK = D / 16;              // k-steps over D
     constexpr int NDB = D / 32;              // 32-row blocks of dQ^T
     constexpr int CH = D / 8;                // 16-byte chunks per row
-    constexpr int TBYTES = BN * D * 2;       // one K, V or K^T tile
-    constexpr int K_OFF = 0, V_OFF = TBYTES, KT_OFF = 2 * TBYTES, CA_OFF = 3 * TBYTES;
-    constexpr int STAGE = 3 * TBYTES + BN * 4;
+    constexpr int TBYTES = BN * D * 2;       // one K or V tile
+    constexpr int K_OFF = 0, V_OFF = TBYTES, CA_OFF = 2 * TBYTES;
+    constexpr int STAGE = 2 * TBYTES + BN * 4;
     constexpr int NSCHED = 64 * NW;
-    constexpr int B_OFF = 2 * STAGE;         // per-wave bias strips (16 values per lane)
+    // per-wave bias strips (16 values per lane), two per wave: the tiles of
+    // even and odd schedule position
+    constexpr int B_OFF = 2 * STAGE;
     constexpr int BSW = 32 * 32 * 4;         // one wave's strip
-    constexpr int SCHED_OFF = B_OFF + NW * BSW;
-    static_assert(NU * (D / 32) * 16 * 64 * 4 <= 2 * STAGE, "the dQ partials fit the staging buffers");
+    constexpr int SCHED_OFF = B_OFF + 2 * NW * BSW;
+    static_assert(NU * (D / 32) * 16 * 64 * 4 <= B_OFF + 2 * NW * BSW,
+                  "the dQ partials fit the staging buffers and strips");
     constexpr int LDS_BYTES = SCHED_OFF + (NSCHED + NW) * 4;
-    constexpr int GPW = TBYTES / 1024 / NW;  // 1 KB DMA groups per wave of one K, V or K^T tile
+    constexpr int GPW = TBYTES / 1024 / NW;  // 1 KB DMA groups per wave of one K or V tile
     constexpr int RPG = 1024 / (2 * D);      // K / V rows per DMA group
     static_assert(GPW >= 1 && TBYTES % (1024 * NW) == 0, "tile DMA groups must divide among the waves");
 
@@ -399,8 +358,6 @@ void bwd_dq_kernel(BwdParams p)
     const long long kvbase = ((long long)b * p.Sk * p.Hkv + g) * D;
     const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(p.k + kvbase, knrec);
     const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(p.v + kvbase, knrec);
-    const __amdgpu_buffer_rsrc_t kts = uniform_rsrc(p.kt + ((size_t)b * p.Hkv + g) * p.nKT * (size_t)(BN * D),
-                                                    (size_t)p.nKT * TBYTES);
     const __amdgpu_buffer_rsrc_t kas = uniform_rsrc(p.kanchor + (size_t)b * p.nKT * BN, (size_t)p.nKT * BN * 4);
     constexpr int ES = PB ? 2 : 4;                               // profile element bytes
     const size_t pblock = (size_t)p.Sq * p.E * ES;               // one (batch row, head) of profiles
@@ -419,18 +376,17 @@ void bwd_dq_kernel(BwdParams p)
         if (rmax < 0 || rmin >= p.E) return BC_NONE;
         return (rmin >= 0 && rmax < p.E) ? BC_FULL : BC_EDGE;
     };
-    float breg[16];    // bias of the next tile's key half: index 4 jj + e is distance rb + e (below)
-    int nbc = BC_NONE; // its class
-    // K, V, K^T and the key start columns of tile kt go to stage buffer sb by
+    // tiles before kt_split carry no bias for any wave of the workgroup (every
+    // distance of its first query column to the tile's last key is at least E)
+    const int qlo_wg = p.qoff + qb_first * BM;
+    const int kt_split = p.E <= 0 ? INT_MAX : (qlo_wg - p.E - (BN - 1) >= 0 ? (qlo_wg - p.E - (BN - 1)) / BN + 1 : 0);
+    // K, V and the key start columns of tile kt go to stage buffer sb by
     // buffer -> LDS DMA: lane l of 1 KB group a writes bytes 1024 a + 16 l of
-    // the tile and fetches the chunk that belongs there (K / V: row
-    // RPG a + l / CH, slot l % CH, i.e. chunk slot ^ row_swz(row); K^T: row
-    // 8 a + l / 8, slot l % 8, chunk slot ^ ((row / 2) % 8)).  Every wave also
-    // fetches the same 64 start columns, so that each wave's sequence of
-    // memory instructions is the same on every path.  The bias of the wave's
-    // key half goes to registers (stored to the strip at the end of the step).
-    auto stage_load = [&](int kt, int sb, auto with_bias) {
-        constexpr bool WB = decltype(with_bias)::value;
+    // the tile and fetches the chunk that belongs there (row RPG a + l / CH,
+    // slot l % CH, i.e. chunk slot ^ row_swz(row)).  Every wave also fetches
+    // the same 64 start columns, so that each wave's sequence of memory
+    // instructions is the same on every path.
+    auto stage_load = [&](int kt, int sb) {
         const int j0 = kt * BN;
         char* const st = smem + sb * STAGE;
         const unsigned ln = opaque((unsigned)lane);   // (offsets formed here, not held in registers)
@@ -443,70 +399,63 @@ void bwd_dq_kernel(BwdParams p)
             const unsigned kvo = ((unsigned)j0 + r) * krow + 16u * ((ln % CH) ^ (unsigned)row_swz<D>((int)r));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + K_OFF + 1024 * a), 16, kvo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + V_OFF + 1024 * a), 16, kvo, 0, 0, 0);
-            const unsigned d = (unsigned)(8 * a) + ln / 8;
-            const unsigned kto = (unsigned)(kt * TBYTES) + d * 128u + 16u * ((ln % 8) ^ ((d >> 1) & 7u));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kts, (lds_void*)(st + KT_OFF + 1024 * a), 16, kto, 0, 0, 0);
         }
         const unsigned cao = (unsigned)j0 * 4u + 4u * ln;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kas, (lds_void*)(st + CA_OFF), 4, cao, 0, 0, 0);
-        if constexpr (!WB) {
-            nbc = BC_NONE;
-            return;
-        }
-        nbc = bias_class(j0);
-        if (nbc == BC_NONE) return;
-        // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3)
-        {
+    };
+    // This wave's bias of tile kt goes by DMA into a strip of the wave, two
+    // tiles ahead of its use.  Entry (jj, e) of a lane is distance rb + e with
+    // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).  Whole runs (BC_FULL, fp32):
+    // one 16-byte run per jj, lane-major (bytes 1024 jj + 16 l); otherwise one
+    // entry per instruction, lane-major per (jj, e) (bytes 256 (4 jj + e) + 4 l;
+    // a bf16 entry lands zero-extended in its dword).  Returns the class; the
+    // instructions issued are bias_dmas(class).
+    auto bias_dma = [&](int kt, char* strip) -> int {
+        if (kt < 0 || kt < kt_split) return BC_NONE;
+        const int j0 = kt * BN;
+        const int bc = bias_class(j0);
+        if (bc == BC_NONE) return BC_NONE;
+        lds_char* const sp = opaque_lds((lds_char*)strip);
+        const unsigned ln = opaque((unsigned)lane);
+        const unsigned gb = (unsigned)gi - (unsigned)(j0 + 32 * kh + 3) - 4u * (ln >> 5);   // rb + 8 jj
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int rb = gi - (j0 + 32 * kh + 8 * jj + 4 * hh + 3);
-                float* w = breg + 4 * jj;
-                const unsigned off = (rowe + (unsigned)rb) * (unsigned)ES;
-                if constexpr (PB) {
-                    // (entry offsets kept opaque: they may wrap modulo 2^32 like
-                    // the run's start, which the instruction's offset field would not)
+        for (int jj = 0; jj < 4; ++jj) {
+            // (entry offsets kept opaque: they may wrap modulo 2^32 like the run's start)
+            const unsigned off = (rowe + gb - 8u * (unsigned)jj) * (unsigned)ES;
+            if (!PB && bc == BC_FULL) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 1024 * jj), 16, opaque(off), 0, 0, 0);
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = __uint_as_float(
-                            (unsigned)__builtin_amdgcn_raw_buffer_load_b16(prs, opaque(off + 2u * e), 0, 0) << 16);
-                } else if (nbc == BC_EDGE) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        w[e] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, opaque(off + 4u * e), 0, 0));
-                } else {
-                    const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = __int_as_float(x[e]);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (PB)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 256 * (4 * jj + e)), 2,
+                                                                 opaque(off + 2u * e), 0, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 256 * (4 * jj + e)), 4,
+                                                                 opaque(off + 4u * e), 0, 0, 0);
                 }
             }
         }
+        return bc;
     };
-    char* const bstrip = smem + B_OFF + wave * BSW;   // this wave's bias, lane-major
-    auto stage_store = [&](int buf, auto with_bias) {
-        constexpr bool WB = decltype(with_bias)::value;
-        (void)buf;
-        if (WB && nbc != BC_NONE) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                *(f32x4*)(bstrip + t * 1024 + 16 * lane) =
-                    f32x4{breg[4 * t], breg[4 * t + 1], breg[4 * t + 2], breg[4 * t + 3]};
-        }
-    };
+    auto bias_dmas = [&](int bc) -> int { return bc == BC_NONE ? 0 : (!PB && bc == BC_FULL) ? 4 : 16; };
+    // profile-gradient stores of a tile of class bc (see the body)
+    auto grad_stores = [&](int bc) -> int { return bc == BC_NONE ? 0 : (!PB && bc == BC_FULL) ? 4 : 16; };
+    char* const bstrip0 = smem + B_OFF + wave * BSW;   // strip 0 of this wave; strip 1 at + NW * BSW
 
     using F = std::false_type;
     using T = std::true_type;
-    // Tiles before kt_split carry no bias for any wave of the workgroup (every
-    // distance of its first query column to the tile's last key is at least
-    // E); while the current and the next tile are such, a loop body without
-    // the bias code runs.  The schedule is read one tile ahead for that.
-    const int qlo_wg = p.qoff + qb_first * BM;
-    const int kt_split = p.E <= 0 ? INT_MAX : (qlo_wg - p.E - (BN - 1) >= 0 ? (qlo_wg - p.E - (BN - 1)) / BN + 1 : 0);
+    // While the current tile lies before kt_split, a loop body without the
+    // bias code runs.
     int2 cur = next_entry(sch, kt_hi, classify);
-    int2 nxt = make_int2(-1, 0);
+    int2 nxt = make_int2(-1, 0), nx2 = make_int2(-1, 0);
+    int par = 0;        // strip of cur: its position in the schedule, mod 2
     if (cur.x >= 0) {
-        stage_load(cur.x, 0, T{});
-        stage_store(0, T{});
+        stage_load(cur.x, 0);
+        bias_dma(cur.x, bstrip0);
         nxt = next_entry(sch, kt_hi, classify);
+        bias_dma(nxt.x, bstrip0 + NW * BSW);
+        if (nxt.x >= 0) nx2 = next_entry(sch, kt_hi, classify);
     }
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is outstanding inside it
@@ -515,15 +464,54 @@ void bwd_dq_kernel(BwdParams p)
     int buf = 0;
     const int xw = qb - qb_first;
     const float nlse2 = -lse2;
+    // K^T operand of dQ^T += K^T dS^T, from the K rows by transposing LDS
+    // reads: for 16-key step c and d-block db, lane l reads 4 bf16 of key row
+    // 16 c + 4 hh + (l % 16) / 4 (and 8 rows further) at columns 32 db +
+    // 16 ((l / 16) % 2) + 4 (l % 4), and receives column d = 32 db + (l % 32)
+    // of the keys 16 c + 4 hh + t and 16 c + 8 + 4 hh + t, t < 4: the order of
+    // the dS^T operand below.  trof() is the byte offset in the swizzled rows
+    // (formed where used: not held in registers across the loop).
+    auto trof = [&](unsigned ln, int c2, int hi, int db) -> unsigned {
+        const unsigned r = 16u * (unsigned)(2 * kh + c2) + 8u * (unsigned)hi + 4u * (ln >> 5) + (ln & 15u) / 4u;
+        const unsigned col = 32u * (unsigned)db + 16u * ((ln >> 4) & 1u) + 4u * (ln & 3u);   // bf16 column
+        return (unsigned)K_OFF + r * (2u * D) + 16u * ((col / 8u) ^ (unsigned)row_swz<D>((int)r)) + 2u * (col % 8u);
+    };
     auto step = [&](auto with_bias) {
         constexpr bool WB = decltype(with_bias)::value;
-        // (buffer buf ^ 1 was last read before the barrier that ended the
-        // previous iteration)
-        if (nxt.x >= 0) stage_load(nxt.x, buf ^ 1, with_bias);
         const int j0 = cur.x * BN;
         const int my_cls = (cur.y >> (2 * xw)) & 3;
         const int bc = WB ? bias_class(j0) : (int)BC_NONE;
         const char* st = smem + buf * STAGE;
+        char* const strip = bstrip0 + par * (NW * BSW);
+        // ---- this tile's bias out of its strip (it landed by the end of the
+        // iteration before), so that the strip takes the tile two ahead
+        f32x4 bv[4];
+        if constexpr (WB) {
+            if (bc != BC_NONE) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    if (!PB && bc == BC_FULL) {
+                        bv[jj] = *(const f32x4*)(strip + jj * 1024 + 16 * lane);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const unsigned x = *(const unsigned*)(strip + 256 * (4 * jj + e) + 4 * lane);
+                            bv[jj][e] = PB ? __uint_as_float(x << 16) : __uint_as_float(x);
+                        }
+                    }
+                }
+            }
+#if defined(__HIP_DEVICE_COMPILE__)
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // (lgkmcnt(0)) read before the DMA below rewrites it
+#endif
+        }
+        asm volatile("" ::: "memory");
+        // (buffer buf ^ 1 was last read before the barrier that ended the
+        // previous iteration)
+        if (nxt.x >= 0) stage_load(nxt.x, buf ^ 1);
+        asm volatile("" ::: "memory");
+        const int nbc2 = bias_dma(nx2.x, strip);
+        asm volatile("" ::: "memory");
 
         // ---- S^T = K Q^T and dP^T = V dO^T for this wave's key half, keys
         // 32 kh + ((lane & 31) ^ 3) on M
@@ -557,7 +545,8 @@ void bwd_dq_kernel(BwdParams p)
 
         // ---- P, dS, profile gradients.  Element (jj, e) is key
         // j0 + 32 kh + 8 jj + 4 hh + (e ^ 3), distance rb + e with
-        // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).
+        // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).  The dS^T operand holds the
+        // keys of each group of 4 in increasing order (element 4 (jj % 2) + (e ^ 3)).
         const int* ca = (const int*)(st + CA_OFF);
         bf16x8 pd[2];
         auto body = [&](auto bct, auto mt) {
@@ -572,10 +561,9 @@ void bwd_dq_kernel(BwdParams p)
                     if constexpr (BCT == BC_NONE) {
                         pre = f32x4{nlse2, nlse2, nlse2, nlse2};
                     } else {
-                        const f32x4 bias = *(const f32x4*)(bstrip + jj * 1024 + 16 * lane);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            pre[e] = __builtin_fmaf(bias[e], LOG2E, nlse2);
+                            pre[e] = __builtin_fmaf(bv[jj][e], LOG2E, nlse2);
                             if constexpr (BCT == BC_EDGE)
                                 if ((unsigned)(rb + e) >= (unsigned)p.E) pre[e] = nlse2;
                         }
@@ -591,7 +579,7 @@ void bwd_dq_kernel(BwdParams p)
                             dz[e] = key_visible(gi_eff, a_q, j0 + kl + (e ^ 3), c4[e ^ 3], wlim) ? x : 0.0f;
                         else
                             dz[e] = x;
-                        pd[jj >> 1][4 * (jj & 1) + e] = (__bf16)dz[e];
+                        pd[jj >> 1][4 * (jj & 1) + (e ^ 3)] = (__bf16)dz[e];
                     }
                     // profile gradients: stores outside this query's row [0, E)
                     // get an offset past the buffer and are dropped
@@ -639,30 +627,33 @@ void bwd_dq_kernel(BwdParams p)
             else if (bc == BC_FULL) body(FULL{}, T{});
             else body(EDGE{}, T{});
         }
+        asm volatile("" ::: "memory");
 
         // ---- dQ^T += K^T dS^T over this wave's key half (16-key steps
-        // 2 kh, 2 kh + 1; K^T rows in the staged key order)
+        // 2 kh, 2 kh + 1), K^T read from the K rows
+        const unsigned tln = opaque((unsigned)lane);
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int c = 2 * kh + c2;
-                const int d = 32 * db + qi;
-                const bf16x8 a = *(const bf16x8*)(st + KT_OFF + d * 128 + 16 * ((2 * c + hh) ^ ((d >> 1) & 7)));
-                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pd[c2], dqacc[db], 0, 0, 0);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + trof(tln, c2, 0, db)));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + trof(tln, c2, 1, db)));
+                const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pd[c2],
+                                                                   dqacc[db], 0, 0, 0);
             }
 
-        // (this wave has read its bias strip: it takes the next tile's)
-        if (nxt.x >= 0) stage_store(buf ^ 1, with_bias);
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA of the next tile has landed
-#endif
-        __syncthreads();
+        // this wave's DMA of the next tile has landed (the bias DMA of the
+        // tile two ahead and this tile's profile-gradient stores, issued after
+        // it, may still be in flight); then every wave's has
+        wait_vm_and_barrier(bias_dmas(nbc2) + (WB ? grad_stores(bc) : 0));
         buf ^= 1;
+        par ^= 1;
         cur = nxt;
-        nxt = cur.x >= 0 ? next_entry(sch, kt_hi, classify) : make_int2(-1, 0);
+        nxt = nx2;
+        nx2 = nxt.x >= 0 ? next_entry(sch, kt_hi, classify) : make_int2(-1, 0);
     };
-    while (cur.x >= 0 && cur.x < kt_split && nxt.x < kt_split) step(F{});
+    while (cur.x >= 0 && cur.x < kt_split) step(F{});
     while (cur.x >= 0) step(T{});
 
     // ---- the two key halves' partials (the staging buffers are free: the
@@ -1163,18 +1154,16 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, s
 // Host side
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    size_t qinfo, rowstat, dob, kt, total;
+    size_t qinfo, rowstat, dob, total;
 };
 
 BwdLayout bwd_layout(int B, int Sq, int Sk, int Hq, int Hkv, int D)
 {
     BwdLayout l;
-    const size_t nKT = (size_t)ceil_div(Sk, BN);
     size_t o = summaries_bytes(B, Sq, Sk);
     l.qinfo = o;   o += round256((size_t)B * Sq * 8);
     l.rowstat = o; o += round256((size_t)B * Hq * Sq * 8);
     l.dob = o;     o += round256((size_t)B * Sq * Hq * D * 2);
-    l.kt = o;      o += round256((size_t)B * Hkv * nKT * BN * D * 2);
     l.total = o;
     return l;
 }
@@ -1186,12 +1175,6 @@ int launch_bwd(const BwdParams& p, hipStream_t st)
     const int rpb = 256 / (D / 4);
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, p);
     if (int rc = check_launch("bwd_prep_kernel")) return rc;
-    const unsigned nkt = (unsigned)((size_t)p.B * p.Hkv * p.nKT);
-    if (nkt > 0)
-        hipLaunchKernelGGL((bwd_stage_kernel<D, BN, 3, false>), dim3(nkt), dim3((BN / 8) * (D / 8)), 0, st,
-                           (const void*)p.k, p.key_valid, p.Sk, p.Hkv, p.nKT, (long long)p.Sk * p.Hkv * D,
-                           (long long)p.Hkv * D, (long long)D, p.kt);
-    if (int rc = check_launch("bwd_stage_kernel")) return rc;
     const size_t ndq = (size_t)p.nQG * p.B * p.Hkv * p.nchunk;
     hipLaunchKernelGGL((bwd_dq_kernel<D, PB>), dim3((unsigned)ndq), dim3(64 * DQ_WAVES), 0, st, p);
     if (int rc = check_launch("bwd_dq_kernel")) return rc;
@@ -1285,7 +1268,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* profiles, 
     p.qinfo = (int2*)(ws + lay.qinfo);
     p.rowstat = (float2*)(ws + lay.rowstat);
     p.dob = (__bf16*)(ws + lay.dob);
-    p.kt = (__bf16*)(ws + lay.kt);
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
