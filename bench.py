@@ -426,7 +426,7 @@ def bench_backward(args, w, x):
         "hbm_gbs_algorithmic": nbytes / (call_ms * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "attn_bwd call (pre-pass, prep, staging, bwd_dq_kernel, bwd_dkdv_kernel)",
+                     "kernel": "attn_bwd call (pre-pass, prep, bwd_dq_kernel, bwd_dkdv_kernel)",
                      "kernel_ms": call_ms, "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes},
     }
