@@ -67,7 +67,7 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_oracle_bwd.argtypes = [
         P, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-        P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
+        P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
     lib.attn_oracle_relproj_profiles.restype = ctypes.c_int
     lib.attn_oracle_relproj_profiles.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_int, P]
@@ -215,12 +215,15 @@ def attn_fwd(q, k, v, profiles, sink, valid, key_valid=None, positions=None,
 
 def attn_bwd(q, k, v, profiles, sink, valid, dout, dlse=None, key_valid=None, positions=None,
              key_positions=None, window: Optional[int] = None, query_offset: int = 0,
-             profiles_bf16: Optional[bool] = None, row_lo: int = 0, magnitudes: bool = False):
+             profiles_bf16: Optional[bool] = None, row_lo: int = 0, row_hi: int = 0,
+             magnitudes: bool = False, n_threads: int = 0):
     """fp64 gradients of the forward for upstream gradients ``dout [B,Sq,Hq,D]`` and ``dlse
     [B,Sq,Hq]`` (None: zero).  Returns ``(dq, dk, dv, dprofiles, dsink)`` as fp64 numpy arrays.
 
-    ``row_lo`` leaves out the query rows below it (dk / dv then hold only the later rows'
-    contributions); ``magnitudes`` returns the sums of absolute contributions instead."""
+    Only the query rows ``row_lo <= i < row_hi`` take part (``row_hi`` 0: up to Sq); dk / dv
+    then hold only those rows' contributions.  ``magnitudes`` returns the sums of absolute
+    contributions instead.  The work runs on ``n_threads`` threads (0: OpenMP's default)
+    split by (batch row, K/V head); the result does not depend on the count."""
     import torch
 
     B, Sq, Hq, D = (int(x) for x in q.shape)
@@ -246,7 +249,8 @@ def attn_bwd(q, k, v, profiles, sink, valid, dout, dlse=None, key_valid=None, po
         _ptr(qn), _ptr(kn), _ptr(vn), _ptr(pn), int(bool(profiles_bf16)), _ptr(sn),
         _ptr(valid_n), _ptr(kvalid_n), _ptr(pos_n), _ptr(kpos_n), w, int(query_offset),
         B, Sq, Sk, Hq, Hkv, D, E, _ptr(don), None if dln is None else _ptr(dln), int(row_lo),
-        int(bool(magnitudes)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dp), _ptr(ds))
+        int(row_hi), int(bool(magnitudes)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dp), _ptr(ds),
+        int(n_threads))
     if rc != 0:
         raise RuntimeError(f"attn_oracle_bwd failed ({rc})")
     return dq, dk, dv, dp, ds

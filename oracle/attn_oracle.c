@@ -320,12 +320,18 @@ int flex_oracle_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  *   dsink  = p_s (dlse - Delta)
  * out / lse are recomputed here in fp64.  Outputs: dq [B,Sq,Hq,D],
  * dk / dv [B,Sk,Hkv,D], dprofiles [B,Hq,Sq,E], dsink [B,Sq,Hq], all fp64.
- * Single-threaded over rows for dk / dv (they accumulate across rows).
  *
- * row_lo > 0 leaves out the query rows i < row_lo (their outputs stay 0):
- * dq / dprofiles / dsink of the other rows are unchanged, and dk / dv are
- * exact for the keys no earlier row can see (under the causal order, keys
- * j >= query_offset + row_lo).
+ * Only the query rows row_lo <= i < row_hi take part (row_hi <= 0 or above
+ * Sq means Sq); the others' outputs stay 0.  dq / dprofiles / dsink of the
+ * rows taken are those of the whole computation, and dk / dv are exact for
+ * the keys that no row outside the range can see (under the causal order
+ * with row_hi = Sq: keys j >= query_offset + row_lo; with a window w as well:
+ * keys j with j + w - 1 < query_offset + row_hi, when row_hi < Sq).
+ *
+ * The work is spread over threads by (batch row, K/V head): each thread owns
+ * the dk / dv rows of its head group, and every output element sums its
+ * terms in the same order (rows ascending, then the group's heads) whatever
+ * the thread count.  n_threads <= 0 leaves OpenMP's default.
  *
  * magnitudes != 0 returns, in the same arrays, each output's sum of absolute
  * contributions instead (every product and difference above taken in
@@ -338,8 +344,8 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const int32_t* positions, const int32_t* key_positions,
                     int64_t window, int64_t query_offset,
                     int B, int Sq, int Sk, int Hq, int Hkv, int D, int E,
-                    const double* dout, const double* dlse, int row_lo, int magnitudes,
-                    double* dq, double* dk, double* dv, double* dprofiles, double* dsink)
+                    const double* dout, const double* dlse, int row_lo, int row_hi, int magnitudes,
+                    double* dq, double* dk, double* dv, double* dprofiles, double* dsink, int n_threads)
 {
     if (!q || !k || !v || !profiles || !sink || !valid || !key_valid || !positions || !key_positions ||
         !dout || !dq || !dk || !dv || !dprofiles || !dsink)
@@ -351,91 +357,107 @@ int attn_oracle_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     memset(dk, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
     memset(dv, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
     memset(dprofiles, 0, sizeof(double) * (size_t)B * Hq * Sq * E);
-    double* z = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
-    double* o = (double*)malloc(sizeof(double) * (size_t)D);
-    uint8_t* ok = (uint8_t*)malloc((size_t)(Sk > 0 ? Sk : 1));
-    if (!z || !o || !ok) {
-        free(z); free(o); free(ok);
-        return -1;
-    }
     memset(dsink, 0, sizeof(double) * (size_t)B * Sq * Hq);
-    for (int b = 0; b < B; ++b)
-        for (int i = row_lo > 0 ? row_lo : 0; i < Sq; ++i) {
-            int count = 0;
-            for (int j = 0; j < Sk; ++j) {
-                ok[j] = (uint8_t)allowed(valid, key_valid, positions, key_positions, window, query_offset,
-                                         Sq, Sk, b, i, j);
-                count += ok[j];
-            }
-            int64_t p_i = positions[(size_t)b * Sq + i];
-            for (int h = 0; h < Hq; ++h) {
-                int g = h / G;
-                size_t row = ((size_t)b * Sq + i) * Hq + h;
-                double sigma = (double)sink[row];
-                double dl = dlse ? dlse[row] : 0.0;
-                const double* dov = dout + row * D;
-                if (count == 0) {                  /* lse = sigma, out = 0: only the sink moves lse */
-                    dsink[row] = isinf(sigma) && sigma < 0 ? 0.0 : (magnitudes ? fabs(dl) : dl);
-                    continue;
-                }
-                const uint16_t* qrow = q + row * D;
-                double M = sigma;
+    const int i_lo = row_lo > 0 ? row_lo : 0;
+    const int i_hi = (row_hi <= 0 || row_hi > Sq) ? Sq : row_hi;
+    int failed = 0;
+
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        double* o = (double*)malloc(sizeof(double) * (size_t)D);
+        uint8_t* ok = (uint8_t*)malloc((size_t)(Sk > 0 ? Sk : 1));
+        if (!z || !o || !ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int bg = 0; bg < B * Hkv; ++bg) {
+            if (!z || !o || !ok) continue;
+            const int b = bg / Hkv, g = bg % Hkv;
+            for (int i = i_lo; i < i_hi; ++i) {
+                int count = 0;
                 for (int j = 0; j < Sk; ++j) {
-                    if (!ok[j]) continue;
-                    const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    double dot = 0.0;
-                    for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
-                    int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
-                    double bias = 0.0;
-                    if (r >= 0 && r < E)
-                        bias = profile_at(profiles, profiles_is_bf16, (((size_t)b * Hq + h) * Sq + i) * (size_t)E + r);
-                    z[j] = scale * dot + bias;
-                    if (z[j] > M) M = z[j];
+                    ok[j] = (uint8_t)allowed(valid, key_valid, positions, key_positions, window, query_offset,
+                                             Sq, Sk, b, i, j);
+                    count += ok[j];
                 }
-                double L = exp(sigma - M);
-                for (int d = 0; d < D; ++d) o[d] = 0.0;
-                for (int j = 0; j < Sk; ++j) {
-                    if (!ok[j]) continue;
-                    double pj = exp(z[j] - M);
-                    L += pj;
-                    const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    for (int d = 0; d < D; ++d) o[d] += pj * bf16_to_double(vrow[d]);
-                }
-                double lse = M + log(L);
-                double delta = 0.0;
-                for (int d = 0; d < D; ++d)
-                    delta += magnitudes ? fabs(dov[d] * (o[d] / L)) : dov[d] * (o[d] / L);
-                dsink[row] = magnitudes ? exp(sigma - lse) * (fabs(dl) + delta) : exp(sigma - lse) * (dl - delta);
-                for (int j = 0; j < Sk; ++j) {
-                    if (!ok[j]) continue;
-                    double pj = exp(z[j] - lse);
-                    const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    double dp = 0.0;
-                    for (int d = 0; d < D; ++d)
-                        dp += magnitudes ? fabs(dov[d] * bf16_to_double(vrow[d])) : dov[d] * bf16_to_double(vrow[d]);
-                    double dz = magnitudes ? pj * (dp + delta + fabs(dl)) : pj * (dp - delta + dl);
-                    double* dkr = dk + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    double* dvr = dv + (((size_t)b * Sk + j) * Hkv + g) * D;
-                    double* dqr = dq + row * D;
-                    for (int d = 0; d < D; ++d) {
-                        double kd = bf16_to_double(krow[d]), qd = bf16_to_double(qrow[d]), od = dov[d];
-                        if (magnitudes) {
-                            kd = fabs(kd);
-                            qd = fabs(qd);
-                            od = fabs(od);
-                        }
-                        dqr[d] += scale * dz * kd;
-                        dkr[d] += scale * dz * qd;
-                        dvr[d] += pj * od;
+                int64_t p_i = positions[(size_t)b * Sq + i];
+                for (int h = g * G; h < (g + 1) * G; ++h) {
+                    size_t row = ((size_t)b * Sq + i) * Hq + h;
+                    double sigma = (double)sink[row];
+                    double dl = dlse ? dlse[row] : 0.0;
+                    const double* dov = dout + row * D;
+                    if (count == 0) {                  /* lse = sigma, out = 0: only the sink moves lse */
+                        dsink[row] = isinf(sigma) && sigma < 0 ? 0.0 : (magnitudes ? fabs(dl) : dl);
+                        continue;
                     }
-                    int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
-                    if (r >= 0 && r < E) dprofiles[(((size_t)b * Hq + h) * Sq + i) * (size_t)E + r] = dz;
+                    const uint16_t* qrow = q + row * D;
+                    double M = sigma;
+                    for (int j = 0; j < Sk; ++j) {
+                        if (!ok[j]) continue;
+                        const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+                        int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
+                        double bias = 0.0;
+                        if (r >= 0 && r < E)
+                            bias = profile_at(profiles, profiles_is_bf16, (((size_t)b * Hq + h) * Sq + i) * (size_t)E + r);
+                        z[j] = scale * dot + bias;
+                        if (z[j] > M) M = z[j];
+                    }
+                    double L = exp(sigma - M);
+                    for (int d = 0; d < D; ++d) o[d] = 0.0;
+                    for (int j = 0; j < Sk; ++j) {
+                        if (!ok[j]) continue;
+                        double pj = exp(z[j] - M);
+                        L += pj;
+                        const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        for (int d = 0; d < D; ++d) o[d] += pj * bf16_to_double(vrow[d]);
+                    }
+                    double lse = M + log(L);
+                    double delta = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        delta += magnitudes ? fabs(dov[d] * (o[d] / L)) : dov[d] * (o[d] / L);
+                    dsink[row] = magnitudes ? exp(sigma - lse) * (fabs(dl) + delta) : exp(sigma - lse) * (dl - delta);
+                    for (int j = 0; j < Sk; ++j) {
+                        if (!ok[j]) continue;
+                        double pj = exp(z[j] - lse);
+                        const uint16_t* krow = k + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        const uint16_t* vrow = v + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        double dp = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            dp += magnitudes ? fabs(dov[d] * bf16_to_double(vrow[d])) : dov[d] * bf16_to_double(vrow[d]);
+                        double dz = magnitudes ? pj * (dp + delta + fabs(dl)) : pj * (dp - delta + dl);
+                        double* dkr = dk + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        double* dvr = dv + (((size_t)b * Sk + j) * Hkv + g) * D;
+                        double* dqr = dq + row * D;
+                        for (int d = 0; d < D; ++d) {
+                            double kd = bf16_to_double(krow[d]), qd = bf16_to_double(qrow[d]), od = dov[d];
+                            if (magnitudes) {
+                                kd = fabs(kd);
+                                qd = fabs(qd);
+                                od = fabs(od);
+                            }
+                            dqr[d] += scale * dz * kd;
+                            dkr[d] += scale * dz * qd;
+                            dvr[d] += pj * od;
+                        }
+                        int64_t r = p_i - (int64_t)key_positions[(size_t)b * Sk + j];
+                        if (r >= 0 && r < E) dprofiles[(((size_t)b * Hq + h) * Sq + i) * (size_t)E + r] = dz;
+                    }
                 }
             }
         }
-    free(z); free(o); free(ok);
-    return 0;
+        free(z); free(o); free(ok);
+    }
+    return failed ? -1 : 0;
 }
 
 /*

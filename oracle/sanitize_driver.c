@@ -21,8 +21,8 @@ int flex_oracle_fwd(const uint16_t*, const uint16_t*, const uint16_t*, const flo
                     double*, int32_t*, int);
 int attn_oracle_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const void*, int, const float*,
                     const uint8_t*, const uint8_t*, const int32_t*, const int32_t*, int64_t, int64_t, int, int,
-                    int, int, int, int, int, const double*, const double*, int, int, double*, double*, double*,
-                    double*, double*);
+                    int, int, int, int, int, const double*, const double*, int, int, int, double*, double*,
+                    double*, double*, double*, int);
 int attn_oracle_mask(const uint8_t*, const uint8_t*, const int32_t*, const int32_t*, int64_t, int64_t, int, int,
                      int, int32_t*, uint8_t*, int);
 
@@ -100,7 +100,8 @@ static void run_case(int B, int Sq, int Sk, int Hq, int Hkv, int D, int E, int64
     for (int mag = 0; mag < 2; ++mag)
         expect(attn_oracle_bwd(q, k, v, bf16_prof ? (const void*)pb : (const void*)pf, bf16_prof, sink, valid,
                                kvalid, pos, kpos, window, qoff, B, Sq, Sk, Hq, Hkv, D, E, dout,
-                               mag ? NULL : dlse, Sq / 3, mag, dq, dk, dv, dp, ds) == 0,
+                               mag ? NULL : dlse, Sq / 3, mag ? 0 : Sq - 2, mag, dq, dk, dv, dp, ds,
+                               mag ? 1 : 3) == 0,
                "attn_oracle_bwd");
     free(q); free(k); free(v); free(pf); free(pb); free(sink); free(valid); free(kvalid); free(pos); free(kpos);
     free(rows); free(out); free(lse); free(cnt); free(cnt2); free(m); free(dout); free(dlse);

@@ -201,6 +201,39 @@ def test_row_range_keeps_later_rows_and_keys():
     assert np.all(part[0][:, :17] == 0)
 
 
+def test_row_window_range_keeps_its_rows_and_keys():
+    """Rows lo..hi-1 under a window w: their dq / dprofiles / dsink are the whole run's, and dk / dv
+    of the keys j with lo <= j and j + w - 1 < hi (no row outside the range sees them) too."""
+    w = 6
+    x = small(47, window=w, structure="single")
+    dout, dlse = _upstream(x, 147)
+    full = _bwd(x, dout, dlse)
+    lo, hi = 9, 27
+    part = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                           positions=x["positions"], window=w, row_lo=lo, row_hi=hi)
+    np.testing.assert_array_equal(part[0][:, lo:hi], full[0][:, lo:hi])
+    np.testing.assert_array_equal(part[3][:, :, lo:hi], full[3][:, :, lo:hi])
+    np.testing.assert_array_equal(part[4][:, lo:hi], full[4][:, lo:hi])
+    kl, kh = lo, hi - w + 1
+    np.testing.assert_allclose(part[1][:, kl:kh], full[1][:, kl:kh], atol=1e-14, rtol=0)
+    np.testing.assert_allclose(part[2][:, kl:kh], full[2][:, kl:kh], atol=1e-14, rtol=0)
+    # rows outside the range leave nothing, and keys seen from outside differ from the whole run
+    assert np.all(part[0][:, :lo] == 0) and np.all(part[0][:, hi:] == 0)
+    assert np.all(part[3][:, :, hi:] == 0) and np.all(part[4][:, :lo] == 0)
+    assert not np.allclose(part[1][:, kh:hi], full[1][:, kh:hi])
+
+
+def test_thread_count_does_not_change_the_gradients():
+    x = small(48, structure="packed", doc_min=3, doc_max=9)
+    dout, dlse = _upstream(x, 148)
+    one = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                          positions=x["positions"], n_threads=1)
+    many = oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout, dlse,
+                           positions=x["positions"], n_threads=5)
+    for a, b in zip(one, many):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_magnitudes_bound_the_gradients():
     x = small(46, window=7)
     dout, dlse = _upstream(x, 146)

@@ -70,10 +70,10 @@ def run_gpu_bwd(x, out, lse, dout, dlse):
     return [t.float().cpu().numpy().astype(np.float64) for t in g]
 
 
-def oracle_bwd(x, dout, dlse, row_lo=0, magnitudes=False):
+def oracle_bwd(x, dout, dlse, row_lo=0, row_hi=0, magnitudes=False):
     return oracle.attn_bwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"], dout.double(),
-                           None if dlse is None else dlse.double(), row_lo=row_lo, magnitudes=magnitudes,
-                           **_okw(x))
+                           None if dlse is None else dlse.double(), row_lo=row_lo, row_hi=row_hi,
+                           magnitudes=magnitudes, **_okw(x))
 
 
 def oracle_fwd(x):
@@ -219,31 +219,88 @@ def test_bwd_no_keys_and_no_queries():
     assert torch.all(dk == 0) and torch.all(dv == 0)
 
 
-def test_bwd_full_size_last_rows():
-    """The benchmark's full-causal workload in the launch configuration it times: the last 48
-    query rows (dq, dprofiles, dsink) and the last 48 keys (dk, dv, which only those rows see)
-    against the oracle."""
-    w = W.WORKLOADS["full_causal_8k"]
-    x = W.generate(w)
-    S, n = w.S, 48
-    lo = S - n
-    dout, dlse = _upstream(x, 2400)
-    announce(f"bwd full size {w.name}: last {n} rows")
+def _full_size_ranges(name):
+    """Query-row ranges (lo, hi) of a full-size workload, each with the key range (klo, khi) whose
+    keys no row outside [lo, hi) can see (None: rows only).  Within a range the oracle's dq,
+    dprofiles and dsink are exact; dk and dv are exact on the key range."""
+    w = W.WORKLOADS[name]
+    S = w.S
+    if name == "full_causal_8k":
+        return w, [(0, 512, None), (S - 48, S, (S - 48, S))]
+    if name == "local":
+        # key j is seen by rows j .. j + window - 1
+        lo, hi = 4000, 5100
+        return w, [(0, 256, None), (lo, hi, (lo, hi - w.window + 1)), (S - 48, S, (S - 48, S))]
+    if name == "long":
+        return w, [(0, 256, None), (S - 16, S, (S - 16, S))]
+    if name == "causal_gqa":
+        return w, [(0, S, (0, S))]
+    raise KeyError(name)
+
+
+def _check_full_size(x, w, ranges, seed):
+    S = w.S
+    dout, dlse = _upstream(x, seed)
     d = {k: (x[k].cuda() if isinstance(x.get(k), torch.Tensor) else None) for k in ("q", "k", "v", "profiles",
                                                                                    "sink", "valid", "positions")}
+    announce(f"bwd full size {w.name}: forward")
     out, lse = binding.attn_fwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"],
                                 positions=d["positions"], window=w.window)
-    rows = torch.arange(lo, S, dtype=torch.int64)
-    o_r, l_r, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"],
-                                  positions=x["positions"], window=w.window, rows=rows)
-    out[0, lo:] = torch.from_numpy(o_r).float().cuda()
-    lse[0, lo:] = torch.from_numpy(l_r).float().cuda()
+    # the tested rows take the oracle's out / lse, which isolates the backward
+    for lo, hi, _ in ranges:
+        rows = (torch.arange(w.B)[:, None] * S + torch.arange(lo, hi)[None, :]).reshape(-1)
+        o_r, l_r, _ = oracle.attn_fwd(x["q"], x["k"], x["v"], x["profiles"], x["sink"], x["valid"],
+                                      positions=x["positions"], window=w.window, rows=rows)
+        out[:, lo:hi] = torch.from_numpy(o_r).float().reshape(w.B, hi - lo, w.Hq, w.D).cuda()
+        lse[:, lo:hi] = torch.from_numpy(l_r).float().reshape(w.B, hi - lo, w.Hq).cuda()
+    announce(f"bwd full size {w.name}: backward")
     g = binding.attn_bwd(d["q"], d["k"], d["v"], d["profiles"], d["sink"], d["valid"], out, lse, dout.cuda(),
                          dlse.cuda(), positions=d["positions"], window=w.window)
     torch.cuda.synchronize()
-    got = [t.float().cpu().numpy().astype(np.float64) for t in g]
-    ref = oracle_bwd(x, dout, dlse, row_lo=lo)
-    mag = oracle_bwd(x, dout, dlse, row_lo=lo, magnitudes=True)
-    sel = {"dq": (slice(None), slice(lo, S)), "dk": (slice(None), slice(lo, S)), "dv": (slice(None), slice(lo, S)),
-           "dprofiles": (slice(None), slice(None), slice(lo, S)), "dsink": (slice(None), slice(lo, S))}
-    assert_grads_close(got, ref, mag, w.name, sel=sel)
+    bf16_prof = x["profiles"].dtype == torch.bfloat16
+    for lo, hi, keys in ranges:
+        announce(f"bwd full size {w.name}: oracle rows {lo}..{hi - 1}, keys {keys}")
+        sl = {"dq": (slice(None), slice(lo, hi)), "dprofiles": (slice(None), slice(None), slice(lo, hi)),
+              "dsink": (slice(None), slice(lo, hi))}
+        if keys is not None:
+            sl["dk"] = sl["dv"] = (slice(None), slice(keys[0], keys[1]))
+        names = [n for n in NAMES if n in sl]
+        pick = lambda arrs: [arrs[NAMES.index(n)][sl[n]] for n in names]     # noqa: E731
+        got = [g[NAMES.index(n)][sl[n]].float().cpu().numpy().astype(np.float64) for n in names]
+        ref = pick(oracle_bwd(x, dout, dlse, row_lo=lo, row_hi=hi))
+        mag = pick(oracle_bwd(x, dout, dlse, row_lo=lo, row_hi=hi, magnitudes=True))
+        for n, a, r, m in zip(names, got, ref, mag):
+            bound = REL * m + 1e-30
+            if n == "dprofiles" and bf16_prof:
+                bound = bound + np.abs(r) * 2.0 ** -9
+            err = np.abs(a - r)
+            bad = ~(err <= bound)
+            assert not bad.any(), (f"{w.name} rows {lo}..{hi - 1} {n}: {int(bad.sum())} entries off, first "
+                                   f"{np.argwhere(bad)[:3].tolist()}, max err/M "
+                                   f"{np.nanmax(err / np.maximum(m, 1e-300)):.3g}")
+            zero = (r == 0) & (m == 0)
+            assert np.all(a[zero] == 0), f"{w.name} rows {lo}..{hi - 1} {n}: nonzero where no term exists"
+        del ref, mag
+
+
+@pytest.mark.parametrize("name", ["full_causal_8k", "local", "long", "causal_gqa"])
+def test_bwd_full_size_row_ranges(name):
+    """The full-size workloads in the launch configuration the backward bench times: row ranges
+    at the start, inside and at the end of the sequence (dq, dprofiles, dsink of every row in a
+    range; dk, dv of the keys only that range's rows see) against the oracle.  causal_gqa is
+    compared whole (both batch rows, every row and key)."""
+    w, ranges = _full_size_ranges(name)
+    x = W.generate(w)
+    _check_full_size(x, w, ranges, 2400 + len(name))
+
+
+def test_bwd_full_size_packed_documents():
+    """Packed documents (S = 16384, positions reset per document, last 100 tokens not real): two
+    short documents whole (every row and every key of each, which only its own rows see) and the
+    last 160 rows and keys (across the tail that is not real)."""
+    w = W.WORKLOADS["packed"]
+    x = W.generate(w)
+    st = list(x["doc_starts"][0]) + [w.S]
+    docs = sorted(((st[n + 1] - st[n], st[n], st[n + 1]) for n in range(len(st) - 1)))[:2]
+    ranges = [(a, b, (a, b)) for _, a, b in docs] + [(w.S - 160, w.S, (w.S - 160, w.S))]
+    _check_full_size(x, w, ranges, 2500)
