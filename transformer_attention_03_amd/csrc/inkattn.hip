@@ -985,28 +985,53 @@ void attn_fwd_kernel(FwdParams p)
                     *(const f16x8*)(vbp + (vb ^ (32u * c)) + db * 32 * 128), pbp[c], oacc[db], 0, 0, 0);
     }
 
-    // ---- epilogue
+    // ---- epilogue.  fp32 rows leave through this wave's bias strip, free now:
+    // the wave writes its normalised O^T there as rows of D / 2 columns (16-byte
+    // chunks XOR-swizzled by row), reads them back a row run per 16 lanes and
+    // stores 4 whole rows of 256 bytes per instruction (the accumulator layout
+    // would store 32 rows x 32 bytes).  Half of D per pass (8 KB).
     const float l_tot = half_sum(l);
-    if (!qin) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const long long oo = b * p.o_bs + (long long)i * p.o_ts + h * p.o_hs;
+    if (!p.out_bf16) {
+        __builtin_amdgcn_s_waitcnt(WAIT_VM_LGKM);   // no DMA into the strip outstanding, no read of it
+        const int rows_here = qb < p.nQB ? min(BM, p.Sq - i0) : 0;
+        const unsigned ln = opaque((unsigned)lane);
+        float* const orow = (float*)p.out + b * p.o_bs + (long long)i0 * p.o_ts + h * p.o_hs;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+        for (int hp = 0; hp < NDB / 2; ++hp) {
+            // lane (qi, hh) holds columns 64 hp + 32 dbl + 8 jj + 4 hh + 0..3 of row qi: chunk 8 dbl + 2 jj + hh
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            f32x4 w;
+            for (int dbl = 0; dbl < 2; ++dbl)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * jj + e] * inv;
-            const int d0 = 32 * db + 8 * jj + 4 * hh;
-            if (p.out_bf16) {
+                for (int jj = 0; jj < 4; ++jj) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = oacc[2 * hp + dbl][4 * jj + e] * inv;
+                    const unsigned c = 8u * dbl + 2u * jj + (ln >> 5);
+                    *(f32x4*)(bstrip + (ln & 31u) * 256u + 16u * (c ^ (ln & 15u))) = w;
+                }
+            // instruction u: row 4 u + lane / 16, chunk lane % 16
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const unsigned r = 4u * u + (ln >> 4), c = ln & 15u;
+                const f32x4 w = *(const f32x4*)(bstrip + r * 256u + 16u * (c ^ (r & 15u)));
+                if ((int)r < rows_here) *(f32x4*)(orow + (long long)r * p.o_ts + 64 * hp + 4 * (int)c) = w;
+            }
+            __builtin_amdgcn_s_waitcnt(WAIT_LGKM);   // read back before the next pass rewrites the strip
+        }
+    }
+    if (!qin) return;
+    if (p.out_bf16) {
+        const long long oo = b * p.o_bs + (long long)i * p.o_ts + h * p.o_hs;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
                 bf16x4 wb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) wb[e] = (__bf16)w[e];   // round to nearest even
-                *(bf16x4*)((__bf16*)p.out + oo + d0) = wb;
-            } else {
-                *(f32x4*)((float*)p.out + oo + d0) = w;
+                for (int e = 0; e < 4; ++e) wb[e] = (__bf16)(oacc[db][4 * jj + e] * inv);   // round to nearest even
+                *(bf16x4*)((__bf16*)p.out + oo + 32 * db + 8 * jj + 4 * hh) = wb;
             }
-        }
     }
     if (hh == 0 && p.lse) {
         float lse;
