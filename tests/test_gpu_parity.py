@@ -65,6 +65,12 @@ SMALL = {
     "E5_rows_near_end": lambda: W.custom(B=1, S=100, Hq=4, Hkv=2, D=64, E=5, seed=116),
     "bf16_E3_rows_near_end": lambda: W.custom(B=1, S=129, Hq=4, Hkv=1, D=128, E=3, seed=117,
                                               profiles_dtype=torch.bfloat16),
+    # more workgroups than two per CU: 531 (59 batch rows x 9 heads, not a multiple of the
+    # 8 XCDs) and 544 (17 batch rows x 8 K/V heads x 4 query groups, G = 4, documents, window)
+    "items_531_G1_D64": lambda: W.custom(B=59, S=256, Hq=9, Hkv=9, D=64, E=40, seed=118,
+                                         structure="tail_pad", max_tail_pad=60),
+    "items_544_G4_D128": lambda: W.custom(B=17, S=256, Hq=32, Hkv=8, D=128, E=100, seed=119, window=150,
+                                          structure="packed", doc_min=20, doc_max=120, invalid_tail=9),
 }
 
 
