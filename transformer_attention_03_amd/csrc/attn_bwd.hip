@@ -229,6 +229,55 @@ __device__ __forceinline__ void store_grad(void* prow, int r, float x)
     else ((float*)prow)[r] = x;
 }
 
+// N (4 or 8) transposing LDS reads (ds_read_b64_tr_b16) at the LDS byte addresses
+// a[], and the wait for them, in one asm block.  Through the builtin, the
+// compiler puts a wait for every outstanding vector-memory instruction before
+// each such read (it cannot tell the read from the LDS the DMA is still
+// writing), which would hold the DMA sent ahead for later tiles; the reads
+// here only touch data whose DMA has landed.  The outputs are written when the
+// block ends (its own wait), and none overlaps an address (early clobber).
+template <int N>
+__device__ __forceinline__ void tr_read(s16x4 (&r)[N], const unsigned (&a)[N])
+{
+    static_assert(N == 4 || N == 8, "four or eight reads");
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (N == 4) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4\n\t"
+            "ds_read_b64_tr_b16 %1, %5\n\t"
+            "ds_read_b64_tr_b16 %2, %6\n\t"
+            "ds_read_b64_tr_b16 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+            : "memory");
+        return;
+    } else
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+#else
+    for (int x = 0; x < N; ++x) r[x] = s16x4{};
+    (void)a;
+#endif
+}
+
+// LDS byte address of a pointer into the workgroup's shared memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p)
+{
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // ---------------------------------------------------------------------------
 // dQ and the profile gradients.  One workgroup of 8 waves per (batch row, K/V
 // head, head chunk, group of 32-query blocks), the forward's decomposition
@@ -632,16 +681,24 @@ void bwd_dq_kernel(BwdParams p)
         // ---- dQ^T += K^T dS^T over this wave's key half (16-key steps
         // 2 kh, 2 kh + 1), K^T read from the K rows
         const unsigned tln = opaque((unsigned)lane);
+        const unsigned stl = lds_addr(st);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < 2; ++c2) {
+            unsigned ad[2 * NDB];
+            s16x4 rd[2 * NDB];
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + trof(tln, c2, 0, db)));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + trof(tln, c2, 1, db)));
-                const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                ad[2 * db] = stl + trof(tln, c2, 0, db);
+                ad[2 * db + 1] = stl + trof(tln, c2, 1, db);
+            }
+            tr_read<2 * NDB>(rd, ad);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const s16x8 a8 = __builtin_shufflevector(rd[2 * db], rd[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                 dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pd[c2],
                                                                    dqacc[db], 0, 0, 0);
             }
+        }
 
         // this wave's DMA of the next tile has landed (the bias DMA of the
         // tile two ahead and this tile's profile-gradient stores, issued after
@@ -1106,17 +1163,25 @@ void bwd_dkdv_kernel(BwdParams p)
             // ---- dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves); the
             // transposed operands come from the rows by transposing LDS reads
             {
-                const char* rows = st + (role ? Q_OFF : DO_OFF);
+                const unsigned rl = lds_addr(st + (role ? Q_OFF : DO_OFF));
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+                for (int c = 0; c < 2; ++c) {
+                    unsigned ad[2 * NDB];
+                    s16x4 rd[2 * NDB];
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + trof[c][0][db]));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + trof[c][1][db]));
+                        ad[2 * db] = rl + (unsigned)trof[c][0][db];
+                        ad[2 * db + 1] = rl + (unsigned)trof[c][1][db];
+                    }
+                    tr_read<2 * NDB>(rd, ad);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const s16x4 lo = rd[2 * db], hi = rd[2 * db + 1];
                         const bf16x8 a =
                             __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[db], 0, 0, 0);
                     }
+                }
             }
         }
         asm volatile("" ::: "memory");
