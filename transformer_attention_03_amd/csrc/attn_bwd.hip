@@ -272,10 +272,178 @@ __device__ __forceinline__ void tr_read(s16x4 (&r)[N], const unsigned (&a)[N])
 #endif
 }
 
+// The same for N (4 or 8) 16-byte LDS reads at the byte addresses a[].
+template <int N>
+__device__ __forceinline__ void lds_read16(bf16x8 (&r)[N], const unsigned (&a)[N])
+{
+    static_assert(N == 4 || N == 8, "four or eight reads");
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (N == 4) {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\t"
+            "ds_read_b128 %1, %5\n\t"
+            "ds_read_b128 %2, %6\n\t"
+            "ds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %12\n\t"
+            "ds_read_b128 %5, %13\n\t"
+            "ds_read_b128 %6, %14\n\t"
+            "ds_read_b128 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+            : "memory");
+    }
+#else
+    for (int x = 0; x < N; ++x) r[x] = bf16x8{};
+    (void)a;
+#endif
+}
+
+// Eight 16-byte LDS reads at a + 64 jj + 16 h (jj < 4, h < 2; r[2 jj + h]): the
+// per-row pairs (statistics or query descriptors) of one wave half's 16 rows.
+__device__ __forceinline__ void lds_read_pairs(f32x4 (&r)[8], unsigned a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:16\n\t"
+        "ds_read_b128 %2, %8 offset:64\n\t"
+        "ds_read_b128 %3, %8 offset:80\n\t"
+        "ds_read_b128 %4, %8 offset:128\n\t"
+        "ds_read_b128 %5, %8 offset:144\n\t"
+        "ds_read_b128 %6, %8 offset:192\n\t"
+        "ds_read_b128 %7, %8 offset:208\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a)
+        : "memory");
+#else
+    for (int x = 0; x < 8; ++x) r[x] = f32x4{};
+    (void)a;
+#endif
+}
+
+// Sixteen bias entries of a strip, r[4 jj + e] at a + (8 jj + 2 e) * RUNB:
+// 4-byte entries (fp32 profiles, RUNB 128) or 2-byte ones, zero-extended
+// (bf16, RUNB 64).
+template <bool PB>
+__device__ __forceinline__ void lds_read_bias(unsigned (&r)[16], unsigned a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (!PB) {
+        asm volatile(
+            "ds_read_b32 %0, %16\n\t"
+            "ds_read_b32 %1, %16 offset:256\n\t"
+            "ds_read_b32 %2, %16 offset:512\n\t"
+            "ds_read_b32 %3, %16 offset:768\n\t"
+            "ds_read_b32 %4, %16 offset:1024\n\t"
+            "ds_read_b32 %5, %16 offset:1280\n\t"
+            "ds_read_b32 %6, %16 offset:1536\n\t"
+            "ds_read_b32 %7, %16 offset:1792\n\t"
+            "ds_read_b32 %8, %16 offset:2048\n\t"
+            "ds_read_b32 %9, %16 offset:2304\n\t"
+            "ds_read_b32 %10, %16 offset:2560\n\t"
+            "ds_read_b32 %11, %16 offset:2816\n\t"
+            "ds_read_b32 %12, %16 offset:3072\n\t"
+            "ds_read_b32 %13, %16 offset:3328\n\t"
+            "ds_read_b32 %14, %16 offset:3584\n\t"
+            "ds_read_b32 %15, %16 offset:3840\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+              "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+            : "v"(a)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_u16 %0, %16\n\t"
+            "ds_read_u16 %1, %16 offset:128\n\t"
+            "ds_read_u16 %2, %16 offset:256\n\t"
+            "ds_read_u16 %3, %16 offset:384\n\t"
+            "ds_read_u16 %4, %16 offset:512\n\t"
+            "ds_read_u16 %5, %16 offset:640\n\t"
+            "ds_read_u16 %6, %16 offset:768\n\t"
+            "ds_read_u16 %7, %16 offset:896\n\t"
+            "ds_read_u16 %8, %16 offset:1024\n\t"
+            "ds_read_u16 %9, %16 offset:1152\n\t"
+            "ds_read_u16 %10, %16 offset:1280\n\t"
+            "ds_read_u16 %11, %16 offset:1408\n\t"
+            "ds_read_u16 %12, %16 offset:1536\n\t"
+            "ds_read_u16 %13, %16 offset:1664\n\t"
+            "ds_read_u16 %14, %16 offset:1792\n\t"
+            "ds_read_u16 %15, %16 offset:1920\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+              "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+            : "v"(a)
+            : "memory");
+    }
+#else
+    for (int x = 0; x < 16; ++x) r[x] = 0u;
+    (void)a;
+#endif
+}
+
+// Two 16-byte LDS reads at a and a + 1024.
+__device__ __forceinline__ void lds_read_two(bf16x8& r0, bf16x8& r1, unsigned a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1)
+        : "v"(a)
+        : "memory");
+#else
+    r0 = bf16x8{};
+    r1 = bf16x8{};
+    (void)a;
+#endif
+}
+
 // LDS byte address of a pointer into the workgroup's shared memory.
 __device__ __forceinline__ unsigned lds_addr(const void* p)
 {
     return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One LDS DMA (buffer_load ... lds) of SIZE bytes per lane (16, 4 or 2) from
+// the buffer rsrc at the lane's byte offset voff into the LDS from byte lds
+// on (lane l at lds + SIZE l), in an asm block: the compiler does not see an
+// LDS write it cannot place, so it adds no wait for it before later LDS reads
+// or writes of registers (through the builtin it waited for every DMA in
+// flight there).  Every read of DMA'd data follows an explicit vmcnt wait and
+// a barrier; the compiler's own vmcnt counts only grow stricter with DMAs it
+// does not count (they complete in order).  The compiler's hazard pass does
+// not look inside the block, so it begins with the wait states its sources
+// may need: one after the M0 write the compiler puts right before it, five
+// after a VALU write of an SGPR it reads (v_readlane restoring a spilled
+// buffer resource, for one).
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsigned lds, unsigned voff)
+{
+    static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "16, 4 or 2 bytes per lane");
+#if defined(__HIP_DEVICE_COMPILE__)
+    const unsigned m = __builtin_amdgcn_readfirstlane(lds);
+    if constexpr (SIZE == 16)
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(m) : "memory");
+    else if constexpr (SIZE == 4)
+        asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(m) : "memory");
+    else
+        asm volatile("s_nop 4\n\tbuffer_load_ushort %0, %1, 0 offen lds" :: "v"(voff), "s"(rsrc), "{m0}"(m) : "memory");
+#else
+    (void)rsrc; (void)lds; (void)voff;
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -446,11 +614,11 @@ void bwd_dq_kernel(BwdParams p)
             // (whole offsets in the register operand: the range check, which
             // turns rows past Sk into zeros, applies to it)
             const unsigned kvo = ((unsigned)j0 + r) * krow + 16u * ((ln % CH) ^ (unsigned)row_swz<D>((int)r));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(st + K_OFF + 1024 * a), 16, kvo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(st + V_OFF + 1024 * a), 16, kvo, 0, 0, 0);
+            dma_to_lds<16>(krs, lds_addr(st + K_OFF + 1024 * a), kvo);
+            dma_to_lds<16>(vrs, lds_addr(st + V_OFF + 1024 * a), kvo);
         }
         const unsigned cao = (unsigned)j0 * 4u + 4u * ln;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kas, (lds_void*)(st + CA_OFF), 4, cao, 0, 0, 0);
+        dma_to_lds<4>(kas, lds_addr(st + CA_OFF), cao);
     };
     // This wave's bias of tile kt goes by DMA into a strip of the wave, two
     // tiles ahead of its use.  Entry (jj, e) of a lane is distance rb + e with
@@ -472,16 +640,14 @@ void bwd_dq_kernel(BwdParams p)
             // (entry offsets kept opaque: they may wrap modulo 2^32 like the run's start)
             const unsigned off = (rowe + gb - 8u * (unsigned)jj) * (unsigned)ES;
             if (!PB && bc == BC_FULL) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 1024 * jj), 16, opaque(off), 0, 0, 0);
+                dma_to_lds<16>(prs, (unsigned)(size_t)(sp + 1024 * jj), opaque(off));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (PB)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 256 * (4 * jj + e)), 2,
-                                                                 opaque(off + 2u * e), 0, 0, 0);
+                        dma_to_lds<2>(prs, (unsigned)(size_t)(sp + 256 * (4 * jj + e)), opaque(off + 2u * e));
                     else
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(sp + 256 * (4 * jj + e)), 4,
-                                                                 opaque(off + 4u * e), 0, 0, 0);
+                        dma_to_lds<4>(prs, (unsigned)(size_t)(sp + 256 * (4 * jj + e)), opaque(off + 4u * e));
                 }
             }
         }
@@ -933,8 +1099,8 @@ void bwd_dkdv_kernel(BwdParams p)
             const __amdgpu_buffer_rsrc_t qrs = uniform_rsrc(p.q + qbase + (long long)h * D, qnrec);
             const __amdgpu_buffer_rsrc_t drs = uniform_rsrc(p.dob + qbase + (long long)h * D, qnrec);
             const unsigned vo = qv + (unsigned)i0 * qrow;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(st + Q_OFF + 1024 * wave), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (lds_void*)(st + DO_OFF + 1024 * wave), 16, vo, 0, 0, 0);
+            dma_to_lds<16>(qrs, lds_addr(st + Q_OFF + 1024 * wave), vo);
+            dma_to_lds<16>(drs, lds_addr(st + DO_OFF + 1024 * wave), vo);
             n += 2;
         }
         if (wave < 2) {
@@ -944,7 +1110,7 @@ void bwd_dkdv_kernel(BwdParams p)
                 wave ? uniform_rsrc(p.qinfo + (size_t)b * p.Sq, (size_t)p.Sq * 8)
                      : uniform_rsrc(p.rowstat + ((size_t)b * p.Hq + h) * p.Sq, (size_t)p.Sq * 8);
             const unsigned vo = (unsigned)i0 * 8u + 4u * (unsigned)lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void*)(st + (wave ? QI_OFF : RS_OFF)), 4, vo, 0, 0, 0);
+            dma_to_lds<4>(xrs, lds_addr(st + (wave ? QI_OFF : RS_OFF)), vo);
             n += 1;
         }
         if (role == 0 && bias_class(x) != BC_NONE) {
@@ -957,7 +1123,7 @@ void bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
             for (int k = 0; k < NBI; ++k) {
                 const unsigned vo = opaque(base + bvo[k]);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(prs, (lds_void*)(bs + 1024 * k), 16, vo, 0, 0, 0);
+                dma_to_lds<16>(prs, lds_addr(bs + 1024 * k), vo);
             }
             n += NBI;
         }
@@ -1015,6 +1181,12 @@ void bwd_dkdv_kernel(BwdParams p)
     prv.code = 0;
     prv.hs = 0;
     int n_flight = 0;   // DMA instructions of the last stage requested
+#if defined(__HIP_DEVICE_COMPILE__)
+    // the K / V operands and the other loads above have landed: the compiler
+    // then keeps no wait for them inside the loop (where it would also wait
+    // for the stage DMA in flight)
+    __builtin_amdgcn_s_waitcnt(0);
+#endif
     if (cur.x >= 0) {
         issue(cur.x, g * p.G + cur.hs, 0);
         const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads)
@@ -1058,11 +1230,13 @@ void bwd_dkdv_kernel(BwdParams p)
             // ---- S (P waves) or dP (dS waves): A operands are the Q or dO rows
             f32x16 sacc;
             {
-                const char* rows = st + (role ? DO_OFF : Q_OFF);
+                const unsigned rows = lds_addr(st + (role ? DO_OFF : Q_OFF));
                 bf16x8 ar[NKK];
+                unsigned aa[NKK];
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk)
-                    ar[kk] = *(const bf16x8*)(rows + kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl)));
+                    aa[kk] = rows + (unsigned)(kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl)));
+                lds_read16<NKK>(ar, aa);
                 sacc = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk)
@@ -1078,38 +1252,61 @@ void bwd_dkdv_kernel(BwdParams p)
                 auto body = [&](auto bct, auto mt) {
                     constexpr int BCT = decltype(bct)::value;
                     constexpr bool MASKED = decltype(mt)::value;
+                    // (the stage's row statistics, query descriptors and bias runs, read
+                    // in asm blocks: see lds_read16)
+                    f32x4 rsv[8];
+                    lds_read_pairs(rsv, lds_addr(rsl) + 32u * (unsigned)hh);
+                    f32x4 qiv[8];
+                    if constexpr (MASKED) lds_read_pairs(qiv, lds_addr(qil) + 32u * (unsigned)hh);
+                    unsigned bvr[16];
+                    if constexpr (BCT != BC_NONE) lds_read_bias<PB>(bvr, lds_addr(bsl) + (unsigned)(hh * RUNB));
+                    // A run that starts before the block reads as 0 from a DMA piece at
+                    // a wrapped offset: the block's first 8 entries are loaded here.  Only
+                    // the rows of a block with i0 E < 8 can hold them (a uniform test);
+                    // the loads are waited for inside the branch, so that no wait for
+                    // them (which would also wait for the stage DMA) sits on other paths.
+                    if constexpr (BCT == BC_EDGE) {
+                        if (i0 * p.E < 8) {
+                            const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int m0 = 8 * jj + 4 * hh;
+                                    const int r = p.qoff + i0 + m0 + e - j;
+                                    const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
+                                    if (ent < 8 && (unsigned)r < (unsigned)p.E)
+                                        bvr[4 * jj + e] = PB ? (unsigned)((const unsigned short*)pr0)[ent]
+                                                             : ((const unsigned*)pr0)[ent];
+                                }
+#if defined(__HIP_DEVICE_COMPILE__)
+                            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#endif
+                        }
+                    }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int m0 = 8 * jj + 4 * hh;
-                        const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
-                        const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+                        const f32x4 rs01 = rsv[2 * jj];
+                        const f32x4 rs23 = rsv[2 * jj + 1];
                         i32x4 qi01, qi23;
                         if constexpr (MASKED) {
-                            qi01 = *(const i32x4*)(qil + 2 * m0);
-                            qi23 = *(const i32x4*)(qil + 2 * m0 + 4);
+                            qi01 = __builtin_bit_cast(i32x4, qiv[2 * jj]);
+                            qi23 = __builtin_bit_cast(i32x4, qiv[2 * jj + 1]);
                         }
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
                             float pre = -lse2;
                             if constexpr (BCT != BC_NONE) {
-                                const int slot = 8 * jj + 2 * e + hh;
                                 float bias;
                                 if constexpr (PB)
-                                    bias = __uint_as_float((unsigned)*(const unsigned short*)(bsl + slot * RUNB) << 16);
+                                    bias = __uint_as_float(bvr[4 * jj + e] << 16);
                                 else
-                                    bias = *(const float*)(bsl + slot * RUNB);
+                                    bias = __uint_as_float(bvr[4 * jj + e]);
                                 if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
                                 if constexpr (BCT == BC_EDGE) {
                                     const int r = p.qoff + i0 + m0 + e - j;
-                                    // a run that starts before the block reads as 0 from a DMA
-                                    // piece at a wrapped offset: the block's first 8 entries are
-                                    // loaded here (first query blocks only)
-                                    const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
-                                    if (ent < 8 && (unsigned)r < (unsigned)p.E) {
-                                        const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
-                                        bias = PB ? (float)((const __bf16*)pr0)[ent] : ((const float*)pr0)[ent];
-                                    }
                                     pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
                                 }
                             }
@@ -1143,13 +1340,14 @@ void bwd_dkdv_kernel(BwdParams p)
                 // ---- dS = P (dP - (Delta - dlse)); dO (so dP) is 0 on rows that
                 // are not real or lie past Sq, and V on keys that are not real, so
                 // dP is finite everywhere and P = 0 masks dS
-                const bf16x8 p0 = *(const bf16x8*)(xp);
-                const bf16x8 p1 = *(const bf16x8*)(xp + 1024);
+                bf16x8 p0, p1;
+                lds_read_two(p0, p1, lds_addr(xp));
+                f32x4 rsv[8];
+                lds_read_pairs(rsv, lds_addr(rsl) + 32u * (unsigned)hh);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int m0 = 8 * jj + 4 * hh;
-                    const f32x4 rs01 = *(const f32x4*)(rsl + 2 * m0);
-                    const f32x4 rs23 = *(const f32x4*)(rsl + 2 * m0 + 4);
+                    const f32x4 rs01 = rsv[2 * jj];
+                    const f32x4 rs23 = rsv[2 * jj + 1];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
