@@ -99,6 +99,11 @@ struct BwdParams {
 // 16 consecutive rows read at one logical chunk hit 16 distinct groups of 4
 // banks, and so do 4 consecutive rows read at 4 consecutive logical chunks
 // (the pattern of a transposing read).
+// Slot permutation of the 16-byte chunks of a 128-byte whole-run row in a
+// bias strip: rows 2 apart start their chunks at different slots, so that 16
+// consecutive rows read at one chunk index hit distinct banks.
+__device__ __forceinline__ unsigned run_swz(unsigned r) { return (r >> 1) & 7u; }
+
 template <int D> __device__ __forceinline__ int row_swz(int r)
 {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
@@ -620,13 +625,29 @@ void bwd_dq_kernel(BwdParams p)
         const unsigned cao = (unsigned)j0 * 4u + 4u * ln;
         dma_to_lds<4>(kas, lds_addr(st + CA_OFF), cao);
     };
-    // This wave's bias of tile kt goes by DMA into a strip of the wave, two
-    // tiles ahead of its use.  Entry (jj, e) of a lane is distance rb + e with
-    // rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).  Whole runs (BC_FULL, fp32):
-    // one 16-byte run per jj, lane-major (bytes 1024 jj + 16 l); otherwise one
-    // entry per instruction, lane-major per (jj, e) (bytes 256 (4 jj + e) + 4 l;
-    // a bf16 entry lands zero-extended in its dword).  Returns the class; the
-    // instructions issued are bias_dmas(class).
+    // This wave's bias of tile kt goes by DMA into a strip of the wave, about
+    // two tiles ahead of its use.  Entry (jj, e) of a lane is distance rb + e
+    // with rb = gi - (j0 + 32 kh + 8 jj + 4 hh + 3).  Whole runs (BC_FULL,
+    // fp32): row qi of the wave's 32 x 32 block needs the 32 distances from
+    // gi - (j0 + 32 kh + 31) up, 128 contiguous bytes of its profile row; the
+    // strip holds them row-major (128 bytes per row), its 16-byte chunk c at
+    // slot c ^ run_swz(qi), and one instruction fetches 8 whole rows (lane l
+    // of instruction a: row 8 a + l / 8, slot l % 8), so that every request
+    // covers whole runs of a row rather than 32 bytes of each of 32 rows.
+    // Otherwise one entry per instruction, lane-major per (jj, e) (bytes
+    // 256 (4 jj + e) + 4 l; a bf16 entry lands zero-extended in its dword).
+    // Returns the class; the instructions issued are bias_dmas(class).
+    // Byte offset, in the profile (or gradient) block of the head, of the 16
+    // bytes that lane ln moves in whole-run instruction a of the tile at key
+    // column j0: row r = 8 a + ln / 8 of the wave's block, its run chunk
+    // (ln % 8) ^ run_swz(r); past the buffer (dropped) for rows past Sq.
+    auto run_off = [&](unsigned ln, int a, int j0t) -> unsigned {
+        const unsigned r = 8u * (unsigned)a + ln / 8u;
+        const unsigned c = (ln % 8u) ^ run_swz(r);
+        const int row = i0 + (int)r;
+        const unsigned d0 = (unsigned)(p.qoff + row - (j0t + 32 * kh + 31));   // the run's first distance
+        return row < p.Sq ? ((unsigned)row * (unsigned)p.E + d0) * 4u + 16u * c : 0xFFFFFFF0u;
+    };
     auto bias_dma = [&](int kt, char* strip) -> int {
         if (kt < 0 || kt < kt_split) return BC_NONE;
         const int j0 = kt * BN;
@@ -634,14 +655,18 @@ void bwd_dq_kernel(BwdParams p)
         if (bc == BC_NONE) return BC_NONE;
         lds_char* const sp = opaque_lds((lds_char*)strip);
         const unsigned ln = opaque((unsigned)lane);
+        if (!PB && bc == BC_FULL) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                dma_to_lds<16>(prs, (unsigned)(size_t)(sp + 1024 * a), run_off(ln, a, j0));
+            return bc;
+        }
         const unsigned gb = (unsigned)gi - (unsigned)(j0 + 32 * kh + 3) - 4u * (ln >> 5);   // rb + 8 jj
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             // (entry offsets kept opaque: they may wrap modulo 2^32 like the run's start)
             const unsigned off = (rowe + gb - 8u * (unsigned)jj) * (unsigned)ES;
-            if (!PB && bc == BC_FULL) {
-                dma_to_lds<16>(prs, (unsigned)(size_t)(sp + 1024 * jj), opaque(off));
-            } else {
+            {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (PB)
@@ -699,14 +724,16 @@ void bwd_dq_kernel(BwdParams p)
         const char* st = smem + buf * STAGE;
         char* const strip = bstrip0 + par * (NW * BSW);
         // ---- this tile's bias out of its strip (it landed by the end of the
-        // iteration before), so that the strip takes the tile two ahead
+        // iteration before); entries (jj, 0..3) of a whole run are chunk
+        // 7 - 2 jj - hh of row qi
         f32x4 bv[4];
+        const unsigned rslot = 128u * (unsigned)qi + 16u * ((7u - (unsigned)hh) ^ run_swz((unsigned)qi));
         if constexpr (WB) {
             if (bc != BC_NONE) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     if (!PB && bc == BC_FULL) {
-                        bv[jj] = *(const f32x4*)(strip + jj * 1024 + 16 * lane);
+                        bv[jj] = *(const f32x4*)(strip + (rslot ^ (32u * (unsigned)jj)));
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -716,16 +743,11 @@ void bwd_dq_kernel(BwdParams p)
                     }
                 }
             }
-#if defined(__HIP_DEVICE_COMPILE__)
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // (lgkmcnt(0)) read before the DMA below rewrites it
-#endif
         }
         asm volatile("" ::: "memory");
         // (buffer buf ^ 1 was last read before the barrier that ended the
         // previous iteration)
         if (nxt.x >= 0) stage_load(nxt.x, buf ^ 1);
-        asm volatile("" ::: "memory");
-        const int nbc2 = bias_dma(nx2.x, strip);
         asm volatile("" ::: "memory");
 
         // ---- S^T = K Q^T and dP^T = V dO^T for this wave's key half, keys
@@ -799,18 +821,17 @@ void bwd_dq_kernel(BwdParams p)
                     // profile gradients: stores outside this query's row [0, E)
                     // get an offset past the buffer and are dropped
                     if constexpr (BCT == BC_FULL) {
-                        const unsigned off = qin ? (rowe + (unsigned)rb) * (unsigned)ES : 0xFFFFFFF0u;
                         if constexpr (PB) {
+                            const unsigned off = qin ? (rowe + (unsigned)rb) * (unsigned)ES : 0xFFFFFFF0u;
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 __builtin_amdgcn_raw_buffer_store_b16(
                                     (unsigned short)(__float_as_uint((float)(__bf16)dz[e]) >> 16), drs,
                                     opaque(off + 2u * e), 0, 0);
                         } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                i32x4{__float_as_int(dz[0]), __float_as_int(dz[1]), __float_as_int(dz[2]),
-                                      __float_as_int(dz[3])},
-                                drs, off, 0, 0);
+                            // into the strip, in the whole-run layout of the bias
+                            // (its entries were read at the start of the step)
+                            *(f32x4*)(strip + (rslot ^ (32u * (unsigned)jj))) = dz;
                         }
                     } else if constexpr (BCT == BC_EDGE) {
 #pragma unroll
@@ -823,6 +844,19 @@ void bwd_dq_kernel(BwdParams p)
                             else
                                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dz[e]), drs, off, 0, 0);
                         }
+                    }
+                }
+                if constexpr (BCT == BC_FULL && !PB) {
+                    // whole runs back out of the strip, 8 rows per store (the
+                    // wave's own LDS writes above precede these reads)
+                    const unsigned ln = opaque((unsigned)lane);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x4 w = *(const f32x4*)(strip + 1024 * a + 16 * lane);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            i32x4{__float_as_int(w[0]), __float_as_int(w[1]), __float_as_int(w[2]),
+                                  __float_as_int(w[3])},
+                            drs, run_off(ln, a, j0), 0, 0);
                     }
                 }
             }
@@ -842,6 +876,10 @@ void bwd_dq_kernel(BwdParams p)
             else if (bc == BC_FULL) body(FULL{}, T{});
             else body(EDGE{}, T{});
         }
+        asm volatile("" ::: "memory");
+        // the strip takes the bias of the tile two ahead (this tile's entries
+        // and gradients are out of it: the stores above took their data)
+        const int nbc2 = bias_dma(nx2.x, strip);
         asm volatile("" ::: "memory");
 
         // ---- dQ^T += K^T dS^T over this wave's key half (16-key steps
