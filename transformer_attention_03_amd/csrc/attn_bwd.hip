@@ -1063,10 +1063,22 @@ void bwd_dkdv_kernel(BwdParams p)
         (qhi_col >= 0 && qhi_col >= p.qoff) ? min(p.nQB - 1, (qhi_col - p.qoff) / BM) : -1);
     // Query blocks are walked from the last down to the first, so that the
     // workgroups on one XCD (one K/V head) stream the same query tiles at
-    // about the same time and share them in L2.  Candidate c is block qb_hi - c.
+    // about the same time and share them in L2: without a window every range
+    // ends at the last block (or its document's), candidate c is block
+    // qb_hi - c.  With a window the ranges end at different blocks, so the
+    // descending walk is rotated to start at the block congruent to nQB - 1
+    // modulo the range's length: workgroups whose ranges have one length
+    // (every key block away from the sequence's ends) then meet each shared
+    // block at the same candidate.
+    const int nblk = qb_hi - qb_lo + 1;
+    const int rot = (p.window > 0 && nblk > 0) ? (p.nQB - 1 - qb_lo) % nblk : nblk - 1;
+    auto blk = [&](int c) -> int {   // c in [0, nblk)
+        const int t = rot - c;
+        return qb_lo + (t >= 0 ? t : t + nblk);
+    };
     auto classify = [&](int c) -> int {
-        const int x = qb_hi - c;
-        if (x < qb_lo) return -1;
+        if (c >= nblk) return -1;
+        const int x = blk(c);
         const TileSummary qs = p.qsum[(size_t)b * p.nQB + x];
         const int xc = min(BM, p.Sq - x * BM);
         const int xlo = p.qoff + x * BM;
@@ -1194,7 +1206,7 @@ void bwd_dkdv_kernel(BwdParams p)
     auto next_block = [&]() -> It {
         const int2 e = next_entry(sch, qb_hi - qb_lo, classify);
         It r;
-        r.x = e.x >= 0 ? qb_hi - e.x : -1;
+        r.x = e.x >= 0 ? blk(e.x) : -1;
         r.code = e.y;
         r.hs = 0;
         return r;
