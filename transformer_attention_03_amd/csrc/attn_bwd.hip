@@ -109,6 +109,21 @@ template <int D> __device__ __forceinline__ int row_swz(int r)
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((r >> 1) & 7);
 }
 
+// Transposing reads of staged rows (D = 128: pitch 256 bytes, chunks placed by
+// row_swz): lane ln reads 8 bytes of row 16 c + 8 hi + 4 (ln / 32) +
+// (ln % 16) / 4 at the columns 32 db + 16 ((ln / 16) % 2) + 4 (ln % 4).  With
+// t = (ln / 4) % 4 and y = 2 ((ln / 16) % 2) + (ln / 2) % 2 the row's swizzle
+// is 4 t + 2 hi + ln / 32 and the column chunk 4 db + y, so the byte offset is
+// 4096 c + 2048 hi + 1024 (ln / 32) + 256 t + 64 (db ^ t) + 16 (y ^ (ln / 32)
+// ^ 2 hi) + 8 (ln % 2) = (tr_base128(ln) + 2048 hi) ^ (64 db + 32 hi) + 4096 c:
+// c, hi and db enter as constants (the XOR only touches bits 4..7, which the
+// row terms and a row base that is a multiple of 256 leave clear).
+__device__ __forceinline__ unsigned tr_base128(unsigned ln)
+{
+    const unsigned hh = ln >> 5, t = (ln >> 2) & 3u, y = 2u * ((ln >> 4) & 1u) + ((ln >> 1) & 1u);
+    return 1024u * hh + 320u * t + 16u * (y ^ hh) + 8u * (ln & 1u);
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics, bf16 dout, query descriptors.  TPR = D / 4 threads per
 // (batch row, query, head) row.
@@ -241,35 +256,38 @@ __device__ __forceinline__ void store_grad(void* prow, int r, float x)
 // writing), which would hold the DMA sent ahead for later tiles; the reads
 // here only touch data whose DMA has landed.  The outputs are written when the
 // block ends (its own wait), and none overlaps an address (early clobber).
-template <int N>
+// OFF (a multiple of 8 below 65536) is added to every address by the
+// instructions' offset field.
+template <int N, int OFF = 0>
 __device__ __forceinline__ void tr_read(s16x4 (&r)[N], const unsigned (&a)[N])
 {
     static_assert(N == 4 || N == 8, "four or eight reads");
+    static_assert(OFF >= 0 && OFF < 65536 && OFF % 8 == 0, "offset field");
 #if defined(__HIP_DEVICE_COMPILE__)
     if constexpr (N == 4) {
         asm volatile(
-            "ds_read_b64_tr_b16 %0, %4\n\t"
-            "ds_read_b64_tr_b16 %1, %5\n\t"
-            "ds_read_b64_tr_b16 %2, %6\n\t"
-            "ds_read_b64_tr_b16 %3, %7\n\t"
+            "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+            "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+            "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+            "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
             : "memory");
         return;
     } else
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\t"
-        "ds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\t"
-        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
         : "memory");
 #else
     for (int x = 0; x < N; ++x) r[x] = s16x4{};
@@ -710,7 +728,10 @@ void bwd_dq_kernel(BwdParams p)
     // 16 ((l / 16) % 2) + 4 (l % 4), and receives column d = 32 db + (l % 32)
     // of the keys 16 c + 4 hh + t and 16 c + 8 + 4 hh + t, t < 4: the order of
     // the dS^T operand below.  trof() is the byte offset in the swizzled rows
-    // (formed where used: not held in registers across the loop).
+    // (formed where used: not held in registers across the loop); for D = 128
+    // one base per lane serves every read (tr_base128).
+    static_assert(D != 128 || STAGE % 256 == 0, "stage rows start on 256-byte boundaries");
+    const unsigned trb = D == 128 ? opaque(tr_base128((unsigned)lane) + 8192u * (unsigned)kh) : 0u;
     auto trof = [&](unsigned ln, int c2, int hi, int db) -> unsigned {
         const unsigned r = 16u * (unsigned)(2 * kh + c2) + 8u * (unsigned)hi + 4u * (ln >> 5) + (ln & 15u) / 4u;
         const unsigned col = 32u * (unsigned)db + 16u * ((ln >> 4) & 1u) + 4u * (ln & 3u);   // bf16 column
@@ -886,23 +907,38 @@ void bwd_dq_kernel(BwdParams p)
         // 2 kh, 2 kh + 1), K^T read from the K rows
         const unsigned tln = opaque((unsigned)lane);
         const unsigned stl = lds_addr(st);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            unsigned ad[2 * NDB];
-            s16x4 rd[2 * NDB];
+        unsigned ad128[2 * NDB];   // D = 128: the reads of 16-key step 0 (step 1 at + 4096)
+        if constexpr (D == 128) {
+            const unsigned x0 = stl + trb;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                ad[2 * db] = stl + trof(tln, c2, 0, db);
-                ad[2 * db + 1] = stl + trof(tln, c2, 1, db);
+                ad128[2 * db] = x0 ^ (64u * (unsigned)db);
+                ad128[2 * db + 1] = (x0 + 2048u) ^ (64u * (unsigned)db + 32u);
             }
-            tr_read<2 * NDB>(rd, ad);
+        }
+        auto dq_part = [&](auto c2v) {
+            constexpr int c2 = decltype(c2v)::value;
+            s16x4 rd[2 * NDB];
+            if constexpr (D == 128) {
+                tr_read<2 * NDB, 4096 * c2>(rd, ad128);
+            } else {
+                unsigned ad[2 * NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    ad[2 * db] = stl + trof(tln, c2, 0, db);
+                    ad[2 * db + 1] = stl + trof(tln, c2, 1, db);
+                }
+                tr_read<2 * NDB>(rd, ad);
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const s16x8 a8 = __builtin_shufflevector(rd[2 * db], rd[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                 dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pd[c2],
                                                                    dqacc[db], 0, 0, 0);
             }
-        }
+        };
+        dq_part(std::integral_constant<int, 0>{});
+        dq_part(std::integral_constant<int, 1>{});
 
         // this wave's DMA of the next tile has landed (the bias DMA of the
         // tile two ahead and this tile's profile-gradient stores, issued after
@@ -1186,17 +1222,22 @@ void bwd_dkdv_kernel(BwdParams p)
     // receives column d = 32 db + (l % 32) of the queries 16 c + 4 hh + t and
     // 16 c + 8 + 4 hh + t, t < 4: the order of the P / dS registers.  trof[]
     // are the byte offsets of the lane's 8 bytes in the swizzled rows.
+    // (D = 128: one base per lane, tr_base128; the others kept per read)
+    static_assert(D != 128 || (STAGE % 256 == 0 && DO_OFF % 256 == 0), "row tiles start on 256-byte boundaries");
     int trof[2][2][NDB];
+    const unsigned trb = D == 128 ? opaque(tr_base128((unsigned)lane)) : 0u;
+    if constexpr (D != 128) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int hi = 0; hi < 2; ++hi)
+            for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int r = 16 * c + 8 * hi + 4 * hh + (lane & 15) / 4;
-                const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // bf16 column
-                trof[c][hi][db] = r * (2 * D) + 16 * ((col / 8) ^ row_swz<D>(r)) + 2 * (col % 8);
-            }
+                for (int db = 0; db < NDB; ++db) {
+                    const int r = 16 * c + 8 * hi + 4 * hh + (lane & 15) / 4;
+                    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // bf16 column
+                    trof[c][hi][db] = r * (2 * D) + 16 * ((col / 8) ^ row_swz<D>(r)) + 2 * (col % 8);
+                }
+    }
 
     // iteration = (live query block, head of the group); descriptors of the
     // next two are kept for the DMA ahead
@@ -1412,16 +1453,29 @@ void bwd_dkdv_kernel(BwdParams p)
             // transposed operands come from the rows by transposing LDS reads
             {
                 const unsigned rl = lds_addr(st + (role ? Q_OFF : DO_OFF));
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    unsigned ad[2 * NDB];
-                    s16x4 rd[2 * NDB];
+                unsigned ad128[2 * NDB];   // D = 128: the reads of query step 0 (step 1 at + 4096)
+                if constexpr (D == 128) {
+                    const unsigned x0 = rl + trb;
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        ad[2 * db] = rl + (unsigned)trof[c][0][db];
-                        ad[2 * db + 1] = rl + (unsigned)trof[c][1][db];
+                        ad128[2 * db] = x0 ^ (64u * (unsigned)db);
+                        ad128[2 * db + 1] = (x0 + 2048u) ^ (64u * (unsigned)db + 32u);
                     }
-                    tr_read<2 * NDB>(rd, ad);
+                }
+                auto part = [&](auto cv) {
+                    constexpr int c = decltype(cv)::value;
+                    s16x4 rd[2 * NDB];
+                    if constexpr (D == 128) {
+                        tr_read<2 * NDB, 4096 * c>(rd, ad128);
+                    } else {
+                        unsigned ad[2 * NDB];
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            ad[2 * db] = rl + (unsigned)trof[c][0][db];
+                            ad[2 * db + 1] = rl + (unsigned)trof[c][1][db];
+                        }
+                        tr_read<2 * NDB>(rd, ad);
+                    }
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
                         const s16x4 lo = rd[2 * db], hi = rd[2 * db + 1];
@@ -1429,7 +1483,9 @@ void bwd_dkdv_kernel(BwdParams p)
                             __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
                         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[db], 0, 0, 0);
                     }
-                }
+                };
+                part(std::integral_constant<int, 0>{});
+                part(std::integral_constant<int, 1>{});
             }
         }
         asm volatile("" ::: "memory");
