@@ -626,21 +626,27 @@ void bwd_dq_kernel(BwdParams p)
     // slot l % CH, i.e. chunk slot ^ row_swz(row)).  Every wave also fetches
     // the same 64 start columns, so that each wave's sequence of memory
     // instructions is the same on every path.
+    // The lane's part of the offset (row RPG wave + ln / CH of the tile, its
+    // chunk) is formed once: group a = wave + NW u adds RPG NW u rows, which
+    // leaves the row's swizzle (a function of the row modulo 16) unchanged.
+    static_assert(GPW == 1 || (RPG * NW) % 16 == 0, "the swizzle of a lane's rows is the same in every group");
+    const unsigned kvlane = [&] {
+        const unsigned r = (unsigned)(RPG * wave) + (unsigned)lane / CH;
+        return opaque(r * krow + 16u * (((unsigned)lane % CH) ^ (unsigned)row_swz<D>((int)r)));
+    }();
     auto stage_load = [&](int kt, int sb) {
         const int j0 = kt * BN;
         char* const st = smem + sb * STAGE;
-        const unsigned ln = opaque((unsigned)lane);   // (offsets formed here, not held in registers)
 #pragma unroll
         for (int u = 0; u < GPW; ++u) {
             const int a = wave + NW * u;
-            const unsigned r = (unsigned)(RPG * a) + ln / CH;
             // (whole offsets in the register operand: the range check, which
             // turns rows past Sk into zeros, applies to it)
-            const unsigned kvo = ((unsigned)j0 + r) * krow + 16u * ((ln % CH) ^ (unsigned)row_swz<D>((int)r));
+            const unsigned kvo = kvlane + (unsigned)(j0 + RPG * NW * u) * krow;
             dma_to_lds<16>(krs, lds_addr(st + K_OFF + 1024 * a), kvo);
             dma_to_lds<16>(vrs, lds_addr(st + V_OFF + 1024 * a), kvo);
         }
-        const unsigned cao = (unsigned)j0 * 4u + 4u * ln;
+        const unsigned cao = (unsigned)j0 * 4u + 4u * opaque((unsigned)lane);
         dma_to_lds<4>(kas, lds_addr(st + CA_OFF), cao);
     };
     // This wave's bias of tile kt goes by DMA into a strip of the wave, about
