@@ -100,9 +100,11 @@ struct BwdParams {
 // banks, and so do 4 consecutive rows read at 4 consecutive logical chunks
 // (the pattern of a transposing read).
 // Slot permutation of the 16-byte chunks of a 128-byte whole-run row in a
-// bias strip: rows 2 apart start their chunks at different slots, so that 16
-// consecutive rows read at one chunk index hit distinct banks.
-__device__ __forceinline__ unsigned run_swz(unsigned r) { return (r >> 1) & 7u; }
+// bias strip: 8 consecutive rows (from a multiple of 8) read at one chunk
+// index hit 8 distinct slots, and 16 consecutive rows hit each slot once
+// from an even and once from an odd row, so that neither a 128-byte nor a
+// 256-byte bank period leaves two lanes of a group on the same banks.
+__device__ __forceinline__ unsigned run_swz(unsigned r) { return (r & 7u) ^ ((r >> 3) & 1u); }
 
 template <int D> __device__ __forceinline__ int row_swz(int r)
 {
