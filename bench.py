@@ -430,6 +430,12 @@ def bench_backward(args, w, x):
                      "kernel_ms": call_ms, "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes},
     }
+    if w.window:
+        # window-bound shapes (about 120 flops per algorithmic byte, under the 312 at which
+        # the two peaks meet): the HBM roofline is the binding one, as for the forward
+        gbs = nbytes / (call_ms * 1e-3) / 1e9
+        line["roofline"].update({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": gbs / HBM_PEAK_GBS})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = backward_cpu_baseline(x, dout_h.double(), dlse_h.double(), args.cpu_seconds)
     print(json.dumps(line), flush=True)
