@@ -1279,230 +1279,237 @@ void bwd_dkdv_kernel(BwdParams p)
     prv.x = -1;
     prv.code = 0;
     prv.hs = 0;
-    int n_flight = 0;   // DMA instructions of the last stage requested
+    // The loop, specialised per role (each wave runs one of the two copies,
+    // so neither carries the other's registers and branches).
+    auto kv_loop = [&](auto rolec) {
+        constexpr int ROLE = decltype(rolec)::value;
+        int n_flight = 0;   // DMA instructions of the last stage requested
 #if defined(__HIP_DEVICE_COMPILE__)
-    // the K / V operands and the other loads above have landed: the compiler
-    // then keeps no wait for them inside the loop (where it would also wait
-    // for the stage DMA in flight)
-    __builtin_amdgcn_s_waitcnt(0);
+        // the K / V operands and the other loads above have landed: the compiler
+        // then keeps no wait for them inside the loop (where it would also wait
+        // for the stage DMA in flight)
+        __builtin_amdgcn_s_waitcnt(0);
 #endif
-    if (cur.x >= 0) {
-        issue(cur.x, g * p.G + cur.hs, 0);
-        const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads)
-        n_flight = issue(d.x, g * p.G + d.hs, 1);
-    }
-    int buf = 0, par = 0;
-    while (cur.x >= 0 || prv.x >= 0) {
-        const It n2 = succ(n1);
-        // this wave's DMA of stage t has landed (stage t + 1's may still be in
-        // flight); after the barrier every wave's has, every wave is done with
-        // the buffer the next request overwrites and with the exchange slot
-        // the P waves write now
-        switch (n_flight) {   // s_waitcnt vmcnt(n_flight) lgkmcnt(0) (operand must be a constant)
+        if (cur.x >= 0) {
+            issue(cur.x, g * p.G + cur.hs, 0);
+            const It d = n1.x >= 0 ? n1 : cur;   // (a copy nothing reads)
+            n_flight = issue(d.x, g * p.G + d.hs, 1);
+        }
+        int buf = 0, par = 0;
+        while (cur.x >= 0 || prv.x >= 0) {
+            const It n2 = succ(n1);
+            // this wave's DMA of stage t has landed (stage t + 1's may still be in
+            // flight); after the barrier every wave's has, every wave is done with
+            // the buffer the next request overwrites and with the exchange slot
+            // the P waves write now
+            switch (n_flight) {   // s_waitcnt vmcnt(n_flight) lgkmcnt(0) (operand must be a constant)
 #if defined(__HIP_DEVICE_COMPILE__)
-        case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0073); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0075); break;
-        case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
-        case 7: __builtin_amdgcn_s_waitcnt(0x0077); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0070); break;
+            case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+            case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
+            case 3: __builtin_amdgcn_s_waitcnt(0x0073); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+            case 5: __builtin_amdgcn_s_waitcnt(0x0075); break;
+            case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+            case 7: __builtin_amdgcn_s_waitcnt(0x0077); break;
+            default: __builtin_amdgcn_s_waitcnt(0x0070); break;
 #endif
-        }
-        asm volatile("s_barrier" ::: "memory");
-        {
-            const It d = n2.x >= 0 ? n2 : (cur.x >= 0 ? cur : prv);   // (a copy nothing reads)
-            n_flight = issue(d.x, g * p.G + d.hs, (buf + 2) & 3);     // stage t + 2
-        }
-        asm volatile("" ::: "memory");
-        // the P wave's work is (block, head) t; the dS wave's is t - 1
-        const It w = role ? prv : cur;
-        if (w.x >= 0) {
-            const char* st = smem + (role ? ((buf + 3) & 3) : buf) * STAGE;
-            char* const xp = smem + XP_OFF + (role ? par ^ 1 : par) * 8192 + kg * 2048 + 16 * lane;   // + 1024 h
-            const int i0 = w.x * BM;
-            const int hcur = g * p.G + w.hs;
-            const int my_cls = (w.code >> (2 * xk)) & 3;
-            const float* rsl = (const float*)(st + RS_OFF);
-
-            // ---- S (P waves) or dP (dS waves): A operands are the Q or dO rows
-            f32x16 sacc;
-            {
-                const unsigned rows = lds_addr(st + (role ? DO_OFF : Q_OFF));
-                bf16x8 ar[NKK];
-                unsigned aa[NKK];
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk)
-                    aa[kk] = rows + (unsigned)(kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl)));
-                lds_read16<NKK>(ar, aa);
-                sacc = f32x16{};
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk)
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[kk], kvreg[kk], sacc, 0, 0, 0);
             }
+            asm volatile("s_barrier" ::: "memory");
+            {
+                const It d = n2.x >= 0 ? n2 : (cur.x >= 0 ? cur : prv);   // (a copy nothing reads)
+                n_flight = issue(d.x, g * p.G + d.hs, (buf + 2) & 3);     // stage t + 2
+            }
+            asm volatile("" ::: "memory");
+            // the P wave's work is (block, head) t; the dS wave's is t - 1
+            const It w = ROLE ? prv : cur;
+            if (w.x >= 0) {
+                const char* st = smem + (ROLE ? ((buf + 3) & 3) : buf) * STAGE;
+                char* const xp = smem + XP_OFF + (ROLE ? par ^ 1 : par) * 8192 + kg * 2048 + 16 * lane;   // + 1024 h
+                const int i0 = w.x * BM;
+                const int hcur = g * p.G + w.hs;
+                const int my_cls = (w.code >> (2 * xk)) & 3;
+                const float* rsl = (const float*)(st + RS_OFF);
 
-            bf16x8 pb[2];   // P (P waves) / dS (dS waves): queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
-            if (role == 0) {
-                // ---- P = exp2(S c + bias log2(e) - lse2), masked
-                const int bc = bias_class(w.x);
-                const int* qil = (const int*)(st + QI_OFF);
-                const char* bsl = st + BS_OFF + kg * BSW + ES * (31 - kl);   // + slot * RUNB
-                auto body = [&](auto bct, auto mt) {
-                    constexpr int BCT = decltype(bct)::value;
-                    constexpr bool MASKED = decltype(mt)::value;
-                    // (the stage's row statistics, query descriptors and bias runs, read
-                    // in asm blocks: see lds_read16)
+                // ---- S (P waves) or dP (dS waves): A operands are the Q or dO rows
+                f32x16 sacc;
+                {
+                    const unsigned rows = lds_addr(st + (ROLE ? DO_OFF : Q_OFF));
+                    bf16x8 ar[NKK];
+                    unsigned aa[NKK];
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk)
+                        aa[kk] = rows + (unsigned)(kl * (2 * D) + 16 * ((2 * kk + hh) ^ row_swz<D>(kl)));
+                    lds_read16<NKK>(ar, aa);
+                    sacc = f32x16{};
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk)
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[kk], kvreg[kk], sacc, 0, 0, 0);
+                }
+
+                bf16x8 pb[2];   // P (P waves) / dS (dS waves): queries 16 c + 8 (t / 4) + 4 hh + (t % 4)
+                if (ROLE == 0) {
+                    // ---- P = exp2(S c + bias log2(e) - lse2), masked
+                    const int bc = bias_class(w.x);
+                    const int* qil = (const int*)(st + QI_OFF);
+                    const char* bsl = st + BS_OFF + kg * BSW + ES * (31 - kl);   // + slot * RUNB
+                    auto body = [&](auto bct, auto mt) {
+                        constexpr int BCT = decltype(bct)::value;
+                        constexpr bool MASKED = decltype(mt)::value;
+                        // (the stage's row statistics, query descriptors and bias runs, read
+                        // in asm blocks: see lds_read16)
+                        f32x4 rsv[8];
+                        lds_read_pairs(rsv, lds_addr(rsl) + 32u * (unsigned)hh);
+                        f32x4 qiv[8];
+                        if constexpr (MASKED) lds_read_pairs(qiv, lds_addr(qil) + 32u * (unsigned)hh);
+                        unsigned bvr[16];
+                        if constexpr (BCT != BC_NONE) lds_read_bias<PB>(bvr, lds_addr(bsl) + (unsigned)(hh * RUNB));
+                        // A run that starts before the block reads as 0 from a DMA piece at
+                        // a wrapped offset: the block's first 8 entries are loaded here.  Only
+                        // the rows of a block with i0 E < 8 can hold them (a uniform test);
+                        // the loads are waited for inside the branch, so that no wait for
+                        // them (which would also wait for the stage DMA) sits on other paths.
+                        if constexpr (BCT == BC_EDGE) {
+                            if (i0 * p.E < 8) {
+                                const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
+#pragma unroll
+                                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const int m0 = 8 * jj + 4 * hh;
+                                        const int r = p.qoff + i0 + m0 + e - j;
+                                        const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
+                                        if (ent < 8 && (unsigned)r < (unsigned)p.E)
+                                            bvr[4 * jj + e] = PB ? (unsigned)((const unsigned short*)pr0)[ent]
+                                                                 : ((const unsigned*)pr0)[ent];
+                                    }
+#if defined(__HIP_DEVICE_COMPILE__)
+                                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#endif
+                            }
+                        }
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int m0 = 8 * jj + 4 * hh;
+                            const f32x4 rs01 = rsv[2 * jj];
+                            const f32x4 rs23 = rsv[2 * jj + 1];
+                            i32x4 qi01, qi23;
+                            if constexpr (MASKED) {
+                                qi01 = __builtin_bit_cast(i32x4, qiv[2 * jj]);
+                                qi23 = __builtin_bit_cast(i32x4, qiv[2 * jj + 1]);
+                            }
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
+                                float pre = -lse2;
+                                if constexpr (BCT != BC_NONE) {
+                                    float bias;
+                                    if constexpr (PB)
+                                        bias = __uint_as_float(bvr[4 * jj + e] << 16);
+                                    else
+                                        bias = __uint_as_float(bvr[4 * jj + e]);
+                                    if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
+                                    if constexpr (BCT == BC_EDGE) {
+                                        const int r = p.qoff + i0 + m0 + e - j;
+                                        pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
+                                    }
+                                }
+                                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
+                                if constexpr (MASKED) {
+                                    const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
+                                    const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
+                                    pr = key_visible(gq, aq, j, c_k, wlim) ? pr : 0.0f;
+                                }
+                                pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
+                            }
+                        }
+                    };
+                    using F = std::false_type;
+                    using T = std::true_type;
+                    using NONE = std::integral_constant<int, BC_NONE>;
+                    using FULL = std::integral_constant<int, BC_FULL>;
+                    using EDGE = std::integral_constant<int, BC_EDGE>;
+                    if (my_cls == TILE_FULL) {
+                        if (bc == BC_NONE) body(NONE{}, F{});
+                        else if (bc == BC_FULL) body(FULL{}, F{});
+                        else body(EDGE{}, F{});
+                    } else {
+                        if (bc == BC_NONE) body(NONE{}, T{});
+                        else if (bc == BC_FULL) body(FULL{}, T{});
+                        else body(EDGE{}, T{});
+                    }
+                    *(bf16x8*)(xp) = pb[0];
+                    *(bf16x8*)(xp + 1024) = pb[1];
+                } else {
+                    // ---- dS = P (dP - (Delta - dlse)); dO (so dP) is 0 on rows that
+                    // are not real or lie past Sq, and V on keys that are not real, so
+                    // dP is finite everywhere and P = 0 masks dS
+                    bf16x8 p0, p1;
+                    lds_read_two(p0, p1, lds_addr(xp));
                     f32x4 rsv[8];
                     lds_read_pairs(rsv, lds_addr(rsl) + 32u * (unsigned)hh);
-                    f32x4 qiv[8];
-                    if constexpr (MASKED) lds_read_pairs(qiv, lds_addr(qil) + 32u * (unsigned)hh);
-                    unsigned bvr[16];
-                    if constexpr (BCT != BC_NONE) lds_read_bias<PB>(bvr, lds_addr(bsl) + (unsigned)(hh * RUNB));
-                    // A run that starts before the block reads as 0 from a DMA piece at
-                    // a wrapped offset: the block's first 8 entries are loaded here.  Only
-                    // the rows of a block with i0 E < 8 can hold them (a uniform test);
-                    // the loads are waited for inside the branch, so that no wait for
-                    // them (which would also wait for the stage DMA) sits on other paths.
-                    if constexpr (BCT == BC_EDGE) {
-                        if (i0 * p.E < 8) {
-                            const char* pr0 = (const char*)p.profiles + ((size_t)b * p.Hq + hcur) * pblock;
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const int m0 = 8 * jj + 4 * hh;
-                                    const int r = p.qoff + i0 + m0 + e - j;
-                                    const int ent = (i0 + m0 + e) * p.E + r;   // entry index in the block
-                                    if (ent < 8 && (unsigned)r < (unsigned)p.E)
-                                        bvr[4 * jj + e] = PB ? (unsigned)((const unsigned short*)pr0)[ent]
-                                                             : ((const unsigned*)pr0)[ent];
-                                }
-#if defined(__HIP_DEVICE_COMPILE__)
-                            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-#endif
-                        }
-                    }
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int m0 = 8 * jj + 4 * hh;
                         const f32x4 rs01 = rsv[2 * jj];
                         const f32x4 rs23 = rsv[2 * jj + 1];
-                        i32x4 qi01, qi23;
-                        if constexpr (MASKED) {
-                            qi01 = __builtin_bit_cast(i32x4, qiv[2 * jj]);
-                            qi23 = __builtin_bit_cast(i32x4, qiv[2 * jj + 1]);
-                        }
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float lse2 = e < 2 ? rs01[2 * e] : rs23[2 * (e - 2)];
-                            float pre = -lse2;
-                            if constexpr (BCT != BC_NONE) {
-                                float bias;
-                                if constexpr (PB)
-                                    bias = __uint_as_float(bvr[4 * jj + e] << 16);
-                                else
-                                    bias = __uint_as_float(bvr[4 * jj + e]);
-                                if constexpr (BCT == BC_FULL) pre = __builtin_fmaf(bias, LOG2E, -lse2);
-                                if constexpr (BCT == BC_EDGE) {
-                                    const int r = p.qoff + i0 + m0 + e - j;
-                                    pre = (unsigned)r < (unsigned)p.E ? __builtin_fmaf(bias, LOG2E, -lse2) : pre;
-                                }
-                            }
-                            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * jj + e], p.c_log2, pre));
-                            if constexpr (MASKED) {
-                                const int gq = e < 2 ? qi01[2 * e] : qi23[2 * (e - 2)];
-                                const int aq = e < 2 ? qi01[2 * e + 1] : qi23[2 * (e - 2) + 1];
-                                pr = key_visible(gq, aq, j, c_k, wlim) ? pr : 0.0f;
-                            }
-                            pb[jj >> 1][4 * (jj & 1) + e] = (__bf16)pr;
+                            const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
+                            const int t = 4 * (jj & 1) + e;
+                            const float pr = (float)((jj >> 1) ? p1[t] : p0[t]);
+                            pb[jj >> 1][t] = (__bf16)(pr * (sacc[4 * jj + e] - dlt));
                         }
                     }
-                };
-                using F = std::false_type;
-                using T = std::true_type;
-                using NONE = std::integral_constant<int, BC_NONE>;
-                using FULL = std::integral_constant<int, BC_FULL>;
-                using EDGE = std::integral_constant<int, BC_EDGE>;
-                if (my_cls == TILE_FULL) {
-                    if (bc == BC_NONE) body(NONE{}, F{});
-                    else if (bc == BC_FULL) body(FULL{}, F{});
-                    else body(EDGE{}, F{});
-                } else {
-                    if (bc == BC_NONE) body(NONE{}, T{});
-                    else if (bc == BC_FULL) body(FULL{}, T{});
-                    else body(EDGE{}, T{});
                 }
-                *(bf16x8*)(xp) = pb[0];
-                *(bf16x8*)(xp + 1024) = pb[1];
-            } else {
-                // ---- dS = P (dP - (Delta - dlse)); dO (so dP) is 0 on rows that
-                // are not real or lie past Sq, and V on keys that are not real, so
-                // dP is finite everywhere and P = 0 masks dS
-                bf16x8 p0, p1;
-                lds_read_two(p0, p1, lds_addr(xp));
-                f32x4 rsv[8];
-                lds_read_pairs(rsv, lds_addr(rsl) + 32u * (unsigned)hh);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const f32x4 rs01 = rsv[2 * jj];
-                    const f32x4 rs23 = rsv[2 * jj + 1];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float dlt = e < 2 ? rs01[2 * e + 1] : rs23[2 * (e - 2) + 1];
-                        const int t = 4 * (jj & 1) + e;
-                        const float pr = (float)((jj >> 1) ? p1[t] : p0[t]);
-                        pb[jj >> 1][t] = (__bf16)(pr * (sacc[4 * jj + e] - dlt));
-                    }
-                }
-            }
 
-            // ---- dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves); the
-            // transposed operands come from the rows by transposing LDS reads
-            {
-                const unsigned rl = lds_addr(st + (role ? Q_OFF : DO_OFF));
-                unsigned ad128[2 * NDB];   // D = 128: the reads of query step 0 (step 1 at + 4096)
-                if constexpr (D == 128) {
-                    const unsigned x0 = rl + trb;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        ad128[2 * db] = x0 ^ (64u * (unsigned)db);
-                        ad128[2 * db + 1] = (x0 + 2048u) ^ (64u * (unsigned)db + 32u);
-                    }
-                }
-                auto part = [&](auto cv) {
-                    constexpr int c = decltype(cv)::value;
-                    s16x4 rd[2 * NDB];
+                // ---- dV^T += dO^T P (P waves) or dK^T += Q^T dS (dS waves); the
+                // transposed operands come from the rows by transposing LDS reads
+                {
+                    const unsigned rl = lds_addr(st + (ROLE ? Q_OFF : DO_OFF));
+                    unsigned ad128[2 * NDB];   // D = 128: the reads of query step 0 (step 1 at + 4096)
                     if constexpr (D == 128) {
-                        tr_read<2 * NDB, 4096 * c>(rd, ad128);
-                    } else {
-                        unsigned ad[2 * NDB];
+                        const unsigned x0 = rl + trb;
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
-                            ad[2 * db] = rl + (unsigned)trof[c][0][db];
-                            ad[2 * db + 1] = rl + (unsigned)trof[c][1][db];
+                            ad128[2 * db] = x0 ^ (64u * (unsigned)db);
+                            ad128[2 * db + 1] = (x0 + 2048u) ^ (64u * (unsigned)db + 32u);
                         }
-                        tr_read<2 * NDB>(rd, ad);
                     }
+                    auto part = [&](auto cv) {
+                        constexpr int c = decltype(cv)::value;
+                        s16x4 rd[2 * NDB];
+                        if constexpr (D == 128) {
+                            tr_read<2 * NDB, 4096 * c>(rd, ad128);
+                        } else {
+                            unsigned ad[2 * NDB];
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const s16x4 lo = rd[2 * db], hi = rd[2 * db + 1];
-                        const bf16x8 a =
-                            __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[db], 0, 0, 0);
-                    }
-                };
-                part(std::integral_constant<int, 0>{});
-                part(std::integral_constant<int, 1>{});
+                            for (int db = 0; db < NDB; ++db) {
+                                ad[2 * db] = rl + (unsigned)trof[c][0][db];
+                                ad[2 * db + 1] = rl + (unsigned)trof[c][1][db];
+                            }
+                            tr_read<2 * NDB>(rd, ad);
+                        }
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const s16x4 lo = rd[2 * db], hi = rd[2 * db + 1];
+                            const bf16x8 a =
+                                __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[db], 0, 0, 0);
+                        }
+                    };
+                    part(std::integral_constant<int, 0>{});
+                    part(std::integral_constant<int, 1>{});
+                }
             }
+            asm volatile("" ::: "memory");
+            buf = (buf + 1) & 3;
+            par ^= 1;
+            prv = cur;
+            cur = n1;
+            n1 = n2;
         }
-        asm volatile("" ::: "memory");
-        buf = (buf + 1) & 3;
-        par ^= 1;
-        prv = cur;
-        cur = n1;
-        n1 = n2;
-    }
+    };
+    if (role) kv_loop(std::integral_constant<int, 1>{});
+    else kv_loop(std::integral_constant<int, 0>{});
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_s_waitcnt(0);   // no DMA outstanding at exit
 #endif
