@@ -215,6 +215,22 @@ def test_sink_extremes(sink):
     check_full(x, f"sink={sink}")
 
 
+@pytest.mark.parametrize("growth,sink", [(6.0, None), (6.0, -math.inf), (-0.8, None), (10.0, 3.0)],
+                         ids=["rising", "rising_no_sink", "falling", "steep_sink3"])
+def test_softmax_frame_moves_within_rows(growth, sink):
+    # Logit scale that changes along the keys: the fp16 weights of later tiles
+    # leave the range of the frame set by earlier ones (rising), or fall far
+    # below it (falling), so the frame has to move in the middle of rows.
+    x = W.custom(B=2, S=700, Hq=8, Hkv=2, D=128, E=90, seed=125, structure="tail_pad", max_tail_pad=50,
+                 window=500 if growth > 9 else None)
+    S = x["k"].shape[1]
+    f = 1.0 + growth * torch.arange(S, dtype=torch.float32) / S
+    x["k"] = (x["k"].float() * f[None, :, None, None]).to(torch.bfloat16)
+    if sink is not None:
+        x["sink"].fill_(sink)
+    check_full(x, f"frame growth={growth} sink={sink}")
+
+
 def test_all_invalid_and_empty_keys():
     x = W.custom(B=1, S=130, Hq=4, Hkv=2, D=64, E=8, seed=123)
     x["valid"].zero_()

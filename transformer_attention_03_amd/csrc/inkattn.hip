@@ -68,7 +68,7 @@ namespace {
 using namespace inkattn;
 
 constexpr int NWAVES = 8; // waves per attention workgroup (one workgroup per CU)
-constexpr float RESCALE_SLACK = 8.0f;   // log2 units the running max may lag behind
+constexpr float FRAME_LIMIT = 32768.0f;   // bound on a lane's partial sum of 32 fp16 weights in the frame
 // s_waitcnt operands (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
 // vmcnt(0) lgkmcnt(0); lgkmcnt(0) alone
 [[maybe_unused]] constexpr int WAIT_VM_LGKM = 0x0070;   // (used by the device pass only)
@@ -831,9 +831,9 @@ void attn_fwd_kernel(FwdParams p)
         }
         // operands of step 0 of the previous tile's PV product (read while the
         // chains above finish)
-        f16x8 avn[NDB];
+        f16x8 avs[4][NDB];   // operands of the four steps (each step's own registers)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vbp + vb + db * 32 * 128);
+        for (int db = 0; db < NDB; ++db) avs[0][db] = *(const f16x8*)(vbp + vb + db * 32 * 128);
         // ---- + bias * sqrt(D) (nothing on tiles this wave skips); the bias
         // registers / strip then take the next tile's
         int ncode = 0;   // bias code of the next tile
@@ -869,49 +869,31 @@ void attn_fwd_kernel(FwdParams p)
                 }
         }
 
-        // ---- step 0 of the previous tile's O^T += V^T P^T, with this tile's
-        // row max (log2 units) on the vector units meanwhile; the operands of
-        // step 1 are read meanwhile
+        // ---- the softmax frame.  The running frame m (log2 units) only has to
+        // keep this tile's fp16 weights e^{z - m} in range; it is not moved to
+        // each tile's row max.  A row takes its first frame from the first tile
+        // with a finite logit when it has no sink (its output, denominator and
+        // previous weights are still zero then); afterwards the frame moves
+        // only when a weight would leave the fp16 range, which the row's partial
+        // sums show after the fact (below).
+        auto row_max = [&]() -> float {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avn[db], pbp[0], oacc[db], 0, 0, 0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) avn[db] = *(const f16x8*)(vbp + (vb ^ 32u) + db * 32 * 128);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            mx = fmaxf(mx, acc[0][t]);
-            mx = fmaxf(mx, acc[1][t]);
+            for (int t = 0; t < 16; ++t) {
+                mx = fmaxf(mx, acc[0][t]);
+                mx = fmaxf(mx, acc[1][t]);
+            }
+            return half_max(mx * p.c_log2);
+        };
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY) != 0) {
+            const float mx = row_max();
+            if (m == -INFINITY) m = mx;
         }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
-        mx = half_max(mx * p.c_log2);
-        const bool move = mx > m + RESCALE_SLACK;   // false when mx is -inf; true from m = -inf
-        const float m_new = move ? mx : m;
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-            // into the new frame: the output so far (with step 0 of the previous
-            // tile) and the previous tile's weights still to be multiplied
-            const float alpha = move ? __builtin_amdgcn_exp2f(m - m_use) : 1.0f;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
-#pragma unroll
-            for (int c = 1; c < 4; ++c)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) pbp[c][t] = (_Float16)((float)pbp[c][t] * alpha);
-        }
-        m = m_new;
+        float m_use = (m == -INFINITY) ? 0.0f : m;
 
-        // ---- steps 1..3 of the previous tile's product, with this tile's
-        // weights P^T on the vector units meanwhile.  pb[c] holds keys 16 c + ...
-        // in the order of V^T's staged rows.
+        // ---- the previous tile's O^T += V^T P^T in four steps, with this
+        // tile's weights P^T on the vector units meanwhile.  pb[c] holds keys
+        // 16 c + ... in the order of V^T's staged rows.
         f16x8 pb[4];
         float ls0 = 0.0f, ls1 = 0.0f;
         auto make_p = [&](int c) {
@@ -928,33 +910,51 @@ void attn_fwd_kernel(FwdParams p)
             }
         };
 #pragma unroll
-        for (int c = 1; c < 4; ++c) {
-            f16x8 av[NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) av[db] = avn[db];
+        for (int c = 0; c < 4; ++c) {
             // the operands of step c + 1 are read while step c multiplies
             if (c < 3) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    avn[db] = *(const f16x8*)(vbp + (vb ^ (32u * (c + 1))) + db * 32 * 128);
+                    avs[c + 1][db] = *(const f16x8*)(vbp + (vb ^ (32u * (c + 1))) + db * 32 * 128);
             }
-            if (c == 1) make_p(0);
             make_p(c);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[db], pbp[c], oacc[db], 0, 0, 0);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avs[c][db], pbp[c], oacc[db], 0, 0, 0);
             if (c < 3) __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (c == 1) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);   // VALU
-                else __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
+            __builtin_amdgcn_sched_barrier(0);   // each step is scheduled on its own
         }
         // (the weights are pinned here, so that the compiler does not sink
         // their computation below the MFMAs it is meant to overlap)
 #pragma unroll
         for (int c = 0; c < 4; ++c) pin(pb[c]);
+        // A lane's 32 weights summing below 2^15 are each below 2^15, inside
+        // fp16's range.  Otherwise (or a NaN) the frame moves to the row max:
+        // the output so far (all of the previous tile's product included) and
+        // the denominator are rescaled and this tile's weights are formed again.
+        if (__builtin_amdgcn_ballot_w64(!(ls0 + ls1 < FRAME_LIMIT)) != 0) {
+            const float mx = row_max();
+            const float m_new = fmaxf(m, mx);
+            // (rows of the wave whose frame stays put, one still unset among
+            // them, keep their sums: e^{-inf - (-inf)} would be a NaN)
+            const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) oacc[db][t] *= alpha;
+            m = m_new;
+            m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            ls0 = 0.0f;
+            ls1 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) make_p(c);
+        }
         l += ls0 + ls1;
 #pragma unroll
         for (int c = 0; c < 4; ++c) pbp[c] = pb[c];
