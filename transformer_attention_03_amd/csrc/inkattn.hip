@@ -894,7 +894,11 @@ void attn_fwd_kernel(FwdParams p)
         // ---- the previous tile's O^T += V^T P^T in four steps, with this
         // tile's weights P^T on the vector units meanwhile.  pb[c] holds keys
         // 16 c + ... in the order of V^T's staged rows.
-        f16x8 pb[4];
+        // Without bias, this tile's weights replace the previous tile's in pbp,
+        // step by step, once the products that read them have been issued (no
+        // copy closes the iteration); the bias loop keeps its own array
+        f16x8 pbl[4];
+        f16x8 (&pb)[4] = *(WB ? &pbl : &pbp);
         float ls0 = 0.0f, ls1 = 0.0f;
         auto make_p = [&](int c) {
 #pragma unroll
@@ -917,17 +921,18 @@ void attn_fwd_kernel(FwdParams p)
                 for (int db = 0; db < NDB; ++db)
                     avs[c + 1][db] = *(const f16x8*)(vbp + (vb ^ (32u * (c + 1))) + db * 32 * 128);
             }
-            make_p(c);
+            if constexpr (WB) make_p(c);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(avs[c][db], pbp[c], oacc[db], 0, 0, 0);
+            if constexpr (!WB) make_p(c);
             if (c < 3) __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // LDS reads
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
             }
-            __builtin_amdgcn_sched_barrier(0);   // each step is scheduled on its own
+            if constexpr (WB) __builtin_amdgcn_sched_barrier(0);   // each step is scheduled on its own
         }
         // (the weights are pinned here, so that the compiler does not sink
         // their computation below the MFMAs it is meant to overlap)
@@ -956,8 +961,10 @@ void attn_fwd_kernel(FwdParams p)
             for (int c = 0; c < 4; ++c) make_p(c);
         }
         l += ls0 + ls1;
+        if constexpr (WB) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) pbp[c] = pb[c];
+            for (int c = 0; c < 4; ++c) pbp[c] = pb[c];
+        }
 
         // this wave's part of the next tile's DMA has landed (the bias loads
         // issued after it may still be in flight); then every wave's has
