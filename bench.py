@@ -35,6 +35,31 @@ MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / fp16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 DEFAULT_WORKLOAD = "full_causal_8k"
 MALL_FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB MALL
+
+
+class MallFlush:
+    """Evicts the step's inputs from the 256 MB MALL before every timed step.
+
+    ``read``: a reduction reads a 512 MiB buffer, which leaves the MALL full of
+    clean lines.  ``write``: a fill writes it, which leaves the MALL full of
+    dirty lines that the timed kernels then write back to HBM as they evict
+    them (traffic that is not theirs).
+    """
+
+    def __init__(self, mode, dev):
+        import torch
+        self.mode = mode
+        self.buf = torch.ones(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        self.sink = None
+
+    def __call__(self):
+        if self.mode == "read":
+            self.sink = self.buf.sum()
+        else:
+            self.buf.fill_(1)
+
+    def describe(self):
+        return f"a {MALL_FLUSH_BYTES >> 20} MiB {self.mode}"
 # the forward kernel's sources: its traffic record holds their combined sha256
 KERNEL_SRCS = [os.path.join(ROOT, "transformer_attention_03_amd", "csrc", f) for f in ("inkattn.hip", "common.h")]
 
@@ -179,6 +204,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mall-flush", action="store_true",
                     help="do not flush the 256 MB MALL between timed steps (then ms_per_step is wall clock)")
+    ap.add_argument("--mall-flush", choices=("read", "write"), default="write",
+                    help="how the MALL is flushed before each timed step: a 512 MiB read or write")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -239,12 +266,13 @@ def main():
         window=w.window, out=out, lse=lse, workspace=ws, stream=stream)
 
     # The 256 MB MALL (last-level cache) would otherwise keep inputs of one step
-    # for the next: a 512 MiB write before every step, outside the step's events.
-    flush = None if args.no_mall_flush else torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    # for the next: a 512 MiB read or write before every step, outside the
+    # step's events.
+    flush = None if args.no_mall_flush else MallFlush(args.mall_flush, dev)
 
     def step(evs=None):
         if flush is not None:
-            flush.fill_(1)
+            flush()
         if evs is not None:
             evs[0].record(stream)
         plan()
@@ -292,8 +320,8 @@ def main():
                                f"window={w.window} profiles={str(w.profiles_dtype).replace('torch.', '')}",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
                    "qk_mfma": "bf16", "pv_mfma": "fp16", "accumulate": "fp32"},
-        "timing": ("per-step HIP events (pre-pass, value copy, attention kernel); the MALL is flushed by a "
-                   f"{MALL_FLUSH_BYTES >> 20} MiB write before each step, outside the events; wall clock over the "
+        "timing": ("per-step HIP events (pre-pass, value copy, attention kernel); the MALL is flushed by "
+                   f"{flush.describe() if flush is not None else ''} before each step, outside the events; wall clock over the "
                    f"{args.steps} steps, flushes included: {wall_ms:.4f} ms/step") if flush is not None else
                   "wall clock over the timed steps, no cache flush between them",
         "tokens_per_s": valid_tokens / (ms_step * 1e-3),
@@ -587,7 +615,7 @@ def bench_relproj(args):
                                  positions=d["positions"], window=w.window, out=out, lse=lse, workspace=ws,
                                  stream=stream)
 
-    flush = None if args.no_mall_flush else torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = None if args.no_mall_flush else MallFlush(args.mall_flush, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -595,7 +623,7 @@ def bench_relproj(args):
     t0 = time.perf_counter()
     for e0, e1 in evs:
         if flush is not None:
-            flush.fill_(1)
+            flush()
         e0.record(stream)
         step()
         e1.record(stream)
