@@ -768,6 +768,10 @@ void attn_fwd_kernel(FwdParams p)
     const int kt_split = p.E <= 0 ? INT_MAX : (qlo_wg - p.E - (BN - 1) >= 0 ? (qlo_wg - p.E - (BN - 1)) / BN + 1 : 0);
     if (cur.kt <= kt_hi) issue_tile(cur, 0, 0);
     wait_all_and_barrier();
+    // The descriptor of the tile after the current one is read one tile
+    // ahead, before the barrier that ends the previous tile, so that its LDS
+    // read is not waited for at the start of the tile.
+    TileDesc nxt_pre = next_live();
     int kbuf = 0, vbuf = 0, vprev = 2;
     f16x8 pbp[4];   // P^T of the previous tile (zero when this wave did not compute it)
 #pragma unroll
@@ -776,7 +780,7 @@ void attn_fwd_kernel(FwdParams p)
     // One tile of the pipeline; WB: with the bias code.
     auto step = [&](auto with_bias) {
         constexpr bool WB = decltype(with_bias)::value;
-        const TileDesc nxt = next_live();
+        const TileDesc nxt = nxt_pre;
         const int j0 = cur.kt * BN;
         const int vnext = vbuf == 2 ? 0 : vbuf + 1;
 
@@ -966,6 +970,7 @@ void attn_fwd_kernel(FwdParams p)
             for (int c = 0; c < 4; ++c) pbp[c] = pb[c];
         }
 
+        nxt_pre = next_live();   // (the tile after nxt)
         // this wave's part of the next tile's DMA has landed (the bias loads
         // issued after it may still be in flight); then every wave's has
         wait_dma_and_barrier(WB ? bias_loads(ncode) : 0);
