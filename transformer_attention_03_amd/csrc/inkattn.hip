@@ -795,27 +795,29 @@ void attn_fwd_kernel(FwdParams p)
             formed = rel_needed(cur);
             if (formed) load_table(j0, tab);
         }
+        // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains.  The
+        // operands of k-step kk + 2 are read from LDS while k-step kk multiplies;
+        // those of the first two k-steps go out before the next tile's DMA, whose
+        // address set-up then hides their latency.
+        const char* kb = smem + K_OFF + kbuf * KBYTES;
+        auto kread = [&](int kk, int h2) -> bf16x8 {
+            return *(const bf16x8*)(kb + ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk + h2 * KHALF);
+        };
+        bf16x8 ka[NKK][2];
+        ka[0][0] = kread(0, 0);
+        ka[0][1] = kread(0, 1);
+        ka[1][0] = kread(1, 0);
+        ka[1][1] = kread(1, 1);
         asm volatile("" ::: "memory");
         issue_tile(nxt.kt <= kt_hi ? nxt : cur, kbuf ^ 1, vnext);
         asm volatile("" ::: "memory");
-        const char* kb = smem + K_OFF + kbuf * KBYTES;
         const char* vbp = smem + V_OFF + vprev * VBYTES;
         // V^T chunk 2 c + hh of row qi sits at slot (2 c + hh) ^ vt_swz(qi) = (hh ^ vt_swz(qi)) ^ 2 c
         const unsigned ln = opaque((unsigned)lane);   // (derived here, not held in registers)
         const unsigned vb = (ln & 31u) * 128u + 16u * ((ln >> 5) ^ (unsigned)vt_swz((int)(ln & 31u)));
 
-        // ---- S^T = K Q^T for keys j0 .. j0 + 63: two independent chains.  The
-        // operands of k-step kk + 2 are read from LDS while k-step kk multiplies.
-        auto kread = [&](int kk, int h2) -> bf16x8 {
-            return *(const bf16x8*)(kb + ((kk & 1) ? kbase_odd : kbase_even) + 32 * kk + h2 * KHALF);
-        };
         f32x16 acc[2];
         {
-            bf16x8 ka[NKK][2];
-            ka[0][0] = kread(0, 0);
-            ka[0][1] = kread(0, 1);
-            ka[1][0] = kread(1, 0);
-            ka[1][1] = kread(1, 1);
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 if (kk + 2 < NKK) {
@@ -825,7 +827,6 @@ void attn_fwd_kernel(FwdParams p)
                 acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][0], qreg[kk], kk ? acc[0] : f32x16{}, 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][1], qreg[kk], kk ? acc[1] : f32x16{}, 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads
 #pragma unroll
             for (int kk = 0; kk + 2 < NKK; ++kk) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
