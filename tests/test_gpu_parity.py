@@ -215,14 +215,16 @@ def test_sink_extremes(sink):
     check_full(x, f"sink={sink}")
 
 
-@pytest.mark.parametrize("growth,sink", [(6.0, None), (6.0, -math.inf), (-0.8, None), (10.0, 3.0)],
-                         ids=["rising", "rising_no_sink", "falling", "steep_sink3"])
-def test_softmax_frame_moves_within_rows(growth, sink):
+@pytest.mark.parametrize("growth,sink,D,pdt", [(6.0, None, 128, torch.float32), (6.0, -math.inf, 128, torch.float32),
+                                               (-0.8, None, 128, torch.float32), (10.0, 3.0, 128, torch.float32),
+                                               (8.0, -math.inf, 64, torch.bfloat16)],
+                         ids=["rising", "rising_no_sink", "falling", "steep_sink3", "rising_no_sink_D64_bf16"])
+def test_softmax_frame_moves_within_rows(growth, sink, D, pdt):
     # Logit scale that changes along the keys: the fp16 weights of later tiles
     # leave the range of the frame set by earlier ones (rising), or fall far
     # below it (falling), so the frame has to move in the middle of rows.
-    x = W.custom(B=2, S=700, Hq=8, Hkv=2, D=128, E=90, seed=125, structure="tail_pad", max_tail_pad=50,
-                 window=500 if growth > 9 else None)
+    x = W.custom(B=2, S=700, Hq=8, Hkv=2, D=D, E=90, seed=125, structure="tail_pad", max_tail_pad=50,
+                 window=500 if growth > 9 else None, profiles_dtype=pdt)
     S = x["k"].shape[1]
     f = 1.0 + growth * torch.arange(S, dtype=torch.float32) / S
     x["k"] = (x["k"].float() * f[None, :, None, None]).to(torch.bfloat16)
