@@ -36,13 +36,13 @@
 //                         LDS strip by DMA (whole row strips, 4-entry runs or
 //                         single entries, by how the tile meets [0, E));
 //        mask             only on tiles classed as masked;
-//        online softmax   running max / denominator per lane over the 64 keys,
-//                         started from the sink logit (the sink's weight
-//                         enters the denominator, never the value sum); the
-//                         running max moves only when a row's tile max
-//                         exceeds it by more than 8 (log2 units), so
-//                         probabilities stay <= 2^8 and most tiles skip the
-//                         output rescale;
+//        online softmax   a running frame and denominator per lane over the
+//                         64 keys, started from the sink logit (the sink's
+//                         weight enters the denominator, never the value
+//                         sum); no per-tile row max: the frame moves (to the
+//                         row max, with an output rescale) only when a
+//                         lane's sum of its fp16 weights reaches 2^15, which
+//                         keeps every weight inside fp16's range;
 //        O^T += V^T P^T   fp16 MFMA 32x32x16; P^T comes straight from the S^T
 //                         accumulator registers and V^T is one 16-byte LDS
 //                         read per lane and MFMA (the staging pass put the
